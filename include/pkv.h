@@ -1,0 +1,206 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: attention over a paged KV cache on AMD MI355X
+ * (gfx950).  Three operations, each one or two hand-written HIP kernels:
+ *
+ *   pkv_kv_cache_write   scatter the step's new K/V rows into cache slots
+ *   pkv_paged_decode     one query per sequence over its cached keys
+ *   pkv_varlen_prefill   causal attention for a packed batch of query chunks
+ *
+ * Page citations (titles as the pages give them):
+ *   [KV-mgmt]   itan.pw, "効率的な KV キャッシュ管理と Attention 計算"
+ *   [paged-doc] transformers documentation, "ページド・アテンション"
+ *   [ch15]      1s.xyz, "KV cache / batching / paged attention"
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is a DEVICE pointer, except where a comment says
+ *   otherwise.  Scalars are passed by value.  Index arrays are int32.
+ * - The caller allocates and owns every buffer, including the decode
+ *   workspace.  The library keeps no device memory between calls.
+ * - Every call validates its scalar arguments on the host, enqueues its
+ *   kernels on `stream` (a hipStream_t; NULL = the null stream) and returns
+ *   without synchronising.  It reads no device memory on the host, so
+ *   metadata that lives on the device (slot maps, block tables, lengths) is
+ *   trusted: see "device-side data" below.
+ * - Return value: PKV_OK (0) or a negative PKV_ERR_* code; the message of the
+ *   last failure on the calling thread is returned by pkv_last_error().  On an
+ *   error no kernel has been launched (except PKV_ERR_LAUNCH).
+ *
+ * Cache layout ([KV-mgmt] section "Triton カーネルによる KV キャッシュ書き込み"
+ * stores a token at slot * (heads * head_dim); section "Python 層からのカーネル
+ * 呼び出し" requires that token stride of the cache; [paged-doc] section
+ * デコードパス: a block table row lists, per logical block of a sequence, the
+ * physical block holding it, -1 meaning unallocated):
+ *   k_cache, v_cache: separate tensors [num_blocks, block_size, num_kv_heads,
+ *   head_dim], contiguous.  Slot s = block * block_size + offset holds one
+ *   token; key j of a sequence lives at slot
+ *   block_table[b][j / block_size] * block_size + j % block_size.
+ *
+ * Element types: PKV_F32 (IEEE fp32), PKV_BF16 (bfloat16) and, for caches
+ * only, PKV_FP8_E4M3 (OCP E4M3 "FN": bias 7, max 448, S.1111.111 = NaN) with
+ * one fp32 scale per KV head for K and one for V: stored code = e4m3(x /
+ * scale), value = code * scale.  (The pages only say an FP8 cache halves the
+ * memory, [ch15] "KVキャッシュはどれくらいメモリを食う？"; the format is the
+ * gfx950-native one.)
+ *
+ * Supported shapes: head_dim in {64, 128}; block_size a power of two in
+ * [8, 256]; num_heads a multiple of num_kv_heads with group size
+ * G = num_heads / num_kv_heads in {1, 2, 4, 8, 16}.
+ *
+ * Device-side data (slot_map, block_table, cache_seqlens, cu_seqlens) is not
+ * read on the host.  The kernels stay inside the buffers whatever it holds:
+ * a slot outside [0, num_slots) is not written, a block id outside
+ * [0, num_blocks) is read as an empty block (its keys are skipped), a length
+ * beyond max_blocks_per_seq * block_size is cut there, and query rows beyond
+ * the max_seqlen_q hint are not computed.  Results for such inputs are
+ * unspecified but memory-safe.  With the environment variable PKV_VALIDATE=1
+ * each call first synchronises, copies the metadata to the host and rejects
+ * such inputs (and duplicate slots) with PKV_ERR_INVALID.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define PKV_OK 0
+#define PKV_ERR_INVALID (-1)     /* bad argument or, under PKV_VALIDATE=1, bad metadata */
+#define PKV_ERR_UNSUPPORTED (-2) /* valid but not built: dtype pair, head_dim, block_size, G */
+#define PKV_ERR_LAUNCH (-3)      /* a HIP runtime call failed */
+
+/* element types */
+#define PKV_F32 0
+#define PKV_BF16 1
+#define PKV_FP8_E4M3 2
+
+/* Message of the last failing call on this thread ("" if none).  The string
+ * is owned by the library and valid until the next call on this thread. */
+const char* pkv_last_error(void);
+
+/* Library version string (static storage). */
+const char* pkv_version(void);
+
+/*
+ * pkv_kv_cache_write -- the slot-map scatter.
+ * [KV-mgmt] section "Triton カーネルによる KV キャッシュ書き込み": each new token
+ * stores its whole K row and V row ([num_kv_heads, head_dim]) at the cache
+ * slot slot_map[t]; section "Python 層からのカーネル呼び出し": the launcher
+ * checks the strides and that there is one slot per token.
+ *
+ *   k, v            [num_tokens, num_kv_heads, head_dim] of src_dtype (F32 or
+ *                   BF16); heads and dims contiguous; consecutive tokens
+ *                   k_token_stride / v_token_stride ELEMENTS apart (>= the
+ *                   row width num_kv_heads * head_dim).
+ *   k_cache,v_cache caches of cache_dtype, layout above, num_slots =
+ *                   num_blocks * block_size rows; modified in place.
+ *   k_scale,v_scale [num_kv_heads] fp32, required iff cache_dtype is FP8,
+ *                   else ignored (may be NULL).
+ *   slot_map        [num_tokens]; -1 = skip the token.  Slots must be
+ *                   distinct (two tokens writing one slot race).
+ * Supported pairs: F32->F32, BF16->BF16 (bit copies), F32->FP8 and BF16->FP8
+ * (code = e4m3 round-to-nearest-even of the IEEE fp32 quotient x / scale,
+ * saturating to +-448, NaN -> 0x7F).
+ * Pointers and byte strides must be 16-byte aligned.
+ * Errors: PKV_ERR_INVALID for NULL pointers, num_tokens < 0, stride below the
+ * row width, misalignment, non-positive sizes; PKV_ERR_UNSUPPORTED for other
+ * dtype pairs or head_dim.  num_tokens == 0 is a no-op.
+ */
+int pkv_kv_cache_write(const void* k, int64_t k_token_stride,
+                       const void* v, int64_t v_token_stride, int src_dtype,
+                       void* k_cache, void* v_cache, int cache_dtype, int64_t num_slots,
+                       const float* k_scale, const float* v_scale,
+                       const int32_t* slot_map, int32_t num_tokens,
+                       int32_t num_kv_heads, int32_t head_dim, void* stream);
+
+/*
+ * pkv_paged_decode_workspace_size -- bytes of fp32 scratch pkv_paged_decode
+ * needs for the same geometry and split_keys (0 when no merge pass is needed).
+ * Returns 0 as well for unsupported arguments (the decode call reports them).
+ */
+size_t pkv_paged_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size,
+                                       int32_t max_blocks_per_seq, int32_t split_keys);
+
+/*
+ * pkv_paged_decode -- one query token per sequence attending to its cache.
+ * [paged-doc] section デコードパス: every sequence brings one query; the kernel
+ * finds its keys through block_table ([batch, max_blocks_per_seq]) and
+ * cache_seqlens; [KV-mgmt] section "Attention モジュールの実装" writes the step's
+ * K/V before this call, so cache_seqlens[b] counts the new token as well.
+ *
+ *   out   [batch, num_heads, head_dim] of q_dtype, written.
+ *   q     [batch, num_heads, head_dim] of q_dtype (F32 or BF16), contiguous.
+ *   k_cache, v_cache of cache_dtype (F32 with F32 q; BF16 or FP8 with BF16 q).
+ *   k_scale, v_scale [num_kv_heads] fp32, required iff FP8.
+ *   block_table [batch, max_blocks_per_seq], row-major; entries past the
+ *               sequence's last block are never read (may be -1).
+ *   cache_seqlens [batch] keys per sequence (0 -> output row of zeros).
+ * out[b, h] = sum_j softmax_j(scale * q[b,h] . k_j) v_j over the sequence's
+ * keys j < cache_seqlens[b], with k_j, v_j read from KV head h / G (q heads
+ * are grouped contiguously).
+ *   split_keys  keys per work unit of the split-K plan: 0 = automatic, else a
+ *               multiple of 128.  Long contexts are cut into units processed
+ *               in parallel; a second kernel merges their partial results.
+ *   workspace   device scratch of at least pkv_paged_decode_workspace_size()
+ *               bytes for the same arguments (NULL allowed when that is 0).
+ *               Its contents on entry do not matter.
+ * Errors: PKV_ERR_INVALID (NULL pointers, sizes <= 0, Hq % Hkv != 0, bad
+ * split_keys, workspace too small); PKV_ERR_UNSUPPORTED (dtype pair,
+ * head_dim, block_size, G).
+ */
+int pkv_paged_decode(void* out, const void* q, int q_dtype,
+                     const void* k_cache, const void* v_cache, int cache_dtype,
+                     const float* k_scale, const float* v_scale,
+                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* cache_seqlens, int32_t batch,
+                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t num_blocks, float softmax_scale,
+                     int32_t split_keys, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * pkv_varlen_prefill -- causal attention for a packed batch of query chunks.
+ * [paged-doc] section "Varlen パス": request b owns query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows [cu_seqlens_k[b],
+ * cu_seqlens_k[b+1]); max_seqlen_q / max_seqlen_k bound the lengths.
+ * [KV-mgmt] section "Attention モジュールの実装": with a block table the paged
+ * caches take the place of k and v (prefix sharing).
+ *
+ *   out   [total_q, num_heads, head_dim] of q_dtype, written (every row of
+ *         every request; rows that see no key are zero).
+ *   q     [total_q, num_heads, head_dim] of q_dtype (BF16, or F32), contiguous.
+ *   k, v  block_table == NULL: packed [total_k, num_kv_heads, head_dim] of
+ *         kv_dtype, contiguous, request b's keys at rows cu_seqlens_k[b]...
+ *         block_table != NULL: the paged caches (layout above, num_blocks
+ *         blocks of block_size); request b has Lk = cu_seqlens_k[b+1] -
+ *         cu_seqlens_k[b] keys read through block_table row b
+ *         ([batch, max_blocks_per_seq]).
+ *   kv_dtype  BF16 with BF16 q (contiguous or paged), FP8 with BF16 q (paged
+ *             only, k_scale/v_scale required), F32 with F32 q.
+ *   causal  1: query row i of a request with Lq queries and Lk keys sees keys
+ *           j <= i + Lk - Lq (aligned to the end, so a chunk after a cached
+ *           prefix sees the whole prefix); 0: sees all Lk keys.
+ *   total_q, total_k  rows held by q/out and, without a block table, by k/v
+ *           (host values; rows beyond them are never touched).
+ * Errors: as for pkv_paged_decode; also max_seqlen_q < 0 or causal not 0/1.
+ */
+int pkv_varlen_prefill(void* out, const void* q, int q_dtype,
+                       const void* k, const void* v, int kv_dtype,
+                       const float* k_scale, const float* v_scale,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                       int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                       int32_t causal, const int32_t* block_table, int32_t max_blocks_per_seq,
+                       int32_t block_size, int32_t num_blocks,
+                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t total_q, int32_t total_k, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -184,7 +184,7 @@ def gather(cache: np.ndarray, block_table_row, num_keys: int) -> np.ndarray:
 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
-              heads=None) -> np.ndarray:
+              heads=None, positions=None, num_queries=None) -> np.ndarray:
     """Textbook scaled softmax attention of one sequence, float64.
 
     q ``[Lq, Hq, D]``, k and v ``[Lk, Hkv, D]`` -> ``[Lq, Hq, D]``.
@@ -200,6 +200,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal:
     * A row that sees no key outputs zeros (an empty sum; reading for the
       zero-key request of the [paged-doc] varlen example).
     * ``heads``: optional subset of q heads to compute (others stay 0).
+    * ``positions`` / ``num_queries``: the given q rows are rows ``positions``
+      of a chunk of ``num_queries`` queries (default: all rows, in order).
     """
     lq, hq, _ = q.shape
     lk, hkv, dv = v.shape
@@ -209,10 +211,11 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal:
     out = np.zeros((lq, hq, dv), dtype=np.float64)
     if lq == 0:
         return out
-    rows = np.arange(lq)[:, None]
+    rows = (np.arange(lq) if positions is None else np.asarray(positions))[:, None]
+    chunk = lq if num_queries is None else int(num_queries)
     cols = np.arange(lk)[None, :]
     if causal:
-        visible = cols <= rows + (lk - lq)
+        visible = cols <= rows + (lk - chunk)
     else:
         visible = np.ones((lq, lk), dtype=bool)
     has_key = visible.any(axis=1)
@@ -286,10 +289,13 @@ def varlen_prefill(q, q_dtype, k, v, kv_dtype, cu_seqlens_q, cu_seqlens_k, scale
     out = np.zeros_like(q64)
     cu_q = np.asarray(cu_seqlens_q, dtype=np.int64)
     cu_k = np.asarray(cu_seqlens_k, dtype=np.int64)
+    wanted = None if rows is None else np.unique(np.asarray(rows, dtype=np.int64))
     for b in range(len(cu_q) - 1):
         q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
-        if rows is not None and not any(q0 <= r < q1 for r in rows):
-            continue
+        if wanted is not None:
+            mine = wanted[(wanted >= q0) & (wanted < q1)]
+            if len(mine) == 0:
+                continue
         lk = int(cu_k[b + 1] - cu_k[b])
         if block_table is None:
             k_rows = k[cu_k[b]:cu_k[b + 1]]
@@ -299,7 +305,11 @@ def varlen_prefill(q, q_dtype, k, v, kv_dtype, cu_seqlens_q, cu_seqlens_k, scale
             v_rows = gather(v, block_table[b], lk)
         k64 = _rows_to_f64(k_rows, kv_dtype, k_scale)
         v64 = _rows_to_f64(v_rows, kv_dtype, v_scale)
-        out[q0:q1] = attention(q64[q0:q1], k64, v64, scale, causal)
+        if wanted is None:
+            out[q0:q1] = attention(q64[q0:q1], k64, v64, scale, causal)
+        else:
+            out[mine] = attention(q64[mine], k64, v64, scale, causal, positions=mine - q0,
+                                  num_queries=q1 - q0)
     return out
 
 

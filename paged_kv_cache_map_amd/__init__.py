@@ -1,0 +1,186 @@
+"""Attention over a paged KV cache on AMD MI355X (gfx950).
+
+Thin Python binding of ``libpkv.so`` (C ABI in ``include/pkv.h``).  Every
+operation runs in the library's HIP kernels; this module only reads shapes,
+strides and device pointers from torch tensors, allocates outputs and the
+decode workspace with torch, and passes the current HIP stream.  The first
+call (or :func:`library`) raises ImportError when the library has not been
+built (``python -m paged_kv_cache_map_amd.build``): there is no fallback path.
+
+Calls (same names as the C entry points without the ``pkv_`` prefix):
+
+* :func:`kv_cache_write` -- scatter new K/V rows into cache slots;
+* :func:`paged_decode`   -- one query per sequence through the block table;
+* :func:`varlen_prefill` -- causal attention for a packed batch of chunks.
+"""
+
+import ctypes
+import pathlib
+
+LIB_PATH = pathlib.Path(__file__).resolve().with_name("libpkv.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_LAUNCH = 0, -1, -2, -3
+
+
+class PkvError(RuntimeError):
+    """A libpkv call returned a non-zero status."""
+
+    def __init__(self, code, message):
+        super().__init__(f"libpkv error {code}: {message}")
+        self.code = code
+
+
+def _load_library():
+    if not LIB_PATH.exists():
+        raise ImportError(f"{LIB_PATH} is missing; build it with "
+                          "`python -m paged_kv_cache_map_amd.build`")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_last_error.argtypes = []
+    lib.pkv_version.restype = ctypes.c_char_p
+    lib.pkv_version.argtypes = []
+    lib.pkv_kv_cache_write.restype = ctypes.c_int
+    lib.pkv_kv_cache_write.argtypes = [vp, i64, vp, i64, ctypes.c_int, vp, vp, ctypes.c_int, i64,
+                                       vp, vp, vp, i32, i32, i32, vp]
+    lib.pkv_paged_decode_workspace_size.restype = sz
+    lib.pkv_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.pkv_paged_decode.restype = ctypes.c_int
+    lib.pkv_paged_decode.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, i32, vp,
+                                     i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.pkv_varlen_prefill.restype = ctypes.c_int
+    lib.pkv_varlen_prefill.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                                       i32, i32, i32, f32, i32, vp, i32, i32, i32, i32, i32, i32,
+                                       i32, i32, vp]
+    return lib
+
+
+_LIB = None
+
+
+def library():
+    """The loaded ``libpkv.so`` (ctypes handle); raises ImportError if it is not built."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load_library()
+    return _LIB
+
+
+def _check(code):
+    if code != OK:
+        raise PkvError(code, library().pkv_last_error().decode())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def kv_cache_write(k, v, k_cache, v_cache, slot_map, k_scale=None, v_scale=None, stream=None):
+    """Store ``k[t]`` and ``v[t]`` ([T, Hkv, D]) at cache slot ``slot_map[t]`` (-1 skips).
+
+    Caches are ``[num_blocks, block_size, Hkv, D]`` (fp32, bf16, or uint8 /
+    float8_e4m3fn codes with per-head fp32 ``k_scale``/``v_scale``).
+    """
+    _require(k.dim() == 3 and v.shape == k.shape, "k and v must be [T, Hkv, D]")
+    _require(k.stride(2) == 1 and k.stride(1) == k.shape[2], "k heads/dims must be contiguous")
+    _require(v.stride(2) == 1 and v.stride(1) == v.shape[2], "v heads/dims must be contiguous")
+    _require(k_cache.is_contiguous() and v_cache.is_contiguous() and k_cache.dim() == 4,
+             "caches must be contiguous [num_blocks, block_size, Hkv, D]")
+    _require(slot_map.numel() == k.shape[0], "one slot per token")
+    t, hkv, d = k.shape
+    _check(library().pkv_kv_cache_write(
+        _ptr(k), k.stride(0) if t > 0 else hkv * d, _ptr(v), v.stride(0) if t > 0 else hkv * d,
+        _dtype_code(k), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+        k_cache.shape[0] * k_cache.shape[1], _ptr(k_scale), _ptr(v_scale), _ptr(slot_map), t, hkv, d,
+        _stream(stream)))
+
+
+def paged_decode_workspace_size(batch, num_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, split_keys=0):
+    return int(library().pkv_paged_decode_workspace_size(batch, num_heads, num_kv_heads, head_dim,
+                                                   block_size, max_blocks_per_seq, split_keys))
+
+
+def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, k_scale=None,
+                 v_scale=None, out=None, split_keys=0, workspace=None, stream=None):
+    """One query per sequence: q [B, Hq, D] -> out [B, Hq, D] (q's dtype)."""
+    import torch
+    _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B, Hq, D]")
+    _require(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+    _require(block_table.dim() == 2 and block_table.is_contiguous() and
+             block_table.dtype == torch.int32, "block_table must be contiguous int32 [B, max_blocks]")
+    _require(cache_seqlens.dtype == torch.int32, "cache_seqlens must be int32")
+    b, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    need = paged_decode_workspace_size(b, hq, hkv, d, bs, block_table.shape[1], split_keys)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pkv_paged_decode(
+        _ptr(out), _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens),
+        b, hq, hkv, d, bs, nb, float(softmax_scale), int(split_keys), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+    return out
+
+
+def varlen_prefill(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale,
+                   causal=True, block_table=None, k_scale=None, v_scale=None, out=None, stream=None):
+    """Packed varlen attention: q [sum Lq, Hq, D] -> out [sum Lq, Hq, D].
+
+    Without ``block_table`` k/v are packed [sum Lk, Hkv, D]; with it they are
+    the paged caches [num_blocks, block_size, Hkv, D].
+    """
+    import torch
+    _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [sum Lq, Hq, D]")
+    _require(k.is_contiguous() and v.is_contiguous(), "k and v must be contiguous")
+    _require(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32,
+             "cu_seqlens must be int32")
+    total_q, hq, d = q.shape
+    batch = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty_like(q)
+    if block_table is not None:
+        _require(block_table.dim() == 2 and block_table.is_contiguous() and
+                 block_table.dtype == torch.int32, "block_table must be contiguous int32")
+        nb, bs, hkv, _ = k.shape
+        maxblk, total_k = block_table.shape[1], 0
+    else:
+        nb, bs, maxblk = 0, 0, 0
+        total_k, hkv = k.shape[0], k.shape[1]
+    _check(library().pkv_varlen_prefill(
+        _ptr(out), _ptr(q), _dtype_code(q), _ptr(k), _ptr(v), _dtype_code(k), _ptr(k_scale),
+        _ptr(v_scale), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, int(max_seqlen_q),
+        int(max_seqlen_k), float(softmax_scale), int(bool(causal)), _ptr(block_table), maxblk, bs, nb,
+        hq, hkv, d, total_q, total_k, _stream(stream)))
+    return out
+
+
+def version():
+    return library().pkv_version().decode()

@@ -1,0 +1,337 @@
+// extern "C" entry points of libpkv.so: argument checks, the optional
+// metadata validation (PKV_VALIDATE=1) and dispatch to the kernel launchers.
+#include <hip/hip_runtime_api.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return PKV_OK;
+}
+
+bool validate_mode() {
+  const char* v = getenv("PKV_VALIDATE");
+  return v && v[0] == '1';
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elt_bytes(int dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+bool pow2_in(int32_t x, int32_t lo, int32_t hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+bool group_ok(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+// Synchronous copy of n int32 from the device (validation mode only).
+bool fetch(std::vector<int32_t>& dst, const int32_t* src, int64_t n, hipStream_t stream) {
+  dst.resize((size_t)n);
+  if (n == 0) return true;
+  if (hipStreamSynchronize(stream) != hipSuccess) return false;
+  return hipMemcpy(dst.data(), src, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost) == hipSuccess;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Every block a sequence of `len` keys touches must name a block in [0, num_blocks).
+int check_table_rows(const std::vector<int32_t>& table, const std::vector<int32_t>& lens,
+                     int32_t max_blocks, int32_t block_size, int32_t num_blocks, const char* what) {
+  for (size_t b = 0; b < lens.size(); ++b) {
+    const int64_t len = lens[b];
+    if (len < 0) return fail(PKV_ERR_INVALID, "%s: sequence %zu has negative length", what, b);
+    const int64_t need = (len + block_size - 1) / block_size;
+    if (need > max_blocks)
+      return fail(PKV_ERR_INVALID, "%s: sequence %zu needs %lld blocks > max_blocks_per_seq %d", what,
+                  b, (long long)need, max_blocks);
+    for (int64_t j = 0; j < need; ++j) {
+      const int32_t id = table[b * (size_t)max_blocks + j];
+      if (id < 0 || id >= num_blocks)
+        return fail(PKV_ERR_INVALID, "%s: sequence %zu logical block %lld maps to %d (pool %d)", what,
+                    b, (long long)j, id, num_blocks);
+    }
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_error.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
+
+int pkv_kv_cache_write(const void* k, int64_t k_token_stride, const void* v, int64_t v_token_stride,
+                       int src_dtype, void* k_cache, void* v_cache, int cache_dtype, int64_t num_slots,
+                       const float* k_scale, const float* v_scale, const int32_t* slot_map,
+                       int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, void* stream) {
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID, "kv_cache_write: num_tokens < 0");
+  if (num_kv_heads <= 0 || head_dim <= 0 || num_slots <= 0)
+    return fail(PKV_ERR_INVALID, "kv_cache_write: num_kv_heads, head_dim and num_slots must be positive");
+  const bool pair_ok = (src_dtype == PKV_F32 && cache_dtype == PKV_F32) ||
+                       (src_dtype == PKV_BF16 && cache_dtype == PKV_BF16) ||
+                       (src_dtype == PKV_BF16 && cache_dtype == PKV_FP8_E4M3) ||
+                       (src_dtype == PKV_F32 && cache_dtype == PKV_FP8_E4M3);
+  if (!pair_ok)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write: unsupported dtype pair %d -> %d", src_dtype,
+                cache_dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write: head_dim %d not in {64, 128}", head_dim);
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (k_token_stride < row || v_token_stride < row)
+    return fail(PKV_ERR_INVALID, "kv_cache_write: token stride below the row width %lld", (long long)row);
+  if (!k || !v || !k_cache || !v_cache || (!slot_map && num_tokens > 0))
+    return fail(PKV_ERR_INVALID, "kv_cache_write: NULL pointer");
+  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID, "kv_cache_write: fp8 cache needs k_scale and v_scale");
+  const int sb = elt_bytes(src_dtype);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (k_token_stride * sb) % 16 != 0 || (v_token_stride * sb) % 16 != 0)
+    return fail(PKV_ERR_INVALID, "kv_cache_write: pointers and token strides must be 16-byte aligned");
+  if (num_tokens == 0) return ok();
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_mode()) {
+    std::vector<int32_t> slots;
+    if (!fetch(slots, slot_map, num_tokens, s))
+      return fail(PKV_ERR_LAUNCH, "kv_cache_write: could not read slot_map");
+    std::unordered_set<int32_t> seen;
+    for (int32_t t = 0; t < num_tokens; ++t) {
+      const int32_t x = slots[t];
+      if (x == -1) continue;
+      if (x < 0 || x >= num_slots)
+        return fail(PKV_ERR_INVALID, "kv_cache_write: slot_map[%d] = %d outside [0, %lld)", t, x,
+                    (long long)num_slots);
+      if (!seen.insert(x).second)
+        return fail(PKV_ERR_INVALID, "kv_cache_write: slot %d written twice", x);
+    }
+  }
+  pkv::WriteArgs a;
+  a.k = (const uint8_t*)k;
+  a.v = (const uint8_t*)v;
+  a.k_stride_bytes = k_token_stride * sb;
+  a.v_stride_bytes = v_token_stride * sb;
+  a.k_cache = (uint8_t*)k_cache;
+  a.v_cache = (uint8_t*)v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.slot_map = slot_map;
+  a.num_slots = num_slots;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.src_dtype = src_dtype;
+  a.cache_dtype = cache_dtype;
+  return launch_status(pkv::launch_kv_write(a, s), "kv_cache_write");
+}
+
+size_t pkv_paged_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size,
+                                       int32_t max_blocks_per_seq, int32_t split_keys) {
+  pkv::DecodePlan p;
+  const char* why = nullptr;
+  if (!pkv::plan_decode(batch, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        split_keys, &p, &why))
+    return 0;
+  return p.workspace_bytes;
+}
+
+int pkv_paged_decode(void* out, const void* q, int q_dtype, const void* k_cache, const void* v_cache,
+                     int cache_dtype, const float* k_scale, const float* v_scale,
+                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* cache_seqlens, int32_t batch, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                     float softmax_scale, int32_t split_keys, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PKV_ERR_INVALID, "paged_decode: sizes must be positive");
+  if (batch > 65535) return fail(PKV_ERR_INVALID, "paged_decode: batch above 65535");
+  if (num_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "paged_decode: num_heads %% num_kv_heads != 0");
+  if (!out || !q || !k_cache || !v_cache || !block_table || !cache_seqlens)
+    return fail(PKV_ERR_INVALID, "paged_decode: NULL pointer");
+  const bool pair_ok = (q_dtype == PKV_F32 && cache_dtype == PKV_F32) ||
+                       (q_dtype == PKV_BF16 && cache_dtype == PKV_BF16) ||
+                       (q_dtype == PKV_BF16 && cache_dtype == PKV_FP8_E4M3);
+  if (!pair_ok)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_decode: unsupported q/cache dtypes %d/%d", q_dtype,
+                cache_dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_decode: head_dim %d not in {64, 128}", head_dim);
+  if (!pow2_in(block_size, 8, 256))
+    return fail(PKV_ERR_UNSUPPORTED, "paged_decode: block_size %d not a power of two in [8, 256]",
+                block_size);
+  if (!group_ok(num_heads / num_kv_heads))
+    return fail(PKV_ERR_UNSUPPORTED, "paged_decode: group size %d not in {1,2,4,8,16}",
+                num_heads / num_kv_heads);
+  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID, "paged_decode: fp8 cache needs k_scale and v_scale");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(PKV_ERR_INVALID, "paged_decode: q, out and caches must be 16-byte aligned");
+  pkv::DecodePlan plan;
+  const char* why = nullptr;
+  if (!pkv::plan_decode(batch, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        split_keys, &plan, &why))
+    return fail(PKV_ERR_INVALID, "paged_decode: %s", why);
+  if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes > 0 && !workspace))
+    return fail(PKV_ERR_INVALID, "paged_decode: workspace of %zu bytes needed, %zu given",
+                plan.workspace_bytes, workspace_bytes);
+  if (plan.workspace_bytes > 0 && !aligned16(workspace))
+    return fail(PKV_ERR_INVALID, "paged_decode: workspace must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_mode()) {
+    std::vector<int32_t> lens, table;
+    if (!fetch(lens, cache_seqlens, batch, s) ||
+        !fetch(table, block_table, (int64_t)batch * max_blocks_per_seq, s))
+      return fail(PKV_ERR_LAUNCH, "paged_decode: could not read metadata");
+    const int rc = check_table_rows(table, lens, max_blocks_per_seq, block_size, num_blocks,
+                                    "paged_decode");
+    if (rc != PKV_OK) return rc;
+  }
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = (const uint8_t*)k_cache;
+  a.v_cache = (const uint8_t*)v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.cache_seqlens = cache_seqlens;
+  a.workspace = (float*)workspace;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.batch = batch;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.softmax_scale = softmax_scale;
+  a.q_dtype = q_dtype;
+  a.cache_dtype = cache_dtype;
+  return launch_status(pkv::launch_paged_decode(a, plan, s), "paged_decode");
+}
+
+int pkv_varlen_prefill(void* out, const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                       const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
+                       const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
+                       int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                       const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size,
+                       int32_t num_blocks, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t total_q, int32_t total_k, void* stream) {
+  if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+    return fail(PKV_ERR_INVALID, "varlen_prefill: negative size");
+  if (batch > 65535) return fail(PKV_ERR_INVALID, "varlen_prefill: batch above 65535");
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "varlen_prefill: num_heads must be a positive multiple of num_kv_heads");
+  if (causal != 0 && causal != 1) return fail(PKV_ERR_INVALID, "varlen_prefill: causal must be 0 or 1");
+  const bool paged = block_table != nullptr;
+  const bool pair_ok = (q_dtype == PKV_BF16 && kv_dtype == PKV_BF16) ||
+                       (q_dtype == PKV_BF16 && kv_dtype == PKV_FP8_E4M3 && paged) ||
+                       (q_dtype == PKV_F32 && kv_dtype == PKV_F32);
+  if (!pair_ok)
+    return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: unsupported q/kv dtypes %d/%d%s", q_dtype, kv_dtype,
+                paged ? "" : " (fp8 needs the paged cache)");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: head_dim %d not in {64, 128}", head_dim);
+  if (!group_ok(num_heads / num_kv_heads))
+    return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: group size %d not in {1,2,4,8,16}",
+                num_heads / num_kv_heads);
+  if (paged) {
+    if (!pow2_in(block_size, 8, 256))
+      return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: block_size %d not a power of two in [8, 256]",
+                  block_size);
+    if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+      return fail(PKV_ERR_INVALID, "varlen_prefill: max_blocks_per_seq and num_blocks must be positive");
+  }
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID, "varlen_prefill: fp8 cache needs k_scale and v_scale");
+  if (batch == 0 || max_seqlen_q == 0 || total_q == 0) return ok();
+  if (!out || !q || !k || !v || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(PKV_ERR_INVALID, "varlen_prefill: NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(PKV_ERR_INVALID, "varlen_prefill: q, k, v and out must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_mode()) {
+    std::vector<int32_t> cq, ck, table;
+    if (!fetch(cq, cu_seqlens_q, batch + 1, s) || !fetch(ck, cu_seqlens_k, batch + 1, s))
+      return fail(PKV_ERR_LAUNCH, "varlen_prefill: could not read cu_seqlens");
+    if (cq[0] != 0 || ck[0] != 0) return fail(PKV_ERR_INVALID, "varlen_prefill: cu_seqlens must start at 0");
+    std::vector<int32_t> klens((size_t)batch);
+    for (int32_t b = 0; b < batch; ++b) {
+      const int32_t lq = cq[b + 1] - cq[b], lk = ck[b + 1] - ck[b];
+      if (lq < 0 || lk < 0) return fail(PKV_ERR_INVALID, "varlen_prefill: cu_seqlens not monotone at %d", b);
+      if (lq > max_seqlen_q || lk > max_seqlen_k)
+        return fail(PKV_ERR_INVALID, "varlen_prefill: request %d exceeds the max_seqlen hints", b);
+      klens[b] = lk;
+    }
+    if (cq[batch] > total_q) return fail(PKV_ERR_INVALID, "varlen_prefill: cu_seqlens_q exceeds total_q");
+    if (paged) {
+      if (!fetch(table, block_table, (int64_t)batch * max_blocks_per_seq, s))
+        return fail(PKV_ERR_LAUNCH, "varlen_prefill: could not read block_table");
+      const int rc = check_table_rows(table, klens, max_blocks_per_seq, block_size, num_blocks,
+                                      "varlen_prefill");
+      if (rc != PKV_OK) return rc;
+    } else if (ck[batch] > total_k) {
+      return fail(PKV_ERR_INVALID, "varlen_prefill: cu_seqlens_k exceeds total_k");
+    }
+  }
+  pkv::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k = (const uint8_t*)k;
+  a.v = (const uint8_t*)v;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.block_table = block_table;
+  a.batch = batch;
+  a.max_seqlen_q = max_seqlen_q;
+  a.max_seqlen_k = max_seqlen_k;
+  a.softmax_scale = softmax_scale;
+  a.causal = causal;
+  a.max_blocks_per_seq = paged ? max_blocks_per_seq : 0;
+  a.block_size = paged ? block_size : 0;
+  a.num_blocks = paged ? num_blocks : 0;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.q_dtype = q_dtype;
+  a.kv_dtype = kv_dtype;
+  return launch_status(pkv::launch_varlen_prefill(a, s), "varlen_prefill");
+}
+
+}  // extern "C"

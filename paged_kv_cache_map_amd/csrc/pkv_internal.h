@@ -1,0 +1,104 @@
+// Internal interface between the C ABI layer (pkv_api.cpp) and the kernel
+// launchers (*.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct WriteArgs {
+  const uint8_t* k;
+  const uint8_t* v;
+  int64_t k_stride_bytes;
+  int64_t v_stride_bytes;
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* slot_map;
+  int64_t num_slots;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int src_dtype;
+  int cache_dtype;
+};
+
+hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
+
+// Split-K plan of the decode: keys [s * split_keys, (s+1) * split_keys) of a
+// sequence form work unit s.
+struct DecodePlan {
+  int32_t split_keys;   // multiple of kDecodeKeysPerWg
+  int32_t num_splits;   // units per sequence at the longest possible length
+  int32_t head_groups;  // q-head groups of at most 8 per KV head
+  size_t workspace_bytes;
+};
+
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeChunk = 32;                              // keys per wave iteration
+constexpr int kDecodeKeysPerWg = kDecodeWaves * kDecodeChunk;  // 128
+constexpr int kDecodeMaxSplitKeys = 8192;                     // bounds the LDS block table
+
+// Fills `plan`; returns false (with a message in *why) for arguments the
+// planner cannot serve.  Pure host arithmetic, no HIP calls.
+bool plan_decode(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t block_size, int32_t max_blocks_per_seq, int32_t split_keys,
+                 DecodePlan* plan, const char** why);
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* cache_seqlens;
+  float* workspace;
+  int32_t max_blocks_per_seq;
+  int32_t batch;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  float softmax_scale;
+  int q_dtype;
+  int cache_dtype;
+};
+
+hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  const int32_t* block_table;
+  int32_t batch;
+  int32_t max_seqlen_q;
+  int32_t max_seqlen_k;
+  float softmax_scale;
+  int32_t causal;
+  int32_t max_blocks_per_seq;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t total_q;
+  int32_t total_k;
+  int q_dtype;
+  int kv_dtype;
+};
+
+hipError_t launch_varlen_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,464 @@
+// Varlen causal prefill over a packed batch, K/V contiguous or paged.
+//
+// [paged-doc] "ページド・アテンション", section "Varlen パス": request b owns query
+// rows [cu_q[b], cu_q[b+1]) and keys [cu_k[b], cu_k[b+1]).  [KV-mgmt]
+// "効率的な KV キャッシュ管理と Attention 計算", section "Attention モジュールの実装":
+// with block tables the paged caches replace k and v, so a chunk attends its
+// cached prefix and itself.  Causal masking is aligned to the end: row i of a
+// request with Lq queries and Lk keys sees keys j <= i + Lk - Lq.  [ch15]
+// "KV cache / batching / paged attention", section "FlashAttention：注意計算そのも
+// のを速く": tiles stay on chip and the result equals plain attention.
+//
+// bf16 / fp8-cache kernel (gfx950 MFMA, v_mfma_f32_32x32x16_bf16):
+// * workgroup = 128 query rows of one (request, q head); 4 waves x 32 rows.
+// * per 64-key tile: S^T = K Q^T on MFMA (keys x queries), so each lane owns
+//   one query column and 16 of its 32 scores per 32-key block; the row max and
+//   row sum need one cross-lane exchange (lane ^ 32).  P^T, packed to bf16,
+//   is used directly as the B operand of O^T += V^T P^T.
+// * K tiles are staged in LDS row-major; V tiles are transposed in registers
+//   (8 x 8 bf16 blocks with v_perm) and staged as V^T, so both MFMA A operands
+//   are plain LDS reads.  Two LDS buffers: the next tile's global loads are in
+//   flight while the current tile is computed.  fp8 caches are dequantised to
+//   bf16 (exact) while staging; the K scale folds into the logit scale, the V
+//   scale into the output.
+// * workgroups are renumbered so that the tiles of one (request, KV head) run
+//   on the same XCD and share its L2.
+//
+// fp32 kernel: a plain per-row wave kernel (lanes over head_dim), kept for
+// fp32 accuracy checks; it is not tuned.
+
+#include "pkv_device.hpp"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 128;   // query rows per workgroup
+constexpr int BN = 64;    // keys per tile
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;
+
+template <int D>
+struct Lds {
+  static constexpr int k_row = D + 8;    // bf16 elements per K row (16-byte pad)
+  static constexpr int vt_row = BN + 4;  // bf16 elements per V^T row (8-byte pad)
+  static constexpr int k_elems = BN * k_row;
+  static constexpr int vt_elems = D * vt_row;
+  static constexpr int buf_elems = k_elems + vt_elems;
+};
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// 8 x 8 bf16 transpose: r[i] holds 8 elements of row i; out[e] holds element
+// e of rows 0..7.
+__device__ __forceinline__ void transpose8x8(const uint4 (&r)[8], uint4 (&out)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint32_t w[4];
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+      const uint4 a = r[2 * kp], b = r[2 * kp + 1];
+      const uint32_t aw = (e >> 1) == 0 ? a.x : (e >> 1) == 1 ? a.y : (e >> 1) == 2 ? a.z : a.w;
+      const uint32_t bw = (e >> 1) == 0 ? b.x : (e >> 1) == 1 ? b.y : (e >> 1) == 2 ? b.z : b.w;
+      w[kp] = perm(bw, aw, (e & 1) ? 0x07060302u : 0x05040100u);
+    }
+    out[e] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Eight E4M3 codes (two words) -> eight bf16 (four words), exact.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return make_uint4(e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
+                    e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1));
+}
+
+struct KeyAddr {
+  const uint8_t* base;  // k or v + g * row_bytes (+ k_start rows when contiguous)
+  int64_t row_stride;   // bytes between consecutive slots / rows
+  const int32_t* table; // paged: block_table row of the request, else nullptr
+  int log2bs, bs_mask, num_blocks, lk;
+};
+
+// Address of key j's row (nullptr if the key does not exist).
+__device__ __forceinline__ const uint8_t* key_row(const KeyAddr& ka, int j) {
+  if (j >= ka.lk) return nullptr;
+  if (ka.table == nullptr) return ka.base + (int64_t)j * ka.row_stride;
+  const int blk = ka.table[j >> ka.log2bs];
+  if (blk < 0 || blk >= ka.num_blocks) return nullptr;
+  return ka.base + (((int64_t)blk << ka.log2bs) + (j & ka.bs_mask)) * ka.row_stride;
+}
+
+// Registers of one tile in flight between its global loads and its LDS stores.
+template <int KVT, int D>
+struct TileRegs {
+  static constexpr int elt = Elt<KVT>::bytes;
+  static constexpr int k_pieces = D * elt / 16;            // 16-byte pieces per K row
+  static constexpr int k_per_thread = BN * k_pieces / 128;  // threads 0..127 load K
+  static constexpr int v_vec = 8 * elt;                      // bytes of 8 elements
+  static constexpr int v_blocks = (BN / 8) * (D / 8);        // 8x8 blocks, threads 128.. load V
+  uint4 k[k_per_thread];
+  uint4 v[8];   // bf16: 8 rows x 16 B; fp8: 8 rows x 8 B in .x/.y
+};
+
+template <int KVT, int D>
+__device__ __forceinline__ void tile_load(TileRegs<KVT, D>& r, const KeyAddr& ka, const KeyAddr& va,
+                                          int key0, int tid) {
+  using T = TileRegs<KVT, D>;
+  if (tid < 128) {
+#pragma unroll
+    for (int i = 0; i < T::k_per_thread; ++i) {
+      const int p = tid + 128 * i;
+      const int row = p / T::k_pieces, piece = p % T::k_pieces;
+      const uint8_t* src = key_row(ka, key0 + row);
+      r.k[i] = src ? *reinterpret_cast<const uint4*>(src + piece * 16) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  } else {
+    const int u = tid - 128;
+    if (u < T::v_blocks) {
+      const int kg = u / (D / 8), pc = u % (D / 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint8_t* src = key_row(va, key0 + kg * 8 + i);
+        if constexpr (KVT == kBF16) {
+          r.v[i] = src ? *reinterpret_cast<const uint4*>(src + pc * 16) : make_uint4(0u, 0u, 0u, 0u);
+        } else {
+          const uint2 x = src ? *reinterpret_cast<const uint2*>(src + pc * 8) : make_uint2(0u, 0u);
+          r.v[i] = make_uint4(x.x, x.y, 0u, 0u);
+        }
+      }
+    }
+  }
+}
+
+template <int KVT, int D>
+__device__ __forceinline__ void tile_store(const TileRegs<KVT, D>& r, uint16_t* buf, int tid) {
+  using T = TileRegs<KVT, D>;
+  using L = Lds<D>;
+  if (tid < 128) {
+#pragma unroll
+    for (int i = 0; i < T::k_per_thread; ++i) {
+      const int p = tid + 128 * i;
+      const int row = p / T::k_pieces, piece = p % T::k_pieces;
+      if constexpr (KVT == kBF16) {
+        *reinterpret_cast<uint4*>(buf + row * L::k_row + piece * 8) = r.k[i];
+      } else {
+        uint16_t* dst = buf + row * L::k_row + piece * 16;
+        *reinterpret_cast<uint4*>(dst) = e4m3x8_to_bf16x8(r.k[i].x, r.k[i].y);
+        *reinterpret_cast<uint4*>(dst + 8) = e4m3x8_to_bf16x8(r.k[i].z, r.k[i].w);
+      }
+    }
+  } else {
+    const int u = tid - 128;
+    if (u < T::v_blocks) {
+      const int kg = u / (D / 8), pc = u % (D / 8);
+      uint4 rows[8], cols[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (KVT == kBF16) {
+          rows[i] = r.v[i];
+        } else {
+          rows[i] = e4m3x8_to_bf16x8(r.v[i].x, r.v[i].y);
+        }
+      }
+      transpose8x8(rows, cols);
+      uint16_t* vt = buf + L::k_elems;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint2*>(vt + (pc * 8 + e) * L::vt_row + kg * 8) = make_uint2(cols[e].x, cols[e].y),
+        *reinterpret_cast<uint2*>(vt + (pc * 8 + e) * L::vt_row + kg * 8 + 4) = make_uint2(cols[e].z, cols[e].w);
+    }
+  }
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+template <int KVT, int D>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int q_tiles, int total_wg) {
+  using L = Lds<D>;
+  constexpr int KS = D / 16;   // MFMA k-steps over head_dim
+  constexpr int DB = D / 32;   // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::buf_elems];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, col = lane & 31;
+
+  // XCD-aware renumbering: hardware workgroup i runs on XCD i % 8; give each
+  // XCD a contiguous range of logical work so one request/KV head stays on one L2.
+  const int hw = blockIdx.x;
+  const int per_xcd = (total_wg + 7) / 8;
+  const int logical = (hw % 8) * per_xcd + hw / 8;
+  if (logical >= total_wg) return;
+  const int group = a.num_heads / a.num_kv_heads;
+  const int qt = logical % q_tiles;
+  int rest = logical / q_tiles;
+  const int h = rest % a.num_heads;  // q heads of one KV head are adjacent
+  const int b = rest / a.num_heads;
+  const int g = h / group;
+
+  int q_start = a.cu_seqlens_q[b];
+  int lq = a.cu_seqlens_q[b + 1] - q_start;
+  if (lq > a.max_seqlen_q) lq = a.max_seqlen_q;
+  if (q_start < 0 || q_start >= a.total_q) lq = 0;
+  else if (lq > a.total_q - q_start) lq = a.total_q - q_start;
+  const int q0 = qt * BM;
+  if (q0 >= lq) return;
+  const int k_start = a.cu_seqlens_k[b];
+  int lk = a.cu_seqlens_k[b + 1] - k_start;
+  if (lk < 0) lk = 0;
+  const bool paged = a.block_table != nullptr;
+  if (paged) {
+    const int cap = a.max_blocks_per_seq * a.block_size;
+    if (lk > cap) lk = cap;
+  } else {
+    if (k_start < 0 || k_start > a.total_k) lk = 0;
+    else if (lk > a.total_k - k_start) lk = a.total_k - k_start;
+  }
+  const int offset = lk - lq;  // bottom-right causal alignment
+  const int last_row = min(q0 + BM, lq) - 1;
+  int key_end = a.causal ? min(lk, last_row + offset + 1) : lk;
+  if (key_end < 0) key_end = 0;
+  const int n_tiles = (key_end + BN - 1) / BN;
+
+  constexpr int elt = Elt<KVT>::bytes;
+  const int64_t row_bytes = (int64_t)D * elt;
+  KeyAddr ka, va;
+  ka.row_stride = va.row_stride = (int64_t)a.num_kv_heads * row_bytes;
+  ka.base = a.k + g * row_bytes + (paged ? 0 : (int64_t)k_start * ka.row_stride);
+  va.base = a.v + g * row_bytes + (paged ? 0 : (int64_t)k_start * va.row_stride);
+  ka.table = va.table = paged ? a.block_table + (int64_t)b * a.max_blocks_per_seq : nullptr;
+  ka.log2bs = va.log2bs = paged ? __builtin_ctz(a.block_size) : 0;
+  ka.bs_mask = va.bs_mask = paged ? a.block_size - 1 : 0;
+  ka.num_blocks = va.num_blocks = a.num_blocks;
+  ka.lk = va.lk = lk;
+
+  // this wave's query column: row q0 + 32 * wave + col
+  const int qrow = q0 + wave * 32 + col;
+  const bool qvalid = qrow < lq;
+  uint4 qf[KS];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((int64_t)(q_start + qrow) * a.num_heads + h) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = qvalid ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  float scale = a.softmax_scale * kLog2e;
+  float out_scale = 1.0f;
+  if constexpr (KVT == kFP8) {
+    scale *= a.k_scale[g];
+    out_scale = a.v_scale[g];
+  }
+
+  f32x16_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
+  float m = kNegBig, l = 0.0f;
+
+  TileRegs<KVT, D> regs;
+  if (n_tiles > 0) {
+    tile_load<KVT, D>(regs, ka, va, 0, tid);
+    tile_store<KVT, D>(regs, lds, tid);
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    __syncthreads();
+    const int key0 = t * BN;
+    if (t + 1 < n_tiles) tile_load<KVT, D>(regs, ka, va, key0 + BN, tid);
+    const uint16_t* kb_lds = lds + (t & 1) * L::buf_elems;
+    const uint16_t* vt_lds = kb_lds + L::k_elems;
+
+    // S^T for two 32-key blocks
+    f32x16_t s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16_t{};
+      const uint16_t* krow = kb_lds + (kb * 32 + col) * L::k_row + half * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 kf = *reinterpret_cast<const uint4*>(krow + ks * 16);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), s[kb], 0, 0, 0);
+      }
+    }
+    // scale, mask, row max
+    const bool need_mask = (key0 + BN > lk) || (a.causal && key0 + BN - 1 > q0 + wave * 32 + offset);
+    float mx = kNegBig;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[kb][r] * scale;
+        if (need_mask) {
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = key < lk && (!a.causal || key <= qrow + offset);
+          x = vis ? x : -INFINITY;
+        }
+        s[kb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    float psum = 0.0f;
+    uint4 pb[2][2];  // [key block][16-key half] bf16 B operands
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        f32x8_t pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(s[kb][hs * 8 + e] - mn);
+          pv[e] = p;
+          psum += p;
+        }
+        pb[kb][hs] = __builtin_bit_cast(uint4, __builtin_convertvector(pv, bf16x8_t));
+      }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint16_t* vrow = vt_lds + (db * 32 + col) * L::vt_row + 4 * half;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const int k0 = kb * 32 + hs * 16;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + k0);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + k0 + 8);
+          const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pb[kb][hs]), o[db], 0, 0, 0);
+        }
+    }
+    if (t + 1 < n_tiles) tile_store<KVT, D>(regs, lds + ((t + 1) & 1) * L::buf_elems, tid);
+  }
+
+  // normalise and store: lane holds O^T rows 8*(r/4) + 4*half + r%4 of each 32-row block
+  l += shfl_xor(l, 32);
+  if (!qvalid) return;
+  const float inv = l > 0.0f ? out_scale / l : 0.0f;
+  uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q_start + qrow) * a.num_heads + h) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d = db * 32 + rg * 8 + half * 4;
+      const uint32_t w0 = pack_bf16x2(o[db][rg * 4 + 0] * inv, o[db][rg * 4 + 1] * inv);
+      const uint32_t w1 = pack_bf16x2(o[db][rg * 4 + 2] * inv, o[db][rg * 4 + 3] * inv);
+      *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
+    }
+}
+
+// fp32: one wave per (query row, q head); lanes hold head_dim / 64 elements.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
+  constexpr int NV = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;  // (row of the packed q, head)
+  if (item >= (int64_t)a.total_q * a.num_heads) return;
+  const int row = (int)(item / a.num_heads), h = (int)(item % a.num_heads);
+  // request owning this row: binary search over cu_seqlens_q
+  int lo = 0, hi = a.batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_seqlens_q[mid] <= row) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  const int q_start = a.cu_seqlens_q[b];
+  const int lq = a.cu_seqlens_q[b + 1] - q_start;
+  if (row < q_start || row - q_start >= lq) return;
+  const int i = row - q_start;
+  const int g = h / (a.num_heads / a.num_kv_heads);
+  const int k_start = a.cu_seqlens_k[b];
+  int lk = a.cu_seqlens_k[b + 1] - k_start;
+  if (lk < 0) lk = 0;
+  const bool paged = a.block_table != nullptr;
+  if (paged) lk = min(lk, a.max_blocks_per_seq * a.block_size);
+  else if (k_start < 0 || k_start > a.total_k) lk = 0;
+  else lk = min(lk, a.total_k - k_start);
+  const int kend = a.causal ? max(0, min(lk, i + lk - lq + 1)) : lk;
+  const int64_t row_bytes = (int64_t)D * 4;
+  KeyAddr ka, va;
+  ka.row_stride = va.row_stride = (int64_t)a.num_kv_heads * row_bytes;
+  ka.base = a.k + g * row_bytes + (paged ? 0 : (int64_t)k_start * ka.row_stride);
+  va.base = a.v + g * row_bytes + (paged ? 0 : (int64_t)k_start * va.row_stride);
+  ka.table = va.table = paged ? a.block_table + (int64_t)b * a.max_blocks_per_seq : nullptr;
+  ka.log2bs = va.log2bs = paged ? __builtin_ctz(a.block_size) : 0;
+  ka.bs_mask = va.bs_mask = paged ? a.block_size - 1 : 0;
+  ka.num_blocks = va.num_blocks = a.num_blocks;
+  ka.lk = va.lk = lk;
+  const float* qp = reinterpret_cast<const float*>(a.q) + ((int64_t)row * a.num_heads + h) * D;
+  float qv[NV], o[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    qv[e] = qp[lane * NV + e];
+    o[e] = 0.0f;
+  }
+  const float scale = a.softmax_scale * kLog2e;
+  float m = kNegBig, l = 0.0f;
+  for (int j = 0; j < kend; ++j) {
+    const float* kr = reinterpret_cast<const float*>(key_row(ka, j));
+    const float* vr = reinterpret_cast<const float*>(key_row(va, j));
+    if (kr == nullptr) continue;
+    float dot = 0.0f;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) dot = fmaf(qv[e], kr[lane * NV + e], dot);
+    for (int x = 1; x < 64; x <<= 1) dot += shfl_xor(dot, x);
+    const float s = dot * scale;
+    const float mn = fmaxf(m, s);
+    const float alpha = fast_exp2(m - mn);
+    const float p = fast_exp2(s - mn);
+    m = mn;
+    l = l * alpha + p;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) o[e] = fmaf(p, vr[lane * NV + e], o[e] * alpha);
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  float* op = reinterpret_cast<float*>(a.out) + ((int64_t)row * a.num_heads + h) * D;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) op[lane * NV + e] = o[e] * inv;
+}
+
+template <int KVT, int D>
+hipError_t launch_mfma(const PrefillArgs& a, hipStream_t stream) {
+  const int q_tiles = (a.max_seqlen_q + BM - 1) / BM;
+  const int64_t wg = (int64_t)q_tiles * a.num_heads * a.batch;
+  if (wg > 0x7fffffff / 2) return hipErrorInvalidValue;
+  const int total = (int)wg;
+  const int grid = (total + 7) / 8 * 8;
+  hipLaunchKernelGGL((prefill_kernel<KVT, D>), dim3(grid), dim3(kThreads), 0, stream, a, q_tiles, total);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32(const PrefillArgs& a, hipStream_t stream) {
+  const int64_t items = (int64_t)a.total_q * a.num_heads;
+  hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_varlen_prefill(const PrefillArgs& a, hipStream_t stream) {
+  if (a.q_dtype == kF32) {
+    if (a.head_dim == 64) return launch_f32<64>(a, stream);
+    return launch_f32<128>(a, stream);
+  }
+  if (a.kv_dtype == kBF16) {
+    if (a.head_dim == 64) return launch_mfma<kBF16, 64>(a, stream);
+    return launch_mfma<kBF16, 128>(a, stream);
+  }
+  if (a.head_dim == 64) return launch_mfma<kFP8, 64>(a, stream);
+  return launch_mfma<kFP8, 128>(a, stream);
+}
+
+}  // namespace pkv

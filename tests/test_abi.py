@@ -1,0 +1,145 @@
+"""The C ABI library: loads, exports what the header declares, rejects bad
+arguments on the host (CPU only: no call here reaches a kernel)."""
+
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+import paged_kv_cache_map_amd as pkv
+
+HEADER = pathlib.Path(__file__).resolve().parent.parent / "include" / "pkv.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for want in ("pkv_kv_cache_write", "pkv_paged_decode", "pkv_varlen_prefill",
+                 "pkv_paged_decode_workspace_size", "pkv_last_error", "pkv_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(pkv.LIB_PATH))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version():
+    assert "gfx950" in pkv.version()
+
+
+NULL = None
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: every case fails validation first
+ODD = ctypes.c_void_p(0x1008)       # not 16-byte aligned
+
+
+def write(**kw):
+    args = dict(k=FAKE, ks=1024, v=FAKE, vs=1024, src=pkv.BF16, kc=FAKE, vc=FAKE, cdt=pkv.BF16,
+                slots=100, ksc=NULL, vsc=NULL, sm=FAKE, t=3, hkv=8, d=128, stream=NULL)
+    args.update(kw)
+    return pkv.library().pkv_kv_cache_write(
+        args["k"], args["ks"], args["v"], args["vs"], args["src"], args["kc"], args["vc"], args["cdt"],
+        args["slots"], args["ksc"], args["vsc"], args["sm"], args["t"], args["hkv"], args["d"],
+        args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(t=-1), pkv.ERR_INVALID),
+    (dict(ks=1023), pkv.ERR_INVALID),                 # token stride below the row width
+    (dict(k=NULL), pkv.ERR_INVALID),
+    (dict(sm=NULL), pkv.ERR_INVALID),
+    (dict(cdt=pkv.FP8_E4M3), pkv.ERR_INVALID),        # fp8 without scales
+    (dict(src=pkv.F32, cdt=pkv.BF16), pkv.ERR_UNSUPPORTED),
+    (dict(d=96), pkv.ERR_UNSUPPORTED),
+    (dict(k=ODD), pkv.ERR_INVALID),
+    (dict(ks=1028), pkv.ERR_INVALID),                 # 2056-byte stride is not 16-byte aligned
+    (dict(hkv=0), pkv.ERR_INVALID),
+])
+def test_write_rejects(kw, code):
+    assert write(**kw) == code
+    assert pkv.library().pkv_last_error()
+
+
+def test_write_zero_tokens_is_a_no_op():
+    assert write(t=0, sm=NULL) == pkv.OK
+
+
+def decode(**kw):
+    a = dict(out=FAKE, q=FAKE, qdt=pkv.BF16, kc=FAKE, vc=FAKE, cdt=pkv.BF16, ksc=NULL, vsc=NULL,
+             bt=FAKE, maxblk=4, sl=FAKE, b=3, hq=8, hkv=2, d=128, bs=16, nb=10, scale=0.1, split=0,
+             ws=FAKE, wsb=1 << 30, stream=NULL)
+    a.update(kw)
+    return pkv.library().pkv_paged_decode(
+        a["out"], a["q"], a["qdt"], a["kc"], a["vc"], a["cdt"], a["ksc"], a["vsc"], a["bt"],
+        a["maxblk"], a["sl"], a["b"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"],
+        a["split"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=0), pkv.ERR_INVALID),
+    (dict(hq=6, hkv=4), pkv.ERR_INVALID),
+    (dict(hq=24, hkv=1), pkv.ERR_UNSUPPORTED),        # group of 24
+    (dict(q=NULL), pkv.ERR_INVALID),
+    (dict(bt=NULL), pkv.ERR_INVALID),
+    (dict(d=80), pkv.ERR_UNSUPPORTED),
+    (dict(bs=12), pkv.ERR_UNSUPPORTED),
+    (dict(bs=512), pkv.ERR_UNSUPPORTED),
+    (dict(qdt=pkv.F32), pkv.ERR_UNSUPPORTED),         # fp32 q with a bf16 cache
+    (dict(cdt=pkv.FP8_E4M3), pkv.ERR_INVALID),        # fp8 without scales
+    (dict(split=100), pkv.ERR_INVALID),               # not a multiple of 128
+    (dict(split=128, maxblk=64, wsb=0, ws=NULL), pkv.ERR_INVALID),   # workspace too small
+    (dict(out=ODD), pkv.ERR_INVALID),
+])
+def test_decode_rejects(kw, code):
+    assert decode(**kw) == code
+
+
+def prefill(**kw):
+    a = dict(out=FAKE, q=FAKE, qdt=pkv.BF16, k=FAKE, v=FAKE, kdt=pkv.BF16, ksc=NULL, vsc=NULL,
+             cq=FAKE, ck=FAKE, b=3, mq=10, mk=10, scale=0.1, causal=1, bt=NULL, maxblk=0, bs=0, nb=0,
+             hq=8, hkv=2, d=128, tq=14, tk=8, stream=NULL)
+    a.update(kw)
+    return pkv.library().pkv_varlen_prefill(
+        a["out"], a["q"], a["qdt"], a["k"], a["v"], a["kdt"], a["ksc"], a["vsc"], a["cq"], a["ck"],
+        a["b"], a["mq"], a["mk"], a["scale"], a["causal"], a["bt"], a["maxblk"], a["bs"], a["nb"],
+        a["hq"], a["hkv"], a["d"], a["tq"], a["tk"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(causal=2), pkv.ERR_INVALID),
+    (dict(mq=-1), pkv.ERR_INVALID),
+    (dict(hq=9, hkv=2), pkv.ERR_INVALID),
+    (dict(kdt=pkv.FP8_E4M3, ksc=FAKE, vsc=FAKE), pkv.ERR_UNSUPPORTED),   # fp8 needs the paged cache
+    (dict(bt=FAKE, maxblk=4, bs=24, nb=8), pkv.ERR_UNSUPPORTED),
+    (dict(bt=FAKE, maxblk=0, bs=16, nb=8), pkv.ERR_INVALID),
+    (dict(qdt=pkv.F32), pkv.ERR_UNSUPPORTED),
+    (dict(d=32), pkv.ERR_UNSUPPORTED),
+    (dict(cq=NULL), pkv.ERR_INVALID),
+    (dict(q=ODD), pkv.ERR_INVALID),
+])
+def test_prefill_rejects(kw, code):
+    assert prefill(**kw) == code
+
+
+def test_prefill_empty_batch_is_a_no_op():
+    assert prefill(b=0) == pkv.OK
+    assert prefill(mq=0) == pkv.OK
+
+
+def test_decode_workspace_plan():
+    # one split when everything fits in one unit -> no workspace
+    assert pkv.paged_decode_workspace_size(3, 8, 2, 64, 32, 4) == 0
+    # explicit split of 128 keys over 64 blocks of 16 -> 8 splits of (D + 2) floats per (b, h)
+    assert pkv.paged_decode_workspace_size(3, 8, 2, 128, 16, 64, 128) == 3 * 8 * 8 * 130 * 4
+    # automatic plan for the 8B-shaped decode: several splits per sequence
+    ws = pkv.paged_decode_workspace_size(64, 32, 8, 128, 16, 257)
+    assert ws > 0 and ws % (64 * 32 * 130 * 4) == 0
+    # unsupported argument -> 0
+    assert pkv.paged_decode_workspace_size(3, 8, 3, 128, 16, 4) == 0

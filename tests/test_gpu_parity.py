@@ -1,0 +1,284 @@
+"""GPU parity: libpkv through its C ABI against the fp64 oracle on the same bits.
+
+Bars: cache writes bit-exact over the whole cache; fp32 attention max abs
+error <= 1e-5; bf16 and fp8-cache attention <= 2e-2.  Full-size workloads are
+checked on sampled outputs (sampled (sequence, head) pairs or query rows that
+the oracle computes one by one), reduced copies of the same workloads in full.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_helpers import (TOL, GpuStep, assert_cache_equal, max_err, oracle_decode, oracle_prefill,
+                         oracle_write, out_f64, sample_pairs, sample_rows, say, to_dev)
+import paged_kv_cache_map_amd as pkv
+from oracle import paged
+
+pytestmark = pytest.mark.gpu
+
+
+def run_step_and_check(step, *, full=True, pairs=None, rows=None, split_keys=0):
+    say(step.name, "tokens", step.num_tokens, "blocks", step.num_blocks, "split", split_keys)
+    g = GpuStep(step)
+    g.write()
+    torch.cuda.synchronize()
+    kc, vc = oracle_write(step)
+    assert_cache_equal(g.k_cache, kc, step.cache_dtype, "k_cache")
+    assert_cache_equal(g.v_cache, vc, step.cache_dtype, "v_cache")
+    tol = TOL[step.cache_dtype]
+    errs = {}
+    if len(step.ids("prefill")):
+        say(step.name, "prefill")
+        out = out_f64(g.prefill())
+        cu = step.prefill_inputs()["cu_seqlens_q"]
+        use_rows = None if full else rows
+        want = oracle_prefill(step, kc, vc, rows=use_rows)
+        if use_rows is not None:
+            out, want = out[use_rows], want[use_rows]
+        errs["prefill"] = max_err(out, want)
+        assert errs["prefill"] <= tol, (step.name, errs)
+        assert int(cu[-1]) == out.shape[0] or use_rows is not None
+    if len(step.ids("decode")):
+        say(step.name, "decode")
+        out = out_f64(g.decode(split_keys))
+        use_pairs = None if full else pairs
+        want = oracle_decode(step, kc, vc, pairs=use_pairs)
+        if use_pairs is not None:
+            idx = tuple(np.array(use_pairs).T)
+            out, want = out[idx], want[idx]
+        errs["decode"] = max_err(out, want)
+        assert errs["decode"] <= tol, (step.name, errs)
+    print(step.name, errs, flush=True)
+    return g
+
+
+# ---------------------------------------------------------------------------
+# the named workloads
+# ---------------------------------------------------------------------------
+
+
+def test_tiny_decode_page_example():
+    step = workloads.config("tiny_decode")
+    assert list(step.slot_map) == [94, 32, 198]
+    run_step_and_check(step)
+
+
+def test_llama8b_decode_full():
+    run_step_and_check(workloads.config("llama8b_decode"))
+
+
+def test_varlen_prefill_prefix_reduced():
+    run_step_and_check(workloads.config("varlen_prefill_prefix", batch=5, q_hi=300, q_lo=1, p_hi=200))
+
+
+def test_varlen_prefill_prefix_full_sampled():
+    step = workloads.config("varlen_prefill_prefix")
+    rng = np.random.default_rng(0)
+    rows = sample_rows(rng, step.prefill_inputs()["cu_seqlens_q"], 96)
+    run_step_and_check(step, full=False, rows=rows)
+
+
+def test_llama70b_long_decode_sampled():
+    step = workloads.config("llama70b_long_decode")
+    pairs = sample_pairs(np.random.default_rng(1), 8, 64, 12)
+    run_step_and_check(step, full=False, pairs=pairs)
+
+
+def test_mixed_fp8_reduced():
+    step = workloads.config("mixed_fp8", prefill_chunks=3, chunk=200, decode_batch=12, p_hi=700,
+                            len_lo=1, len_hi=900)
+    run_step_and_check(step)
+
+
+def test_mixed_fp8_full_sampled():
+    step = workloads.config("mixed_fp8")
+    rng = np.random.default_rng(2)
+    rows = sample_rows(rng, step.prefill_inputs()["cu_seqlens_q"], 48)
+    pairs = sample_pairs(rng, 256, 32, 40)
+    run_step_and_check(step, full=False, rows=rows, pairs=pairs)
+
+
+# ---------------------------------------------------------------------------
+# decode: split plan, determinism, shapes, edge cases
+# ---------------------------------------------------------------------------
+
+
+def test_decode_split_invariance_and_determinism():
+    step = workloads.config("llama8b_decode", batch=6, len_lo=1, len_hi=1500)
+    g = GpuStep(step)
+    g.write()
+    kc, vc = oracle_write(step)
+    want = oracle_decode(step, kc, vc)
+    outs = {}
+    for sk in (0, 128, 256, 640, 4096):
+        say("split", sk)
+        outs[sk] = out_f64(g.decode(sk))
+        assert max_err(outs[sk], want) <= TOL["bf16"], sk
+    again = out_f64(g.decode(128))
+    assert np.array_equal(again, outs[128]), "run-to-run results differ"
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,dtype", [
+    (8, 8, 128, 16, "bf16"),     # MHA, G = 1
+    (8, 1, 128, 16, "bf16"),     # MQA, G = 8
+    (16, 1, 128, 32, "bf16"),    # G = 16 (two head groups)
+    (4, 2, 64, 8, "bf16"),       # G = 2, D = 64, bs = 8
+    (16, 4, 64, 64, "bf16"),
+    (8, 2, 128, 256, "bf16"),
+    (8, 2, 64, 16, "f32"),
+    (4, 1, 128, 16, "f32"),
+    (32, 8, 128, 16, "fp8"),
+    (8, 8, 64, 32, "fp8"),
+])
+def test_decode_shapes(hq, hkv, d, bs, dtype):
+    step = workloads.config("llama8b_decode", batch=5, len_lo=1, len_hi=700, num_heads=hq,
+                            num_kv_heads=hkv, head_dim=d, block_size=bs,
+                            cache_dtype=dtype) if dtype != "f32" else \
+        workloads.build_step("f32_decode", 77, num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                             block_size=bs, q_dtype="f32", cache_dtype="f32",
+                             prefix=[0, 5, 130, 333, 700], new=[1] * 5, kinds=["decode"] * 5)
+    run_step_and_check(step, split_keys=128)
+    run_step_and_check(step)
+
+
+def test_decode_zero_length_sequence_gives_zeros():
+    step = workloads.config("tiny_decode")
+    g = GpuStep(step)
+    g.write()
+    g.dec_len = to_dev(np.array([0, 33, 0], np.int32), "i32")
+    out = out_f64(g.decode())
+    assert np.all(out[0] == 0) and np.all(out[2] == 0)
+    kc, vc = oracle_write(step)
+    d = step.decode_inputs()
+    want = paged.paged_decode(d["q"], "f32", kc, vc, "f32", d["block_table"],
+                              np.array([0, 33, 0], np.int32), step.scale)
+    assert max_err(out, want) <= TOL["f32"]
+
+
+def test_block_permutation_gives_identical_bits():
+    """Same logical data in two different physical block arrangements."""
+    step = workloads.config("llama8b_decode", batch=4, len_lo=30, len_hi=400)
+    g1 = GpuStep(step)
+    g1.write()
+    a = g1.decode().cpu()
+    # relabel every physical block b -> perm[b]
+    perm = np.random.default_rng(9).permutation(step.num_blocks)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(len(perm))
+    step2 = workloads.config("llama8b_decode", batch=4, len_lo=30, len_hi=400)
+    step2.k_cache = step.k_cache[inv]
+    step2.v_cache = step.v_cache[inv]
+    step2.block_table = np.where(step.block_table >= 0, perm[np.maximum(step.block_table, 0)], -1)
+    step2.block_table = step2.block_table.astype(np.int32)
+    bs = step.block_size
+    step2.slot_map = (perm[step.slot_map // bs] * bs + step.slot_map % bs).astype(np.int32)
+    g2 = GpuStep(step2)
+    g2.write()
+    b = g2.decode().cpu()
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# prefill: the page-2 example, shapes, non-causal
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_page2_varlen_example_contiguous(dtype, causal):
+    c = workloads.page2_varlen_example(dtype=dtype)
+    say("page2 varlen", dtype, causal)
+    out = pkv.varlen_prefill(to_dev(c.q, dtype), to_dev(c.k, dtype), to_dev(c.v, dtype),
+                             to_dev(c.cu_seqlens_q, "i32"), to_dev(c.cu_seqlens_k, "i32"),
+                             c.max_seqlen_q, c.max_seqlen_k, c.scale, causal)
+    got = out_f64(out)
+    want = paged.varlen_prefill(c.q, dtype, c.k, c.v, dtype, c.cu_seqlens_q, c.cu_seqlens_k, c.scale,
+                                causal)
+    assert max_err(got, want) <= TOL[dtype]
+    # request 0 has no key: its ten rows are exactly zero
+    assert np.all(got[0:10] == 0)
+    if causal:
+        assert np.all(got[10:12] == 0)
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,dtype", [
+    (8, 8, 128, 16, "bf16"),
+    (16, 1, 128, 32, "bf16"),
+    (4, 2, 64, 8, "bf16"),
+    (8, 2, 64, 64, "fp8"),
+    (32, 8, 128, 16, "fp8"),
+    (4, 2, 64, 16, "f32"),
+])
+def test_prefill_shapes(hq, hkv, d, bs, dtype):
+    rng = np.random.default_rng(hq * 1000 + d + bs)
+    lq = rng.integers(1, 300, size=4)
+    pre = rng.integers(0, 260, size=4)
+    step = workloads.build_step("prefill_shape", 5000 + hq + d + bs, num_heads=hq, num_kv_heads=hkv,
+                                head_dim=d, block_size=bs,
+                                q_dtype="f32" if dtype == "f32" else "bf16", cache_dtype=dtype,
+                                prefix=pre, new=lq, kinds=["prefill"] * 4)
+    run_step_and_check(step)
+
+
+def test_prefill_noncausal_contiguous_matches_oracle():
+    c = workloads.random_varlen_contig("nc", 321, [70, 1, 200, 0, 33], [5, 260, 1, 9, 120],
+                                       num_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16")
+    for causal in (False, True):
+        out = pkv.varlen_prefill(to_dev(c.q, "bf16"), to_dev(c.k, "bf16"), to_dev(c.v, "bf16"),
+                                 to_dev(c.cu_seqlens_q, "i32"), to_dev(c.cu_seqlens_k, "i32"),
+                                 c.max_seqlen_q, c.max_seqlen_k, c.scale, causal)
+        want = paged.varlen_prefill(c.q, "bf16", c.k, c.v, "bf16", c.cu_seqlens_q, c.cu_seqlens_k,
+                                    c.scale, causal)
+        assert max_err(out_f64(out), want) <= TOL["bf16"], causal
+
+
+# ---------------------------------------------------------------------------
+# fp8 codec through the library
+# ---------------------------------------------------------------------------
+
+
+def test_fp8_write_every_bf16_pattern():
+    """All 65536 bf16 bit patterns (NaN and inf included) through the write,
+    per-head scales 1 and 1/3: codes equal the oracle's bit for bit."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    hkv, d = 2, 128
+    t = 65536 // (hkv * d)
+    k = bits.reshape(t, hkv, d)
+    v = bits[::-1].copy().reshape(t, hkv, d)
+    scale = np.array([1.0, 1.0 / 3.0], np.float32)
+    nb, bs = t // 16, 16
+    kc = np.zeros((nb, bs, hkv, d), np.uint8)
+    slots = np.random.default_rng(4).permutation(t).astype(np.int32)
+    want_k, want_v = paged.kv_cache_write(k, v, kc, kc, slots, "bf16", "fp8", scale, scale)
+    gk, gv = to_dev(kc, "fp8"), to_dev(kc, "fp8")
+    pkv.kv_cache_write(to_dev(k, "bf16"), to_dev(v, "bf16"), gk, gv, to_dev(slots, "i32"),
+                       to_dev(scale, "f32"), to_dev(scale, "f32"))
+    assert_cache_equal(gk, want_k, "fp8", "k")
+    assert_cache_equal(gv, want_v, "fp8", "v")
+
+
+def test_fp8_decode_every_code():
+    """A one-key sequence returns its V row exactly: every finite E4M3 code
+    decodes to its value (scale 1; values are exact in bf16)."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    hkv, d, bs = 1, 128, 16
+    n = len(codes)
+    seqs = (n + d - 1) // d
+    padded = np.resize(codes, seqs * d)
+    v = np.full((seqs, bs, hkv, d), 0x7F, np.uint8)
+    k = np.full((seqs, bs, hkv, d), 0x7F, np.uint8)
+    v[:, 0, 0, :] = padded.reshape(seqs, d)
+    k[:, 0, 0, :] = 0x38
+    table = np.arange(seqs, dtype=np.int32)[:, None]
+    ones = np.ones(1, np.float32)
+    q = np.full((seqs, 4, d), 0x3F80, np.uint16)
+    out = pkv.paged_decode(to_dev(q, "bf16"), to_dev(k, "fp8"), to_dev(v, "fp8"), to_dev(table, "i32"),
+                           to_dev(np.ones(seqs, np.int32), "i32"), 0.1, to_dev(ones, "f32"),
+                           to_dev(ones, "f32"))
+    got = out_f64(out)
+    from oracle import e4m3
+    want = e4m3.decode(padded).reshape(seqs, d)
+    for h in range(4):
+        assert np.array_equal(got[:, h, :], want)

@@ -228,3 +228,17 @@ def test_scale_is_applied_before_softmax():
     assert not np.allclose(a, paged.attention(q, k, v, 1.0, False))
     np.testing.assert_allclose(a, pins._sdpa(q, k, v, 2.0, False), rtol=1e-12)
     assert math.isfinite(float(a.sum()))
+
+
+def test_row_subset_equals_full_computation():
+    """Computing selected query rows gives exactly those rows of the full result."""
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((5 + 9, 4, 8)).astype(np.float32)
+    k = rng.standard_normal((7 + 20, 2, 8)).astype(np.float32)
+    v = rng.standard_normal((7 + 20, 2, 8)).astype(np.float32)
+    cu_q, cu_k = paged.cu_seqlens([5, 9]), paged.cu_seqlens([7, 20])
+    full = paged.varlen_prefill(q, "f32", k, v, "f32", cu_q, cu_k, 0.4, True)
+    rows = [0, 3, 6, 13]
+    part = paged.varlen_prefill(q, "f32", k, v, "f32", cu_q, cu_k, 0.4, True, rows=rows)
+    np.testing.assert_array_equal(part[rows], full[rows])
+    assert np.all(np.delete(part, rows, axis=0) == 0)

@@ -27,8 +27,8 @@ PAGED_CHECKS = [
 # (name, original text, planted text)
 PAGED_MUTATIONS = [
     ("gqa_modulo", "g = h // group", "g = h % hkv"),
-    ("causal_top_left", "visible = cols <= rows + (lk - lq)", "visible = cols <= rows"),
-    ("causal_strict", "visible = cols <= rows + (lk - lq)", "visible = cols < rows + (lk - lq)"),
+    ("causal_top_left", "visible = cols <= rows + (lk - chunk)", "visible = cols <= rows"),
+    ("causal_strict", "visible = cols <= rows + (lk - chunk)", "visible = cols < rows + (lk - chunk)"),
     ("scale_dropped", "logits = scale * (q[:, h, :] @ k[:, g, :].T)",
      "logits = (q[:, h, :] @ k[:, g, :].T)"),
     ("scale_after_softmax", "logits = scale * (q[:, h, :] @ k[:, g, :].T)",

@@ -72,13 +72,7 @@ def _normal(seed: int, stage: int, shape, dtype: str) -> np.ndarray:
         lo = c * _CHUNK
         out[lo:lo + size] = vals if dtype == "f32" else _f32_to_bf16_bits(vals)
 
-    workers = min(len(chunks), max(1, min(16, os.cpu_count() or 1)))
-    if workers == 1:
-        for ch in chunks:
-            fill(ch)
-    else:
-        with ThreadPoolExecutor(workers) as pool:
-            list(pool.map(fill, chunks))
+    _run_chunks(fill, chunks)
     return out.reshape(shape)
 
 
@@ -86,14 +80,28 @@ def _fp8_codes(seed: int, stage: int, shape) -> np.ndarray:
     """Codes drawn uniformly from the 254 finite E4M3 codes (0x7F, 0xFF excluded)."""
     n = int(np.prod(shape, dtype=np.int64))
     out = np.empty(n, dtype=np.uint8)
-    for c in range(max(1, math.ceil(n / _CHUNK))):
-        size = min(_CHUNK, n - c * _CHUNK)
+    chunks = [(c, min(_CHUNK, n - c * _CHUNK)) for c in range(max(1, math.ceil(n / _CHUNK)))]
+
+    def fill(chunk):
+        c, size = chunk
         if size <= 0:
-            break
+            return
         rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stage, c])))
         r = rng.integers(0, 254, size=size, dtype=np.int32)
         out[c * _CHUNK:c * _CHUNK + size] = np.where(r < 0x7F, r, r + 1).astype(np.uint8)
+
+    _run_chunks(fill, chunks)
     return out.reshape(shape)
+
+
+def _run_chunks(fill, chunks):
+    workers = min(len(chunks), max(1, min(16, os.cpu_count() or 1)))
+    if workers == 1:
+        for ch in chunks:
+            fill(ch)
+    else:
+        with ThreadPoolExecutor(workers) as pool:
+            list(pool.map(fill, chunks))
 
 
 # ---------------------------------------------------------------------------
