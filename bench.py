@@ -1,0 +1,289 @@
+"""Throughput of the paged-KV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs all|main]
+
+A step is one pass of the hot path over one batch: the KV write of the new
+tokens followed by the attention call(s) that read them (decode, prefill, or
+both for the mixed step).  The headline line measures the Llama-3.1-8B-shaped
+decode step (batch 64, 32/8 heads, head_dim 128, bf16, contexts U{512..4096},
+block size 16); `value` is that step's algorithmic HBM bytes (write + decode)
+per second.  Inputs are resident in HBM before timing starts; the KV pool is
+replicated and rotated so that consecutive steps never find it in the 256 MB
+Infinity Cache.  Kernel durations come from HIP events recorded on the stream
+the kernels run on.  One JSON line is printed.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "paged-decode HBM GB/s (% of peak); varlen prefill TFLOPS (% MFMA peak)"
+ROTATE_BYTES = 1 << 30         # replicate small pools to at least this many bytes
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--configs", default="all", choices=["all", "main"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (what the method must move / compute)
+# ---------------------------------------------------------------------------
+
+ELT = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def write_bytes(step):
+    """Read the new K/V rows, write them to the cache, read the slot map."""
+    row = step.num_kv_heads * step.head_dim
+    return step.num_tokens * (2 * row * (ELT[step.q_dtype] + ELT[step.cache_dtype]) + 4)
+
+
+def decode_bytes(step):
+    d = step.decode_inputs()
+    b = len(d["seq_ids"])
+    keys = int(d["cache_seqlens"].astype(np.int64).sum())
+    kv = keys * 2 * step.num_kv_heads * step.head_dim * ELT[step.cache_dtype]
+    qo = 2 * b * step.num_heads * step.head_dim * ELT[step.q_dtype]
+    meta = 4 * b + 4 * sum(-(-int(n) // step.block_size) for n in d["cache_seqlens"])
+    return kv + qo + meta
+
+
+def prefill_flops(step):
+    """4 * Hq * D per visible (query, key) pair: Q.K and P.V, 2 flops per MAC."""
+    p = step.prefill_inputs()
+    lq = np.diff(p["cu_seqlens_q"]).astype(np.int64)
+    lk = np.diff(p["cu_seqlens_k"]).astype(np.int64)
+    pre = lk - lq
+    pairs = int(np.sum(lq * pre + lq * (lq + 1) // 2))
+    return 4 * step.num_heads * step.head_dim * pairs
+
+
+# ---------------------------------------------------------------------------
+# GPU side
+# ---------------------------------------------------------------------------
+
+
+class Runner:
+    """A workload step on the GPU with `copies` rotated replicas of its KV pool."""
+
+    def __init__(self, step, copies=1):
+        import torch
+        from workloads.device import to_dev
+        self.torch = torch
+        self.s = step
+        self.copies = []
+        for _ in range(copies):
+            self.copies.append((to_dev(step.k_cache, step.cache_dtype),
+                                to_dev(step.v_cache, step.cache_dtype)))
+        self.k_new = to_dev(step.k_new, step.q_dtype)
+        self.v_new = to_dev(step.v_new, step.q_dtype)
+        self.slot_map = to_dev(step.slot_map, "i32")
+        self.k_scale = None if step.k_scale is None else to_dev(step.k_scale, "f32")
+        self.v_scale = None if step.v_scale is None else to_dev(step.v_scale, "f32")
+        d = step.decode_inputs()
+        self.has_decode = len(d["seq_ids"]) > 0
+        if self.has_decode:
+            import paged_kv_cache_map_amd as pkv
+            self.dq = to_dev(d["q"], step.q_dtype)
+            self.dbt = to_dev(d["block_table"], "i32")
+            self.dlen = to_dev(d["cache_seqlens"], "i32")
+            self.dout = torch.empty_like(self.dq)
+            nb, bs = step.k_cache.shape[:2]
+            need = pkv.paged_decode_workspace_size(self.dq.shape[0], step.num_heads,
+                                                   step.num_kv_heads, step.head_dim, bs,
+                                                   d["block_table"].shape[1])
+            self.dws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        p = step.prefill_inputs()
+        self.has_prefill = len(p["seq_ids"]) > 0
+        if self.has_prefill:
+            self.p = p
+            self.pq = to_dev(p["q"], step.q_dtype)
+            self.pcq = to_dev(p["cu_seqlens_q"], "i32")
+            self.pck = to_dev(p["cu_seqlens_k"], "i32")
+            self.pbt = to_dev(p["block_table"], "i32")
+            self.pout = torch.empty_like(self.pq)
+        torch.cuda.synchronize()
+
+    def run(self, i, ev=None):
+        import paged_kv_cache_map_amd as pkv
+        kc, vc = self.copies[i % len(self.copies)]
+        s = self.s
+        if ev is not None:
+            ev[0].record()
+        pkv.kv_cache_write(self.k_new, self.v_new, kc, vc, self.slot_map, self.k_scale, self.v_scale)
+        if ev is not None:
+            ev[1].record()
+        if self.has_prefill:
+            p = self.p
+            pkv.varlen_prefill(self.pq, kc, vc, self.pcq, self.pck, p["max_seqlen_q"],
+                               p["max_seqlen_k"], s.scale, True, self.pbt, self.k_scale,
+                               self.v_scale, out=self.pout)
+        if ev is not None:
+            ev[2].record()
+        if self.has_decode:
+            pkv.paged_decode(self.dq, kc, vc, self.dbt, self.dlen, s.scale, self.k_scale,
+                             self.v_scale, out=self.dout, workspace=self.dws)
+        if ev is not None:
+            ev[3].record()
+
+    def time(self, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            self.run(i)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.run(warmup + i, evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        write = [e[0].elapsed_time(e[1]) for e in evs]
+        pre = [e[1].elapsed_time(e[2]) for e in evs]
+        dec = [e[2].elapsed_time(e[3]) for e in evs]
+        return dict(ms_per_step=wall * 1e3 / steps,
+                    write_ms=float(np.mean(write)), write_ms_min=float(np.min(write)),
+                    prefill_ms=float(np.mean(pre)), prefill_ms_min=float(np.min(pre)),
+                    decode_ms=float(np.mean(dec)), decode_ms_min=float(np.min(dec)))
+
+
+def copies_for(step):
+    pool = step.k_cache.nbytes + step.v_cache.nbytes
+    return max(1, math.ceil(ROTATE_BYTES / pool))
+
+
+def measure(name, steps, warmup, **overrides):
+    import workloads
+    step = workloads.config(name, **overrides)
+    r = Runner(step, copies_for(step))
+    t = r.time(steps, warmup)
+    res = dict(t)
+    res["write_bytes"] = write_bytes(step)
+    res["write_gbs"] = res["write_bytes"] / (t["write_ms"] * 1e6)
+    if r.has_decode:
+        res["decode_bytes"] = decode_bytes(step)
+        res["decode_gbs"] = res["decode_bytes"] / (t["decode_ms"] * 1e6)
+        res["decode_frac_hbm"] = res["decode_gbs"] / HBM_PEAK_GBS
+    if r.has_prefill:
+        res["prefill_flops"] = prefill_flops(step)
+        res["prefill_tflops"] = res["prefill_flops"] / (t["prefill_ms"] * 1e9)
+        res["prefill_frac_mfma"] = res["prefill_tflops"] / BF16_PEAK_TFLOPS
+    del r
+    import torch
+    torch.cuda.empty_cache()
+    return step, res
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands
+# ---------------------------------------------------------------------------
+
+
+def cpu_baseline(step, algorithmic_bytes):
+    from oracle import paged
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001 - reporting only
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    kc, vc = paged.kv_cache_write(step.k_new, step.v_new, step.k_cache, step.v_cache, step.slot_map,
+                                  step.q_dtype, step.cache_dtype, step.k_scale, step.v_scale)
+    d = step.decode_inputs()
+    paged.paged_decode(d["q"], step.q_dtype, kc, vc, step.cache_dtype, d["block_table"],
+                       d["cache_seqlens"], step.scale, step.k_scale, step.v_scale)
+    secs = time.perf_counter() - t0
+    return {"value": round(algorithmic_bytes / secs / 1e9, 4), "unit": "GB/s",
+            "cores": min(cores, blas_threads), "kind": "oracle",
+            "sample": (f"one whole step of the same workload (write of {step.num_tokens} tokens + "
+                       f"decode of {len(d['seq_ids'])} sequences), fp64 numpy, {secs:.2f} s; "
+                       f"BLAS threads {blas_threads}, host CPUs available {cores}")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import paged_kv_cache_map_amd as pkv
+    pkv.library()
+
+    print("[bench] llama8b_decode", flush=True)
+    step, main_res = measure("llama8b_decode", args.steps, args.warmup)
+    step_bytes = main_res["write_bytes"] + main_res["decode_bytes"]
+    value = step_bytes / (main_res["ms_per_step"] * 1e6)
+    d = step.decode_inputs()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, random block permutation)",
+        "config": {"workload": "llama8b_decode: Llama-3.1-8B-shaped single-layer decode step "
+                               "(kv write + paged decode)",
+                   "batch": int(len(d["seq_ids"])), "num_heads": step.num_heads,
+                   "num_kv_heads": step.num_kv_heads, "head_dim": step.head_dim,
+                   "block_size": step.block_size,
+                   "context": "cached lengths U{512..4096} (+1 new token)",
+                   "keys_total": int(d["cache_seqlens"].sum()),
+                   "step_bytes": int(step_bytes)},
+        "roofline": {"kernel": "paged_decode (split kernel + merge kernel of one call)",
+                     "bound": "hbm", "achieved": round(main_res["decode_gbs"], 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(main_res["decode_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "algorithmic_bytes_per_launch": int(main_res["decode_bytes"]),
+                     "avg_launch_ms": round(main_res["decode_ms"], 5)},
+        "kernels": {"llama8b_decode": {k: (round(v, 5) if isinstance(v, float) else v)
+                                       for k, v in main_res.items()}},
+    }
+    if args.configs == "all":
+        for name, kw in (("varlen_prefill_prefix", {}), ("llama70b_long_decode", {}),
+                         ("mixed_fp8", {})):
+            print(f"[bench] {name}", flush=True)
+            _, res = measure(name, max(3, args.steps // 4), 2, **kw)
+            line["kernels"][name] = {k: (round(v, 5) if isinstance(v, float) else v)
+                                     for k, v in res.items()}
+        pre = line["kernels"]["varlen_prefill_prefix"]
+        line["secondary"] = {
+            "varlen_prefill_tflops": pre["prefill_tflops"],
+            "varlen_prefill_frac_mfma": pre["prefill_frac_mfma"],
+            "varlen_write_gbs": pre["write_gbs"],
+            "long_decode_gbs": line["kernels"]["llama70b_long_decode"]["decode_gbs"],
+            "mixed_fp8_decode_gbs": line["kernels"]["mixed_fp8"]["decode_gbs"],
+            "mixed_fp8_prefill_tflops": line["kernels"]["mixed_fp8"]["prefill_tflops"],
+        }
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", flush=True)
+        line["cpu_baseline"] = cpu_baseline(step, step_bytes)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,7 +17,12 @@ Calls (same names as the C entry points without the ``pkv_`` prefix):
 import ctypes
 import pathlib
 
-LIB_PATH = pathlib.Path(__file__).resolve().with_name("libpkv.so")
+import os
+
+# PKV_LIBRARY may name another build of the same library (A/B timing of
+# kernel variants); by default the in-tree build next to this file is used.
+LIB_PATH = pathlib.Path(os.environ.get("PKV_LIBRARY") or
+                        pathlib.Path(__file__).resolve().with_name("libpkv.so"))
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_LAUNCH = 0, -1, -2, -3

@@ -25,6 +25,10 @@
 // * P.V layout: lane = slice of head_dim; each key's V row is read by the whole
 //   wave with 4-byte (or 8-byte) loads, fully coalesced; p is broadcast from
 //   LDS.
+// * Addressing is scalar: a 16-key sub-step lies in one cache block, so the
+//   block's base address is formed once in SGPRs from the block table (staged
+//   in LDS) and each lane adds a fixed offset.  Masking is confined to the one
+//   chunk that crosses the end of the split.
 // * Loads of the next chunk are issued before the current chunk is computed
 //   (two register buffers), keeping 2 x 16 KiB per wave in flight.
 // * fp8 caches are dequantised in registers (exact E4M3 -> bf16); the K scale
@@ -44,19 +48,19 @@ constexpr float kNegBig = -1.0e30f;   // running-max start: finite, so exp2 neve
 template <int CT, int D, int GW>
 struct Cfg {
   static constexpr int elt = Elt<CT>::bytes;
-  static constexpr int row_bytes = D * elt;  // one KV head's row
-  // Q.K layout: 4 lanes per key
+  static constexpr int row_bytes = D * elt;        // one KV head's row of one slot
+  // Q.K layout: lane = 4 * key + quarter, 16 keys per sub-step
   static constexpr int qk_loads = row_bytes / 64;  // 16-byte loads per lane per key
   static constexpr int qk_elems = D / 4;
   // q words per head: bf16 pairs (bf16/fp8 caches) or fp32 values (fp32 cache)
   static constexpr int q_words = (CT == kF32) ? qk_elems : qk_elems / 2;
-  // P.V layout
-  static constexpr int pv_vec = (row_bytes / 64 > 4) ? row_bytes / 64 : 4;  // bytes per lane per key
-  static constexpr int pv_lanes = row_bytes / pv_vec;                        // lanes per key row
-  static constexpr int pv_kp = 64 / pv_lanes;                                // keys per load instr
-  static constexpr int pv_nv = pv_vec / elt;                                 // elements per lane
-  static constexpr int pv_loads = kChunk / pv_kp;                            // per chunk
-  static_assert(qk_loads >= 1 && pv_kp >= 1 && pv_kp <= 16, "shape");
+  // P.V layout: lane = (key kp, slice of head_dim); pv_vec bytes per lane per key
+  static constexpr int pv_vec = (row_bytes / 64 > 4) ? row_bytes / 64 : 4;
+  static constexpr int pv_lanes = row_bytes / pv_vec;  // lanes per key row
+  static constexpr int pv_kp = 64 / pv_lanes;          // keys per load instruction
+  static constexpr int pv_nv = pv_vec / elt;           // elements per lane
+  static constexpr int pv_loads = kChunk / pv_kp;      // load instructions per chunk
+  static_assert(qk_loads >= 1 && pv_kp >= 1 && pv_kp <= 8, "shape");
 };
 
 // Registers holding one chunk's K (Q.K layout) and V (P.V layout).
@@ -65,91 +69,140 @@ struct ChunkRegs {
   using C = Cfg<CT, D, GW>;
   uint4 k[2][C::qk_loads];
   uint32_t v[C::pv_loads][C::pv_vec / 4];
-  bool kok[2];  // this lane's key of each sub-step exists and sits in a valid block
+  bool clean;  // uniform: every key of the chunk exists and sits in a valid block
 };
 
 struct SeqCtx {
   const uint8_t* kbase;  // cache + g * row_bytes
   const uint8_t* vbase;
-  int64_t slot_stride;   // bytes between slots = num_kv_heads * row_bytes
-  const int32_t* tbl;    // LDS: block ids of the split, first entry = block blk0
-  int blk0;
-  int log2bs;
-  int bs_mask;
-  int lk;
+  int64_t block_bytes;   // block_size slots
+  int slot_stride;       // bytes between slots = num_kv_heads * row_bytes
+  const int32_t* tbl;    // LDS: block ids of the split (-1 = invalid), first = block blk0
+  int blk0, log2bs, bs, end;
+  uint32_t k_off;        // this lane's byte offset from its 8-key row group (Q.K)
+  uint32_t v_off;        // this lane's byte offset from the instruction's first key (P.V)
 };
 
-__device__ __forceinline__ int64_t slot_of_key(const SeqCtx& s, int key, bool& ok) {
-  const int blk = s.tbl[(key >> s.log2bs) - s.blk0];
-  ok = blk >= 0;
-  return ((int64_t)blk << s.log2bs) + (key & s.bs_mask);
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 raw buffer descriptor, dword 3
+
+// Uniform byte offset of `key` (a uniform key) from the cache base; keys at or
+// past the end and keys of invalid blocks map to slot 0 of block 0 (always
+// present) and report valid = false.
+__device__ __forceinline__ int64_t key_offset(const SeqCtx& s, int key, bool& valid) {
+  const bool in_range = key < s.end;
+  int blk = __builtin_amdgcn_readfirstlane(s.tbl[in_range ? (key >> s.log2bs) - s.blk0 : 0]);
+  valid = in_range && blk >= 0;
+  return valid ? (int64_t)blk * s.block_bytes + (int64_t)(key & (s.bs - 1)) * s.slot_stride : 0;
 }
 
-template <int CT, int D, int GW>
+// Buffer resource over 8 consecutive slots starting at base + off.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows8(const uint8_t* base, int64_t off, int stride) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), 0, 8 * stride, kBufferWord3);
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// A chunk's keys come as two 16-key sub-steps, each made of two 8-key row
+// groups that lie in one block (block_size >= 8).  A row group is addressed by
+// one buffer resource in SGPRs; every lane adds a fixed offset, so the loads
+// need no per-key address arithmetic.
+template <int CT, int D, int GW, bool SMALL>
 __device__ __forceinline__ void load_chunk(ChunkRegs<CT, D, GW>& r, const SeqCtx& s, int start,
                                            int lane) {
   using C = Cfg<CT, D, GW>;
-  const int kq = lane >> 2, quarter = lane & 3;
+  bool clean = start + kChunk <= s.end;
+  const bool hi_lane = (lane >> 2) >= 8;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
-    const int key = start + sb * 16 + kq;
-    bool ok = key < s.lk;
-    int64_t slot = 0;
-    if (ok) slot = slot_of_key(s, key, ok);
-    r.kok[sb] = ok;
-    const uint8_t* row = s.kbase + slot * s.slot_stride + quarter * 16;
+    const int key0 = start + sb * 16;
+    bool va, vb = true;
+    const int64_t off_a = key_offset(s, key0, va);
+    int64_t off_b;
+    if constexpr (!SMALL) {
+      off_b = off_a + 8 * (int64_t)s.slot_stride;
+    } else {
+      off_b = key_offset(s, key0 + 8, vb);
+    }
+    clean = clean && va && vb;
+    if constexpr (!SMALL) {
+      // block_size >= 16: the sub-step's 16 rows are one run of one block
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(s.kbase + off_a), 0, 16 * s.slot_stride, kBufferWord3);
 #pragma unroll
-    for (int i = 0; i < C::qk_loads; ++i) {
-      if (ok) {
-        r.k[sb][i] = *reinterpret_cast<const uint4*>(row + i * 64);
+      for (int i = 0; i < C::qk_loads; ++i) {
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(
+            kr, (int)(s.k_off + (hi_lane ? 8 * s.slot_stride : 0)), i * 64, 0);
+        r.k[sb][i] = make_uint4(x.x, x.y, x.z, x.w);
+      }
+    } else {
+      // block_size 8: keys 0..7 and 8..15 sit in two blocks; both loads are
+      // issued for every lane (lanes that share an address merge) and each
+      // lane keeps its own
+      const __amdgpu_buffer_rsrc_t ka = rows8(s.kbase, off_a, s.slot_stride);
+      const __amdgpu_buffer_rsrc_t kb = rows8(s.kbase, off_b, s.slot_stride);
+#pragma unroll
+      for (int i = 0; i < C::qk_loads; ++i) {
+        const u32x4_t xa = __builtin_amdgcn_raw_buffer_load_b128(ka, (int)s.k_off, i * 64, 0);
+        const u32x4_t xb = __builtin_amdgcn_raw_buffer_load_b128(kb, (int)s.k_off, i * 64, 0);
+        const u32x4_t x = hi_lane ? xb : xa;
+        r.k[sb][i] = make_uint4(x.x, x.y, x.z, x.w);
+      }
+    }
+    const __amdgpu_buffer_rsrc_t va_r = rows8(s.vbase, off_a, s.slot_stride);
+    const __amdgpu_buffer_rsrc_t vb_r = rows8(s.vbase, off_b, s.slot_stride);
+#pragma unroll
+    for (int j = 0; j < 16 / C::pv_kp; ++j) {
+      const int x = j * C::pv_kp;  // first key of the instruction within the sub-step
+      const int soff = (x & 7) * s.slot_stride;
+      const int i = sb * (16 / C::pv_kp) + j;
+      if constexpr (C::pv_vec == 4) {
+        r.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(x < 8 ? va_r : vb_r, (int)s.v_off, soff, 0);
       } else {
-        r.k[sb][i] = make_uint4(0u, 0u, 0u, 0u);
+        const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(x < 8 ? va_r : vb_r, (int)s.v_off, soff, 0);
+        r.v[i][0] = w.x;
+        r.v[i][1] = w.y;
       }
     }
   }
-  const int kp = lane / C::pv_lanes;
-  const int off = (lane % C::pv_lanes) * C::pv_vec;
-#pragma unroll
-  for (int i = 0; i < C::pv_loads; ++i) {
-    const int key = start + i * C::pv_kp + kp;
-    bool ok = key < s.lk;
-    int64_t slot = 0;
-    if (ok) slot = slot_of_key(s, key, ok);
-    const uint8_t* row = s.vbase + slot * s.slot_stride + off;
-#pragma unroll
-    for (int w = 0; w < C::pv_vec / 4; ++w) {
-      r.v[i][w] = ok ? reinterpret_cast<const uint32_t*>(row)[w] : 0u;
-    }
-  }
+  r.clean = clean;
 }
 
-// Partial dot product of one key's quarter row with head h's q words.
+// Partial dot product of one key's quarter row with head h's q (in LDS,
+// q_h = that head's row; the four quarters of a quad read four 16-byte pieces).
 template <int CT, int D, int GW>
 __device__ __forceinline__ float qk_partial(const uint4 (&k)[Cfg<CT, D, GW>::qk_loads],
-                                            const uint32_t* qh) {
+                                            const uint8_t* q_h, int quarter) {
   using C = Cfg<CT, D, GW>;
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < C::qk_loads; ++i) {
     const uint32_t kw[4] = {k[i].x, k[i].y, k[i].z, k[i].w};
     if constexpr (CT == kBF16) {
+      const uint4 qv = *reinterpret_cast<const uint4*>(q_h + i * 64 + quarter * 16);
+      const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc = dot2_bf16(qh[i * 4 + j], kw[j], acc);
+      for (int j = 0; j < 4; ++j) acc = dot2_bf16(qw[j], kw[j], acc);
     } else if constexpr (CT == kFP8) {
+      const uint4 q0 = *reinterpret_cast<const uint4*>(q_h + (i * 64 + quarter * 16) * 2);
+      const uint4 q1 = *reinterpret_cast<const uint4*>(q_h + (i * 64 + quarter * 16) * 2 + 16);
+      const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc = dot2_bf16(qh[i * 8 + 2 * j], e4m3x2_to_bf16x2<false>(kw[j]), acc);
-        acc = dot2_bf16(qh[i * 8 + 2 * j + 1], e4m3x2_to_bf16x2<true>(kw[j]), acc);
+        acc = dot2_bf16(qw[2 * j], e4m3x2_to_bf16x2<false>(kw[j]), acc);
+        acc = dot2_bf16(qw[2 * j + 1], e4m3x2_to_bf16x2<true>(kw[j]), acc);
       }
     } else {
+      const uint4 qv = *reinterpret_cast<const uint4*>(q_h + i * 64 + quarter * 16);
+      const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc = fmaf(__uint_as_float(qh[i * 4 + j]), __uint_as_float(kw[j]), acc);
+      for (int j = 0; j < 4; ++j) acc = fmaf(__uint_as_float(qw[j]), __uint_as_float(kw[j]), acc);
     }
   }
   return acc;
 }
 
-// The pv_nv fp32 values of one lane's V slice.
+// The pv_nv fp32 values of one lane's V slice of one key.
 template <int CT, int D, int GW>
 __device__ __forceinline__ void v_values(const uint32_t* w, float* out) {
   using C = Cfg<CT, D, GW>;
@@ -175,28 +228,38 @@ __device__ __forceinline__ void v_values(const uint32_t* w, float* out) {
   }
 }
 
+// Bytes of one q row as the kernel consumes it.
+template <int CT, int D>
+constexpr int kQRowBytes = D * (CT == kF32 ? 4 : 2);
+
 template <int CT, int D, int GW>
 struct WaveState {
   using C = Cfg<CT, D, GW>;
-  float m[GW];                 // running max (log2 domain), uniform across the wave
-  float l[GW];                 // per-lane partial sums of p (replicated within a quad)
-  float o[GW][C::pv_nv];       // per-lane partial outputs (keys = kp mod pv_kp)
+  float m[GW];               // running max (log2 domain), uniform across the wave
+  float l[GW];               // per-lane partial sums of p (replicated within a quad)
+  float o[GW][C::pv_nv];     // per-lane partial outputs (keys == kp mod pv_kp)
 };
 
-template <int CT, int D, int GW>
+// One chunk of 32 keys.  MASKED: some key is past the end or in an invalid
+// block (only the last chunk of a split, or a corrupt table).
+template <int CT, int D, int GW, bool MASKED>
 __device__ __forceinline__ void compute_chunk(WaveState<CT, D, GW>& st, const ChunkRegs<CT, D, GW>& r,
-                                              const uint32_t (&q)[GW][Cfg<CT, D, GW>::q_words],
-                                              float logit_scale, int lane,
-                                              float* p_lds) {
+                                              const uint8_t* q_lds, float logit_scale, int start,
+                                              const SeqCtx& sc, int lane, float* p_lds) {
   using C = Cfg<CT, D, GW>;
   const int kq = lane >> 2, quarter = lane & 3;
   float s[GW][2];
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
+    bool ok = true;
+    if constexpr (MASKED) {
+      const int key = start + sb * 16 + kq;
+      ok = key < sc.end && sc.tbl[key < sc.end ? (key >> sc.log2bs) - sc.blk0 : 0] >= 0;
+    }
 #pragma unroll
     for (int h = 0; h < GW; ++h) {
-      const float dot = quad_sum(qk_partial<CT, D, GW>(r.k[sb], q[h]));
-      s[h][sb] = r.kok[sb] ? dot * logit_scale : -INFINITY;
+      const float dot = quad_sum(qk_partial<CT, D, GW>(r.k[sb], q_lds + h * kQRowBytes<CT, D>, quarter));
+      s[h][sb] = ok ? dot * logit_scale : -INFINITY;
     }
   }
   float alpha[GW];
@@ -228,8 +291,17 @@ __device__ __forceinline__ void compute_chunk(WaveState<CT, D, GW>& st, const Ch
 #pragma unroll
   for (int i = 0; i < C::pv_loads; ++i) {
     const int key = i * C::pv_kp + kp;
+    uint32_t vw[C::pv_vec / 4];
+#pragma unroll
+    for (int w = 0; w < C::pv_vec / 4; ++w) vw[w] = r.v[i][w];
+    if constexpr (MASKED) {
+      const int k = start + key;
+      const bool ok = k < sc.end && sc.tbl[k < sc.end ? (k >> sc.log2bs) - sc.blk0 : 0] >= 0;
+#pragma unroll
+      for (int w = 0; w < C::pv_vec / 4; ++w) vw[w] = ok ? vw[w] : 0u;
+    }
     float vv[C::pv_nv];
-    v_values<CT, D, GW>(r.v[i], vv);
+    v_values<CT, D, GW>(vw, vv);
     float p[GW];
     if constexpr (GW % 4 == 0) {
 #pragma unroll
@@ -248,9 +320,23 @@ __device__ __forceinline__ void compute_chunk(WaveState<CT, D, GW>& st, const Ch
     for (int h = 0; h < GW; ++h)
 #pragma unroll
       for (int e = 0; e < C::pv_nv; ++e) st.o[h][e] = fmaf(p[h], vv[e], st.o[h][e]);
+    // keep the scheduler from hoisting every key's p broadcast (GW registers
+    // per key) to the top of the loop
+    if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+template <int CT, int D, int GW>
+__device__ __forceinline__ void compute_any(WaveState<CT, D, GW>& st, const ChunkRegs<CT, D, GW>& r,
+                                            const uint8_t* q_lds, float logit_scale, int start,
+                                            const SeqCtx& sc, int lane, float* p_lds) {
+  if (r.clean) {
+    compute_chunk<CT, D, GW, false>(st, r, q_lds, logit_scale, start, sc, lane, p_lds);
+  } else {
+    compute_chunk<CT, D, GW, true>(st, r, q_lds, logit_scale, start, sc, lane, p_lds);
+  }
 }
 
 template <int QT>
@@ -262,20 +348,24 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
   }
 }
 
-template <int CT, int D, int GW>
+template <int CT, int D, int GW, bool SMALL>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int split_keys, int num_splits,
                                                      int head_groups) {
   using C = Cfg<CT, D, GW>;
   constexpr int QT = (CT == kF32) ? kF32 : kBF16;
-  const int wave = threadIdx.x >> 6;
+  // wave index in a scalar register: the chunk loop is then uniform per wave
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int split = blockIdx.x;
-  const int g = blockIdx.y / head_groups;
-  const int h0 = g * (a.num_heads / a.num_kv_heads) + (blockIdx.y % head_groups) * GW;
+  // x = KV head (group): the heads of one (sequence, split) are dispatched
+  // together, so they read their slices of the same slot rows at the same time
+  const int split = blockIdx.y;
+  const int g = blockIdx.x / head_groups;
+  const int h0 = g * (a.num_heads / a.num_kv_heads) + (blockIdx.x % head_groups) * GW;
   const int b = blockIdx.z;
 
   __shared__ int32_t tbl[kDecodeMaxSplitKeys / 8 + 2];
-  __shared__ float p_lds[kWaves][kChunk * GW];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[GW * kQRowBytes<CT, D>];
+  __shared__ __attribute__((aligned(16))) float p_lds[kWaves][kChunk * GW];
   __shared__ float red_o[kWaves][GW][D];
   __shared__ float red_m[kWaves][GW];
   __shared__ float red_l[kWaves][GW];
@@ -297,30 +387,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int split_key
     const int id = a.block_table[(int64_t)b * a.max_blocks_per_seq + blk0 + i];
     tbl[i] = (id >= 0 && id < a.num_blocks) ? id : -1;
   }
+  if (threadIdx.x == 0 && nblk == 0) tbl[0] = -1;
 
-  // this wave's q words
-  uint32_t q[GW][C::q_words];
+  // the group's q rows, staged once in LDS (q dtype: fp32 with an fp32 cache, else bf16)
   {
-    const int quarter = lane & 3;
-#pragma unroll
-    for (int h = 0; h < GW; ++h) {
-      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
-                            ((int64_t)b * a.num_heads + h0 + h) * D * Elt<QT>::bytes;
-#pragma unroll
-      for (int i = 0; i < C::qk_loads; ++i) {
-        // this lane's elements of load i: [(i*64 + quarter*16)/elt, +16/elt)
-        const int e0 = (i * 64 + quarter * 16) / C::elt;
-        if constexpr (CT == kFP8) {
-          const uint4 lo = *reinterpret_cast<const uint4*>(qrow + e0 * 2);
-          const uint4 hi = *reinterpret_cast<const uint4*>(qrow + e0 * 2 + 16);
-          q[h][i * 8 + 0] = lo.x; q[h][i * 8 + 1] = lo.y; q[h][i * 8 + 2] = lo.z; q[h][i * 8 + 3] = lo.w;
-          q[h][i * 8 + 4] = hi.x; q[h][i * 8 + 5] = hi.y; q[h][i * 8 + 6] = hi.z; q[h][i * 8 + 7] = hi.w;
-        } else {
-          const uint4 x = *reinterpret_cast<const uint4*>(qrow + e0 * Elt<QT>::bytes);
-          q[h][i * 4 + 0] = x.x; q[h][i * 4 + 1] = x.y; q[h][i * 4 + 2] = x.z; q[h][i * 4 + 3] = x.w;
-        }
-      }
-    }
+    constexpr int qrow = kQRowBytes<CT, D>;
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)b * a.num_heads + h0) * qrow;
+    for (int i = threadIdx.x; i < GW * qrow / 16; i += blockDim.x)
+      reinterpret_cast<uint4*>(q_lds)[i] = reinterpret_cast<const uint4*>(src)[i];
   }
   float logit_scale = a.softmax_scale * kLog2e;
   float out_scale = 1.0f;
@@ -331,15 +405,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int split_key
   __syncthreads();
 
   SeqCtx sc;
-  const int64_t row_bytes = C::row_bytes;
+  const int row_bytes = C::row_bytes;
   sc.kbase = a.k_cache + g * row_bytes;
   sc.vbase = a.v_cache + g * row_bytes;
-  sc.slot_stride = (int64_t)a.num_kv_heads * row_bytes;
+  sc.slot_stride = a.num_kv_heads * row_bytes;
+  sc.block_bytes = (int64_t)a.block_size * sc.slot_stride;
   sc.tbl = tbl;
   sc.blk0 = blk0;
   sc.log2bs = log2bs;
-  sc.bs_mask = a.block_size - 1;
-  sc.lk = end;
+  sc.bs = a.block_size;
+  sc.end = end;
+  {
+    const int kq = lane >> 2, quarter = lane & 3;
+    sc.k_off = (uint32_t)((kq & 7) * sc.slot_stride + quarter * 16);  // within an 8-row group
+    sc.v_off = (uint32_t)((lane / C::pv_lanes) * sc.slot_stride + (lane % C::pv_lanes) * C::pv_vec);
+  }
 
   WaveState<CT, D, GW> st;
 #pragma unroll
@@ -354,19 +434,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int split_key
   const int stride = kWaves * kChunk;
   int c = start + wave * kChunk;
   if (c < end) {
+    // Two register buffers; the next chunk's loads are always issued (past
+    // the end they read a safe row and are masked), so every wait is exact.
     ChunkRegs<CT, D, GW> A, B;
-    load_chunk<CT, D, GW>(A, sc, c, lane);
-    while (true) {
-      const bool more = c + stride < end;
-      if (more) load_chunk<CT, D, GW>(B, sc, c + stride, lane);
-      compute_chunk<CT, D, GW>(st, A, q, logit_scale, lane, my_p);
-      if (!more) break;
+    load_chunk<CT, D, GW, SMALL>(A, sc, c, lane);
+    for (;;) {
+      load_chunk<CT, D, GW, SMALL>(B, sc, c + stride, lane);
+      compute_any<CT, D, GW>(st, A, q_lds, logit_scale, c, sc, lane, my_p);
       c += stride;
-      const bool more2 = c + stride < end;
-      if (more2) load_chunk<CT, D, GW>(A, sc, c + stride, lane);
-      compute_chunk<CT, D, GW>(st, B, q, logit_scale, lane, my_p);
-      if (!more2) break;
+      if (c >= end) break;
+      load_chunk<CT, D, GW, SMALL>(A, sc, c + stride, lane);
+      compute_any<CT, D, GW>(st, B, q_lds, logit_scale, c, sc, lane, my_p);
       c += stride;
+      if (c >= end) break;
     }
   }
 
@@ -463,9 +543,14 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int split_keys
 template <int CT, int D, int GW>
 hipError_t launch_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
   constexpr int QT = (CT == kF32) ? kF32 : kBF16;
-  const dim3 grid(p.num_splits, a.num_kv_heads * p.head_groups, a.batch);
-  hipLaunchKernelGGL((decode_kernel<CT, D, GW>), grid, dim3(256), 0, stream, a, p.split_keys,
-                     p.num_splits, p.head_groups);
+  const dim3 grid(a.num_kv_heads * p.head_groups, p.num_splits, a.batch);
+  if (a.block_size < 16) {
+    hipLaunchKernelGGL((decode_kernel<CT, D, GW, true>), grid, dim3(256), 0, stream, a, p.split_keys,
+                       p.num_splits, p.head_groups);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<CT, D, GW, false>), grid, dim3(256), 0, stream, a, p.split_keys,
+                       p.num_splits, p.head_groups);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.num_splits == 1) return e;
   const int64_t rows = (int64_t)a.batch * a.num_heads;

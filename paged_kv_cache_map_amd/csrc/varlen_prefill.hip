@@ -42,6 +42,7 @@ constexpr int BN = 64;    // keys per tile
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
+constexpr int kWaitVmcnt0 = 0x0f70;  // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)
 
 template <int D>
 struct Lds {
@@ -56,37 +57,30 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// 8 x 8 bf16 transpose: r[i] holds 8 elements of row i; out[e] holds element
-// e of rows 0..7.
-__device__ __forceinline__ void transpose8x8(const uint4 (&r)[8], uint4 (&out)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint32_t w[4];
-#pragma unroll
-    for (int kp = 0; kp < 4; ++kp) {
-      const uint4 a = r[2 * kp], b = r[2 * kp + 1];
-      const uint32_t aw = (e >> 1) == 0 ? a.x : (e >> 1) == 1 ? a.y : (e >> 1) == 2 ? a.z : a.w;
-      const uint32_t bw = (e >> 1) == 0 ? b.x : (e >> 1) == 1 ? b.y : (e >> 1) == 2 ? b.z : b.w;
-      w[kp] = perm(bw, aw, (e & 1) ? 0x07060302u : 0x05040100u);
-    }
-    out[e] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
 // Eight E4M3 codes (two words) -> eight bf16 (four words), exact.
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return make_uint4(e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
                     e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1));
 }
 
+__device__ __forceinline__ uint32_t word_of(const uint4& x, int i) {
+  return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
+}
+
+// bf16 element e (0..7) of rows a and b packed as (a[e], b[e]).
+__device__ __forceinline__ uint32_t pair_elem(const uint4& a, const uint4& b, int e) {
+  return perm(word_of(b, e >> 1), word_of(a, e >> 1), (e & 1) ? 0x07060302u : 0x05040100u);
+}
+
 struct KeyAddr {
   const uint8_t* base;  // k or v + g * row_bytes (+ k_start rows when contiguous)
   int64_t row_stride;   // bytes between consecutive slots / rows
   const int32_t* table; // paged: block_table row of the request, else nullptr
-  int log2bs, bs_mask, num_blocks, lk;
+  int log2bs, bs_mask, num_blocks, lk, max_blocks;
 };
 
-// Address of key j's row (nullptr if the key does not exist).
+// Address of key j's row (nullptr if the key does not exist).  Used by the
+// fp32 kernel only.
 __device__ __forceinline__ const uint8_t* key_row(const KeyAddr& ka, int j) {
   if (j >= ka.lk) return nullptr;
   if (ka.table == nullptr) return ka.base + (int64_t)j * ka.row_stride;
@@ -95,87 +89,119 @@ __device__ __forceinline__ const uint8_t* key_row(const KeyAddr& ka, int j) {
   return ka.base + (((int64_t)blk << ka.log2bs) + (j & ka.bs_mask)) * ka.row_stride;
 }
 
-// Registers of one tile in flight between its global loads and its LDS stores.
+// How the 256 threads of a workgroup move one 64-key tile from HBM to LDS.
+// K: each thread copies `kp` 16-byte pieces (consecutive threads cover a row
+// contiguously).  V: each thread owns a block of `kr` keys x 8 head-dim
+// elements, transposes it in registers and writes it into V^T; threads that
+// share an 8-element group are adjacent so their LDS writes hit distinct banks.
 template <int KVT, int D>
-struct TileRegs {
+struct Loader {
   static constexpr int elt = Elt<KVT>::bytes;
-  static constexpr int k_pieces = D * elt / 16;            // 16-byte pieces per K row
-  static constexpr int k_per_thread = BN * k_pieces / 128;  // threads 0..127 load K
-  static constexpr int v_vec = 8 * elt;                      // bytes of 8 elements
-  static constexpr int v_blocks = (BN / 8) * (D / 8);        // 8x8 blocks, threads 128.. load V
-  uint4 k[k_per_thread];
-  uint4 v[8];   // bf16: 8 rows x 16 B; fp8: 8 rows x 8 B in .x/.y
-};
+  static constexpr int ppr = D * elt / 16;          // 16-byte pieces per K row
+  static constexpr int kp = BN * ppr / kThreads;    // K pieces per thread
+  static constexpr int kstep = kThreads / ppr;      // rows between a thread's K pieces
+  static constexpr int dg = D / 8;                  // 8-element groups per V row
+  static constexpr int kr = BN * dg / kThreads;     // V rows per thread
+  static constexpr int kgroups = BN / kr;           // key groups per 8-element group
+  static_assert(kp >= 1 && (kr == 2 || kr == 4), "tile shape");
 
-template <int KVT, int D>
-__device__ __forceinline__ void tile_load(TileRegs<KVT, D>& r, const KeyAddr& ka, const KeyAddr& va,
-                                          int key0, int tid) {
-  using T = TileRegs<KVT, D>;
-  if (tid < 128) {
+  // per tile in flight
+  uint4 kd[kp];
+  uint4 vd[kr];
+  uint32_t ok;        // validity bit per K piece (bits 0..kp-1) and V row (bits 8..)
+  int32_t tk[kp];     // block ids (paged) of the next tile to load
+  int32_t tv;
+
+  __device__ __forceinline__ int k_row(int tid, int i) const { return tid / ppr + kstep * i; }
+  __device__ __forceinline__ int k_piece(int tid) const { return tid % ppr; }
+  __device__ __forceinline__ int v_group(int tid) const { return tid / kgroups; }   // 8-element group
+  __device__ __forceinline__ int v_key0(int tid) const { return (tid % kgroups) * kr; }
+
+  // Block-table entries of tile `key0` (global loads, consumed one tile later).
+  __device__ __forceinline__ void fetch_table(const KeyAddr& a, int key0, int tid) {
+    if (a.table == nullptr) return;
 #pragma unroll
-    for (int i = 0; i < T::k_per_thread; ++i) {
-      const int p = tid + 128 * i;
-      const int row = p / T::k_pieces, piece = p % T::k_pieces;
-      const uint8_t* src = key_row(ka, key0 + row);
-      r.k[i] = src ? *reinterpret_cast<const uint4*>(src + piece * 16) : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < kp; ++i) {
+      const int j = key0 + k_row(tid, i);
+      tk[i] = a.table[min(j >> a.log2bs, a.max_blocks - 1)];
     }
-  } else {
-    const int u = tid - 128;
-    if (u < T::v_blocks) {
-      const int kg = u / (D / 8), pc = u % (D / 8);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint8_t* src = key_row(va, key0 + kg * 8 + i);
-        if constexpr (KVT == kBF16) {
-          r.v[i] = src ? *reinterpret_cast<const uint4*>(src + pc * 16) : make_uint4(0u, 0u, 0u, 0u);
-        } else {
-          const uint2 x = src ? *reinterpret_cast<const uint2*>(src + pc * 8) : make_uint2(0u, 0u);
-          r.v[i] = make_uint4(x.x, x.y, 0u, 0u);
-        }
-      }
-    }
+    const int j = key0 + v_key0(tid);
+    tv = a.table[min(j >> a.log2bs, a.max_blocks - 1)];
   }
-}
 
-template <int KVT, int D>
-__device__ __forceinline__ void tile_store(const TileRegs<KVT, D>& r, uint16_t* buf, int tid) {
-  using T = TileRegs<KVT, D>;
-  using L = Lds<D>;
-  if (tid < 128) {
+  // Offset of key j given its block id; `valid` false -> offset 0 (a safe row).
+  __device__ __forceinline__ int64_t offset(const KeyAddr& a, int j, int blk, bool& valid) const {
+    if (a.table == nullptr) {
+      valid = j < a.lk;
+      return valid ? (int64_t)j * a.row_stride : 0;
+    }
+    valid = j < a.lk && blk >= 0 && blk < a.num_blocks;
+    return valid ? ((((int64_t)blk) << a.log2bs) + (j & a.bs_mask)) * a.row_stride : 0;
+  }
+
+  // Issue the global loads of tile `key0` with the table entries fetched earlier.
+  __device__ __forceinline__ void load(const KeyAddr& ka, const KeyAddr& va, int key0, int tid) {
+    ok = 0;
 #pragma unroll
-    for (int i = 0; i < T::k_per_thread; ++i) {
-      const int p = tid + 128 * i;
-      const int row = p / T::k_pieces, piece = p % T::k_pieces;
+    for (int i = 0; i < kp; ++i) {
+      bool valid;
+      const int64_t off = offset(ka, key0 + k_row(tid, i), tk[i], valid);
+      kd[i] = *reinterpret_cast<const uint4*>(ka.base + off + k_piece(tid) * 16);
+      ok |= (uint32_t)valid << i;
+    }
+    const int j0 = key0 + v_key0(tid);
+#pragma unroll
+    for (int r = 0; r < kr; ++r) {
+      bool valid;
+      const int64_t off = offset(va, j0 + r, tv, valid);
+      const uint8_t* src = va.base + off + v_group(tid) * 8 * elt;
       if constexpr (KVT == kBF16) {
-        *reinterpret_cast<uint4*>(buf + row * L::k_row + piece * 8) = r.k[i];
+        vd[r] = *reinterpret_cast<const uint4*>(src);
       } else {
-        uint16_t* dst = buf + row * L::k_row + piece * 16;
-        *reinterpret_cast<uint4*>(dst) = e4m3x8_to_bf16x8(r.k[i].x, r.k[i].y);
-        *reinterpret_cast<uint4*>(dst + 8) = e4m3x8_to_bf16x8(r.k[i].z, r.k[i].w);
+        const uint2 x = *reinterpret_cast<const uint2*>(src);
+        vd[r] = make_uint4(x.x, x.y, 0u, 0u);
       }
-    }
-  } else {
-    const int u = tid - 128;
-    if (u < T::v_blocks) {
-      const int kg = u / (D / 8), pc = u % (D / 8);
-      uint4 rows[8], cols[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if constexpr (KVT == kBF16) {
-          rows[i] = r.v[i];
-        } else {
-          rows[i] = e4m3x8_to_bf16x8(r.v[i].x, r.v[i].y);
-        }
-      }
-      transpose8x8(rows, cols);
-      uint16_t* vt = buf + L::k_elems;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint2*>(vt + (pc * 8 + e) * L::vt_row + kg * 8) = make_uint2(cols[e].x, cols[e].y),
-        *reinterpret_cast<uint2*>(vt + (pc * 8 + e) * L::vt_row + kg * 8 + 4) = make_uint2(cols[e].z, cols[e].w);
+      ok |= (uint32_t)valid << (8 + r);
     }
   }
-}
+
+  // Zero invalid rows, dequantise fp8, transpose V, write the tile to LDS.
+  __device__ __forceinline__ void store(uint16_t* buf, int tid) const {
+    using L = Lds<D>;
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < kp; ++i) {
+      const uint4 x = ((ok >> i) & 1) ? kd[i] : zero;
+      uint16_t* dst = buf + k_row(tid, i) * L::k_row + k_piece(tid) * (16 / elt);
+      if constexpr (KVT == kBF16) {
+        *reinterpret_cast<uint4*>(dst) = x;
+      } else {
+        *reinterpret_cast<uint4*>(dst) = e4m3x8_to_bf16x8(x.x, x.y);
+        *reinterpret_cast<uint4*>(dst + 8) = e4m3x8_to_bf16x8(x.z, x.w);
+      }
+    }
+    uint4 rows[kr];
+#pragma unroll
+    for (int r = 0; r < kr; ++r) {
+      const uint4 x = ((ok >> (8 + r)) & 1) ? vd[r] : zero;
+      if constexpr (KVT == kBF16) {
+        rows[r] = x;
+      } else {
+        rows[r] = e4m3x8_to_bf16x8(x.x, x.y);
+      }
+    }
+    uint16_t* vt = buf + L::k_elems + v_group(tid) * 8 * L::vt_row + v_key0(tid);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (kr == 4) {
+        *reinterpret_cast<uint2*>(vt + e * L::vt_row) =
+            make_uint2(pair_elem(rows[0], rows[1], e), pair_elem(rows[2], rows[3], e));
+      } else {
+        *reinterpret_cast<uint32_t*>(vt + e * L::vt_row) = pair_elem(rows[0], rows[1], e);
+      }
+    }
+  }
+};
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
 
@@ -187,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int q_
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::buf_elems];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
 
   // XCD-aware renumbering: hardware workgroup i runs on XCD i % 8; give each
@@ -198,12 +224,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int q_
   if (logical >= total_wg) return;
   const int group = a.num_heads / a.num_kv_heads;
   const int qt = logical % q_tiles;
-  int rest = logical / q_tiles;
+  const int rest = logical / q_tiles;
   const int h = rest % a.num_heads;  // q heads of one KV head are adjacent
   const int b = rest / a.num_heads;
   const int g = h / group;
 
-  int q_start = a.cu_seqlens_q[b];
+  const int q_start = a.cu_seqlens_q[b];
   int lq = a.cu_seqlens_q[b + 1] - q_start;
   if (lq > a.max_seqlen_q) lq = a.max_seqlen_q;
   if (q_start < 0 || q_start >= a.total_q) lq = 0;
@@ -237,6 +263,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int q_
   ka.log2bs = va.log2bs = paged ? __builtin_ctz(a.block_size) : 0;
   ka.bs_mask = va.bs_mask = paged ? a.block_size - 1 : 0;
   ka.num_blocks = va.num_blocks = a.num_blocks;
+  ka.max_blocks = va.max_blocks = a.max_blocks_per_seq;
   ka.lk = va.lk = lk;
 
   // this wave's query column: row q0 + 32 * wave + col
@@ -245,10 +272,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int q_
   uint4 qf[KS];
   {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         ((int64_t)(q_start + qrow) * a.num_heads + h) * D + half * 8;
+                         ((int64_t)(q_start + (qvalid ? qrow : 0)) * a.num_heads + h) * D + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = qvalid ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0u, 0u, 0u, 0u);
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 x = *reinterpret_cast<const uint4*>(qp + ks * 16);
+      qf[ks] = qvalid ? x : make_uint4(0u, 0u, 0u, 0u);
+    }
+    // Resolve the q loads here: otherwise the wait for them lands inside the
+    // tile loop, where it also waits for the next tile's prefetch.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
   float scale = a.softmax_scale * kLog2e;
   float out_scale = 1.0f;
@@ -262,15 +294,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int q_
   for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
   float m = kNegBig, l = 0.0f;
 
-  TileRegs<KVT, D> regs;
+  Loader<KVT, D> ld;
   if (n_tiles > 0) {
-    tile_load<KVT, D>(regs, ka, va, 0, tid);
-    tile_store<KVT, D>(regs, lds, tid);
+    ld.fetch_table(ka, 0, tid);
+    ld.load(ka, va, 0, tid);
+    if (n_tiles > 1) ld.fetch_table(ka, BN, tid);
+    ld.store(lds, tid);
   }
   for (int t = 0; t < n_tiles; ++t) {
     __syncthreads();
     const int key0 = t * BN;
-    if (t + 1 < n_tiles) tile_load<KVT, D>(regs, ka, va, key0 + BN, tid);
+    if (t + 1 < n_tiles) {
+      ld.load(ka, va, key0 + BN, tid);
+      if (t + 2 < n_tiles) ld.fetch_table(ka, key0 + 2 * BN, tid);
+    }
     const uint16_t* kb_lds = lds + (t & 1) * L::buf_elems;
     const uint16_t* vt_lds = kb_lds + L::k_elems;
 
@@ -289,19 +326,27 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int q_
     // scale, mask, row max
     const bool need_mask = (key0 + BN > lk) || (a.causal && key0 + BN - 1 > q0 + wave * 32 + offset);
     float mx = kNegBig;
+    if (need_mask) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[kb][r] * scale;
-        if (need_mask) {
+        for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
           const bool vis = key < lk && (!a.causal || key <= qrow + offset);
-          x = vis ? x : -INFINITY;
+          const float x = vis ? s[kb][r] * scale : -INFINITY;
+          s[kb][r] = x;
+          mx = fmaxf(mx, x);
         }
-        s[kb][r] = x;
-        mx = fmaxf(mx, x);
-      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = s[kb][r] * scale;
+          s[kb][r] = x;
+          mx = fmaxf(mx, x);
+        }
+    }
     mx = fmaxf(mx, shfl_xor(mx, 32));
     const float mn = fmaxf(m, mx);
     const float alpha = fast_exp2(m - mn);
@@ -339,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int q_
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pb[kb][hs]), o[db], 0, 0, 0);
         }
     }
-    if (t + 1 < n_tiles) tile_store<KVT, D>(regs, lds + ((t + 1) & 1) * L::buf_elems, tid);
+    if (t + 1 < n_tiles) ld.store(lds + ((t + 1) & 1) * L::buf_elems, tid);
   }
 
   // normalise and store: lane holds O^T rows 8*(r/4) + 4*half + r%4 of each 32-row block

@@ -8,6 +8,7 @@ import torch
 
 import paged_kv_cache_map_amd as pkv
 from oracle import paged
+from workloads.device import to_dev, to_host  # noqa: F401
 
 DEV = "cuda"
 TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 2e-2}   # max abs error vs the fp64 oracle
@@ -17,32 +18,6 @@ def say(*parts):
     """Name the case before a GPU step (flushed, so it survives a crash)."""
     print("[gpu]", *parts, flush=True)
     sys.stdout.flush()
-
-
-def to_dev(arr, dtype):
-    arr = np.ascontiguousarray(arr)
-    if dtype == "bf16":
-        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16)
-    elif dtype == "f32":
-        t = torch.from_numpy(arr.astype(np.float32, copy=False))
-    elif dtype == "fp8":
-        t = torch.from_numpy(arr.astype(np.uint8, copy=False))
-    elif dtype == "i32":
-        t = torch.from_numpy(arr.astype(np.int32, copy=False))
-    else:
-        raise ValueError(dtype)
-    return t.to(DEV)
-
-
-def to_host(t, dtype):
-    t = t.detach().cpu()
-    if dtype == "bf16":
-        return t.view(torch.int16).numpy().view(np.uint16)
-    if dtype == "f32":
-        return t.numpy()
-    if dtype == "fp8":
-        return t.view(torch.uint8).numpy()
-    raise ValueError(dtype)
 
 
 def out_f64(t):
