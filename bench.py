@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--configs", default="all", choices=["all", "main"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--split-keys", type=int, default=0,
+                    help="decode split size in keys (0: the library's automatic plan)")
     return ap.parse_args()
 
 
@@ -82,11 +84,12 @@ def prefill_flops(step):
 class Runner:
     """A workload step on the GPU with `copies` rotated replicas of its KV pool."""
 
-    def __init__(self, step, copies=1):
+    def __init__(self, step, copies=1, split_keys=0):
         import torch
         from workloads.device import to_dev
         self.torch = torch
         self.s = step
+        self.split_keys = split_keys
         self.copies = []
         for _ in range(copies):
             self.copies.append((to_dev(step.k_cache, step.cache_dtype),
@@ -107,7 +110,7 @@ class Runner:
             nb, bs = step.k_cache.shape[:2]
             need = pkv.paged_decode_workspace_size(self.dq.shape[0], step.num_heads,
                                                    step.num_kv_heads, step.head_dim, bs,
-                                                   d["block_table"].shape[1])
+                                                   d["block_table"].shape[1], split_keys)
             self.dws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
         p = step.prefill_inputs()
         self.has_prefill = len(p["seq_ids"]) > 0
@@ -138,7 +141,8 @@ class Runner:
             ev[2].record()
         if self.has_decode:
             pkv.paged_decode(self.dq, kc, vc, self.dbt, self.dlen, s.scale, self.k_scale,
-                             self.v_scale, out=self.dout, workspace=self.dws)
+                             self.v_scale, out=self.dout, split_keys=self.split_keys,
+                             workspace=self.dws)
         if ev is not None:
             ev[3].record()
 
@@ -167,10 +171,10 @@ def copies_for(step):
     return max(1, math.ceil(ROTATE_BYTES / pool))
 
 
-def measure(name, steps, warmup, **overrides):
+def measure(name, steps, warmup, split_keys=0, **overrides):
     import workloads
     step = workloads.config(name, **overrides)
-    r = Runner(step, copies_for(step))
+    r = Runner(step, copies_for(step), split_keys)
     t = r.time(steps, warmup)
     res = dict(t)
     res["write_bytes"] = write_bytes(step)
@@ -228,7 +232,7 @@ def main():
     pkv.library()
 
     print("[bench] llama8b_decode", flush=True)
-    step, main_res = measure("llama8b_decode", args.steps, args.warmup)
+    step, main_res = measure("llama8b_decode", args.steps, args.warmup, args.split_keys)
     step_bytes = main_res["write_bytes"] + main_res["decode_bytes"]
     value = step_bytes / (main_res["ms_per_step"] * 1e6)
     d = step.decode_inputs()
@@ -267,7 +271,7 @@ def main():
         for name, kw in (("varlen_prefill_prefix", {}), ("llama70b_long_decode", {}),
                          ("mixed_fp8", {})):
             print(f"[bench] {name}", flush=True)
-            _, res = measure(name, max(3, args.steps // 4), 2, **kw)
+            _, res = measure(name, max(3, args.steps // 4), 2, args.split_keys, **kw)
             line["kernels"][name] = {k: (round(v, 5) if isinstance(v, float) else v)
                                      for k, v in res.items()}
         pre = line["kernels"]["varlen_prefill_prefix"]

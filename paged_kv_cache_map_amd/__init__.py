@@ -15,9 +15,8 @@ Calls (same names as the C entry points without the ``pkv_`` prefix):
 """
 
 import ctypes
-import pathlib
-
 import os
+import pathlib
 
 # PKV_LIBRARY may name another build of the same library (A/B timing of
 # kernel variants); by default the in-tree build next to this file is used.

@@ -69,7 +69,7 @@ struct ChunkRegs {
   using C = Cfg<CT, D, GW>;
   uint4 k[2][C::qk_loads];
   uint32_t v[C::pv_loads][C::pv_vec / 4];
-  bool clean;  // uniform: every key of the chunk exists and sits in a valid block
+  uint32_t kmask;  // uniform: bit k set iff key start + k exists and sits in a valid block
 };
 
 struct SeqCtx {
@@ -111,7 +111,7 @@ template <int CT, int D, int GW, bool SMALL>
 __device__ __forceinline__ void load_chunk(ChunkRegs<CT, D, GW>& r, const SeqCtx& s, int start,
                                            int lane) {
   using C = Cfg<CT, D, GW>;
-  bool clean = start + kChunk <= s.end;
+  uint32_t kmask = 0;
   const bool hi_lane = (lane >> 2) >= 8;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
@@ -124,7 +124,8 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<CT, D, GW>& r, const SeqCtx
     } else {
       off_b = key_offset(s, key0 + 8, vb);
     }
-    clean = clean && va && vb;
+    kmask |= (va ? 0xffu : 0u) << (16 * sb);
+    kmask |= (vb ? 0xffu : 0u) << (16 * sb + 8);
     if constexpr (!SMALL) {
       // block_size >= 16: the sub-step's 16 rows are one run of one block
       const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
@@ -165,7 +166,9 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<CT, D, GW>& r, const SeqCtx
       }
     }
   }
-  r.clean = clean;
+  // keys at or past the end (key_offset already clears groups that start there)
+  const int n = s.end - start;
+  r.kmask = n >= kChunk ? kmask : (n <= 0 ? 0u : kmask & ((1u << n) - 1u));
 }
 
 // Partial dot product of one key's quarter row with head h's q (in LDS,
@@ -252,10 +255,7 @@ __device__ __forceinline__ void compute_chunk(WaveState<CT, D, GW>& st, const Ch
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     bool ok = true;
-    if constexpr (MASKED) {
-      const int key = start + sb * 16 + kq;
-      ok = key < sc.end && sc.tbl[key < sc.end ? (key >> sc.log2bs) - sc.blk0 : 0] >= 0;
-    }
+    if constexpr (MASKED) ok = (r.kmask >> (sb * 16 + kq)) & 1u;
 #pragma unroll
     for (int h = 0; h < GW; ++h) {
       const float dot = quad_sum(qk_partial<CT, D, GW>(r.k[sb], q_lds + h * kQRowBytes<CT, D>, quarter));
@@ -295,8 +295,7 @@ __device__ __forceinline__ void compute_chunk(WaveState<CT, D, GW>& st, const Ch
 #pragma unroll
     for (int w = 0; w < C::pv_vec / 4; ++w) vw[w] = r.v[i][w];
     if constexpr (MASKED) {
-      const int k = start + key;
-      const bool ok = k < sc.end && sc.tbl[k < sc.end ? (k >> sc.log2bs) - sc.blk0 : 0] >= 0;
+      const bool ok = (r.kmask >> key) & 1u;
 #pragma unroll
       for (int w = 0; w < C::pv_vec / 4; ++w) vw[w] = ok ? vw[w] : 0u;
     }
@@ -332,7 +331,7 @@ template <int CT, int D, int GW>
 __device__ __forceinline__ void compute_any(WaveState<CT, D, GW>& st, const ChunkRegs<CT, D, GW>& r,
                                             const uint8_t* q_lds, float logit_scale, int start,
                                             const SeqCtx& sc, int lane, float* p_lds) {
-  if (r.clean) {
+  if (r.kmask == 0xffffffffu) {
     compute_chunk<CT, D, GW, false>(st, r, q_lds, logit_scale, start, sc, lane, p_lds);
   } else {
     compute_chunk<CT, D, GW, true>(st, r, q_lds, logit_scale, start, sc, lane, p_lds);
