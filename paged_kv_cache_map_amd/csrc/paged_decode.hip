@@ -106,69 +106,89 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // A chunk's keys come as two 16-key sub-steps, each made of two 8-key row
 // groups that lie in one block (block_size >= 8).  A row group is addressed by
 // one buffer resource in SGPRs; every lane adds a fixed offset, so the loads
-// need no per-key address arithmetic.
+// need no per-key address arithmetic.  off[sb][0/1]: uniform byte offsets of
+// the two row groups of sub-step sb (for block_size >= 16 the second is the
+// first plus 8 slots).
 template <int CT, int D, int GW, bool SMALL>
-__device__ __forceinline__ void load_chunk(ChunkRegs<CT, D, GW>& r, const SeqCtx& s, int start,
-                                           int lane) {
+__device__ __forceinline__ void issue_chunk_loads(ChunkRegs<CT, D, GW>& r, const uint8_t* kbase,
+                                                  const uint8_t* vbase, int stride, uint32_t k_off,
+                                                  uint32_t v_off, const int64_t (&off)[2][2],
+                                                  int lane) {
   using C = Cfg<CT, D, GW>;
-  uint32_t kmask = 0;
   const bool hi_lane = (lane >> 2) >= 8;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
-    const int key0 = start + sb * 16;
-    bool va, vb = true;
-    const int64_t off_a = key_offset(s, key0, va);
-    int64_t off_b;
-    if constexpr (!SMALL) {
-      off_b = off_a + 8 * (int64_t)s.slot_stride;
-    } else {
-      off_b = key_offset(s, key0 + 8, vb);
-    }
-    kmask |= (va ? 0xffu : 0u) << (16 * sb);
-    kmask |= (vb ? 0xffu : 0u) << (16 * sb + 8);
     if constexpr (!SMALL) {
       // block_size >= 16: the sub-step's 16 rows are one run of one block
       const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(s.kbase + off_a), 0, 16 * s.slot_stride, kBufferWord3);
+          (void*)(kbase + off[sb][0]), 0, 16 * stride, kBufferWord3);
 #pragma unroll
       for (int i = 0; i < C::qk_loads; ++i) {
         const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(
-            kr, (int)(s.k_off + (hi_lane ? 8 * s.slot_stride : 0)), i * 64, 0);
+            kr, (int)(k_off + (hi_lane ? 8 * stride : 0)), i * 64, 0);
         r.k[sb][i] = make_uint4(x.x, x.y, x.z, x.w);
       }
     } else {
       // block_size 8: keys 0..7 and 8..15 sit in two blocks; both loads are
       // issued for every lane (lanes that share an address merge) and each
       // lane keeps its own
-      const __amdgpu_buffer_rsrc_t ka = rows8(s.kbase, off_a, s.slot_stride);
-      const __amdgpu_buffer_rsrc_t kb = rows8(s.kbase, off_b, s.slot_stride);
+      const __amdgpu_buffer_rsrc_t ka = rows8(kbase, off[sb][0], stride);
+      const __amdgpu_buffer_rsrc_t kb = rows8(kbase, off[sb][1], stride);
 #pragma unroll
       for (int i = 0; i < C::qk_loads; ++i) {
-        const u32x4_t xa = __builtin_amdgcn_raw_buffer_load_b128(ka, (int)s.k_off, i * 64, 0);
-        const u32x4_t xb = __builtin_amdgcn_raw_buffer_load_b128(kb, (int)s.k_off, i * 64, 0);
+        const u32x4_t xa = __builtin_amdgcn_raw_buffer_load_b128(ka, (int)k_off, i * 64, 0);
+        const u32x4_t xb = __builtin_amdgcn_raw_buffer_load_b128(kb, (int)k_off, i * 64, 0);
         const u32x4_t x = hi_lane ? xb : xa;
         r.k[sb][i] = make_uint4(x.x, x.y, x.z, x.w);
       }
     }
-    const __amdgpu_buffer_rsrc_t va_r = rows8(s.vbase, off_a, s.slot_stride);
-    const __amdgpu_buffer_rsrc_t vb_r = rows8(s.vbase, off_b, s.slot_stride);
+    const __amdgpu_buffer_rsrc_t va_r = rows8(vbase, off[sb][0], stride);
+    const __amdgpu_buffer_rsrc_t vb_r = rows8(vbase, off[sb][1], stride);
 #pragma unroll
     for (int j = 0; j < 16 / C::pv_kp; ++j) {
       const int x = j * C::pv_kp;  // first key of the instruction within the sub-step
-      const int soff = (x & 7) * s.slot_stride;
+      const int soff = (x & 7) * stride;
       const int i = sb * (16 / C::pv_kp) + j;
       if constexpr (C::pv_vec == 4) {
-        r.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(x < 8 ? va_r : vb_r, (int)s.v_off, soff, 0);
+        r.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(x < 8 ? va_r : vb_r, (int)v_off, soff, 0);
       } else {
-        const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(x < 8 ? va_r : vb_r, (int)s.v_off, soff, 0);
+        const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(x < 8 ? va_r : vb_r, (int)v_off, soff, 0);
         r.v[i][0] = w.x;
         r.v[i][1] = w.y;
       }
     }
   }
-  // keys at or past the end (key_offset already clears groups that start there)
-  const int n = s.end - start;
-  r.kmask = n >= kChunk ? kmask : (n <= 0 ? 0u : kmask & ((1u << n) - 1u));
+}
+
+// Validity mask of a chunk from its row groups' validity and the key count.
+__device__ __forceinline__ uint32_t chunk_mask(const bool (&valid)[2][2], int keys_left) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    m |= (valid[sb][0] ? 0xffu : 0u) << (16 * sb);
+    m |= (valid[sb][1] ? 0xffu : 0u) << (16 * sb + 8);
+  }
+  return keys_left >= kChunk ? m : (keys_left <= 0 ? 0u : m & ((1u << keys_left) - 1u));
+}
+
+template <int CT, int D, int GW, bool SMALL>
+__device__ __forceinline__ void load_chunk(ChunkRegs<CT, D, GW>& r, const SeqCtx& s, int start,
+                                           int lane) {
+  int64_t off[2][2];
+  bool valid[2][2];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const int key0 = start + sb * 16;
+    off[sb][0] = key_offset(s, key0, valid[sb][0]);
+    if constexpr (!SMALL) {
+      off[sb][1] = off[sb][0] + 8 * (int64_t)s.slot_stride;
+      valid[sb][1] = valid[sb][0];
+    } else {
+      off[sb][1] = key_offset(s, key0 + 8, valid[sb][1]);
+    }
+  }
+  issue_chunk_loads<CT, D, GW, SMALL>(r, s.kbase, s.vbase, s.slot_stride, s.k_off, s.v_off, off, lane);
+  r.kmask = chunk_mask(valid, s.end - start);
 }
 
 // Partial dot product of one key's quarter row with head h's q (in LDS,
@@ -539,8 +559,401 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int split_keys
   for (int e = 0; e < NV; ++e) store_out<QT>(a.out, bh * D + lane * NV + e, O[e] * inv);
 }
 
+// ---------------------------------------------------------------------------
+// Stream-K decode: every wave is an independent worker that takes an equal,
+// contiguous share of the whole step's work, counted in 32-key chunks over
+// all (sequence, KV head group) units in order.  A wave keeps streaming
+// across unit boundaries; where a unit is split between waves each wave
+// writes a partial (max, sum, output) triple and the stream merge kernel
+// combines them.  This balances variable lengths exactly, and no workgroup
+// waits for a start-up or a tail of its own.
+// ---------------------------------------------------------------------------
+
+// Chunk counts: pre[b] = chunks of all units of sequences before b.
+__device__ __forceinline__ void build_prefix(int32_t* pre, int32_t* part, const DecodeArgs& a,
+                                             int units_per_seq) {
+  const int B = a.batch;
+  const int cap = a.max_blocks_per_seq * a.block_size;
+  const int per = (B + kStreamThreads - 1) / kStreamThreads;
+  const int b0 = threadIdx.x * per;
+  int sum = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < B) {
+      int lk = a.cache_seqlens[b];
+      lk = lk < 0 ? 0 : (lk > cap ? cap : lk);
+      sum += ((lk + kChunk - 1) / kChunk) * units_per_seq;
+    }
+  }
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  // inclusive scan of the per-thread sums (Hillis-Steele, 8 steps)
+  for (int d = 1; d < kStreamThreads; d <<= 1) {
+    const int x = threadIdx.x >= d ? part[threadIdx.x - d] : 0;
+    __syncthreads();
+    part[threadIdx.x] += x;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - sum;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < B) {
+      pre[b] = run;
+      int lk = a.cache_seqlens[b];
+      lk = lk < 0 ? 0 : (lk > cap ? cap : lk);
+      run += ((lk + kChunk - 1) / kChunk) * units_per_seq;
+    }
+  }
+  if (threadIdx.x == kStreamThreads - 1) pre[B] = part[kStreamThreads - 1];
+  __syncthreads();
+}
+
+// Wave that owns global chunk x when T chunks are dealt to W waves
+// (wave w owns [floor(T w / W), floor(T (w+1) / W))).
+__device__ __forceinline__ int wave_of(int64_t x, int64_t T, int W) {
+  return (int)(((x + 1) * W - 1) / T);
+}
+
+struct Pos {
+  int b, gg;    // sequence, unit (KV head group) within the sequence
+  int ch, nch;  // chunk within the unit, chunks per unit of this sequence
+};
+
+__device__ __forceinline__ Pos locate(const int32_t* pre, int B, int ug, int x) {
+  int lo = 0, hi = B;  // largest b with pre[b] <= x (and a non-empty sequence)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= x) lo = mid; else hi = mid;
+  }
+  while (pre[lo + 1] <= x) ++lo;  // skip empty sequences
+  Pos p;
+  p.b = lo;
+  p.nch = (pre[lo + 1] - pre[lo]) / ug;
+  const int r = x - pre[lo];
+  p.gg = r / p.nch;
+  p.ch = r % p.nch;
+  return p;
+}
+
+__device__ __forceinline__ Pos advance(const int32_t* pre, int ug, Pos p) {
+  if (p.ch + 1 < p.nch) {
+    ++p.ch;
+  } else if (p.gg + 1 < ug) {
+    ++p.gg;
+    p.ch = 0;
+  } else {
+    do { ++p.b; } while (pre[p.b + 1] == pre[p.b]);  // callers stay inside [0, T)
+    p.gg = 0;
+    p.ch = 0;
+    p.nch = (pre[p.b + 1] - pre[p.b]) / ug;
+  }
+  return p;
+}
+
+struct StreamCtx {
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  int64_t block_bytes;
+  int slot_stride, row_bytes, max_blocks, num_blocks, log2bs, bs, cap, heads_per_kv, head_groups;
+  uint32_t k_off, v_off;
+};
+
+__device__ __forceinline__ int seq_len(const StreamCtx& c, int b) {
+  const int lk = c.seqlens[b];
+  return lk < 0 ? 0 : (lk > c.cap ? c.cap : lk);
+}
+
+// Block ids of the four 8-key row groups of chunk p (lane j holds group j & 3).
+__device__ __forceinline__ int fetch_table(const StreamCtx& c, const Pos& p, int lane) {
+  const int key = p.ch * kChunk + 8 * (lane & 3);
+  const int idx = min(key >> c.log2bs, c.max_blocks - 1);
+  return c.block_table[(int64_t)p.b * c.max_blocks + idx];
+}
+
+template <int CT, int D, int GW, bool SMALL>
+__device__ __forceinline__ void load_chunk_stream(ChunkRegs<CT, D, GW>& r, const StreamCtx& c,
+                                                  const Pos& p, int tbl, int lane) {
+  const int lk = seq_len(c, p.b);
+  const int start = p.ch * kChunk;
+  const int g = (p.gg / c.head_groups);
+  int64_t off[2][2];
+  bool valid[2][2];
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    const int key = start + 8 * grp;
+    const int id = __builtin_amdgcn_readlane(tbl, grp);
+    const bool ok = key < lk && id >= 0 && id < c.num_blocks;
+    off[grp >> 1][grp & 1] =
+        ok ? (int64_t)id * c.block_bytes + (int64_t)(key & (c.bs - 1)) * c.slot_stride : 0;
+    valid[grp >> 1][grp & 1] = ok;
+  }
+  const uint8_t* kbase = c.k_cache + g * c.row_bytes;
+  const uint8_t* vbase = c.v_cache + g * c.row_bytes;
+  issue_chunk_loads<CT, D, GW, SMALL>(r, kbase, vbase, c.slot_stride, c.k_off, c.v_off, off, lane);
+  r.kmask = chunk_mask(valid, lk - start);
+}
+
+// Copy the q rows of unit (b, gg) into this wave's LDS region.
+template <int CT, int D, int GW>
+__device__ __forceinline__ void load_q(uint8_t* q_w, const DecodeArgs& a, const StreamCtx& c,
+                                       const Pos& p, int lane) {
+  constexpr int qrow = kQRowBytes<CT, D>;
+  const int h0 = (p.gg / c.head_groups) * c.heads_per_kv + (p.gg % c.head_groups) * GW;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)p.b * a.num_heads + h0) * qrow;
+  for (int i = lane; i < GW * qrow / 16; i += 64)
+    reinterpret_cast<uint4*>(q_w)[i] = reinterpret_cast<const uint4*>(src)[i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// End of a wave's segment of a unit: the final rows if the wave processed the
+// whole unit, else a partial triple in slot (wave + unit).
+template <int CT, int D, int GW>
+__device__ __forceinline__ void flush_segment(WaveState<CT, D, GW>& st, const DecodeArgs& a,
+                                              const StreamCtx& c, const Pos& p, bool whole, int slot,
+                                              float out_scale, int lane) {
+  using C = Cfg<CT, D, GW>;
+  constexpr int QT = (CT == kF32) ? kF32 : kBF16;
+  const int kp = lane / C::pv_lanes;
+  const int d0 = (lane % C::pv_lanes) * C::pv_nv;
+  const int h0 = (p.gg / c.head_groups) * c.heads_per_kv + (p.gg % c.head_groups) * GW;
+#pragma unroll
+  for (int h = 0; h < GW; ++h) {
+    const float l = sum_across_quads(st.l[h]);
+#pragma unroll
+    for (int e = 0; e < C::pv_nv; ++e) {
+#pragma unroll
+      for (int x = C::pv_lanes; x < 64; x <<= 1) st.o[h][e] += shfl_xor(st.o[h][e], x);
+    }
+    if (whole) {
+      if (kp == 0) {
+        const float inv = l > 0.0f ? out_scale / l : 0.0f;
+        const int64_t base = ((int64_t)p.b * a.num_heads + h0 + h) * D + d0;
+#pragma unroll
+        for (int e = 0; e < C::pv_nv; ++e) store_out<QT>(a.out, base + e, st.o[h][e] * inv);
+      }
+    } else {
+      float* ws_o = a.workspace + ((int64_t)slot * GW + h) * D;
+      float* ws_ml = a.workspace + (int64_t)a.stream_slots * GW * D + ((int64_t)slot * GW + h) * 2;
+      if (kp == 0) {
+#pragma unroll
+        for (int e = 0; e < C::pv_nv; ++e) ws_o[d0 + e] = st.o[h][e] * out_scale;
+      }
+      if (lane == 0) {
+        ws_ml[0] = st.m[h];
+        ws_ml[1] = l;
+      }
+    }
+    st.m[h] = kNegBig;
+    st.l[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < C::pv_nv; ++e) st.o[h][e] = 0.0f;
+  }
+}
+
+template <int CT, int D, int GW, bool SMALL>
+__global__ __launch_bounds__(kStreamThreads) void decode_stream_kernel(DecodeArgs a, int head_groups) {
+  using C = Cfg<CT, D, GW>;
+  constexpr int qrow = kQRowBytes<CT, D>;
+  __shared__ int32_t pre[kStreamMaxBatch + 1];
+  __shared__ int32_t part[kStreamThreads];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kWaves][GW * qrow];
+  __shared__ __attribute__((aligned(16))) float p_lds[kWaves][kChunk * GW];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int ug = a.num_kv_heads * head_groups;  // units per sequence
+  build_prefix(pre, part, a, ug);
+  const int64_t T = pre[a.batch];
+  const int W = gridDim.x * kWaves;
+  const int w = blockIdx.x * kWaves + wave;
+  const int c0 = (int)(T * w / W), c1 = (int)(T * (w + 1) / W);
+  if (c0 >= c1) return;
+
+  StreamCtx c;
+  c.k_cache = a.k_cache;
+  c.v_cache = a.v_cache;
+  c.block_table = a.block_table;
+  c.seqlens = a.cache_seqlens;
+  c.row_bytes = C::row_bytes;
+  c.slot_stride = a.num_kv_heads * C::row_bytes;
+  c.block_bytes = (int64_t)a.block_size * c.slot_stride;
+  c.max_blocks = a.max_blocks_per_seq;
+  c.num_blocks = a.num_blocks;
+  c.log2bs = __builtin_ctz(a.block_size);
+  c.bs = a.block_size;
+  c.cap = a.max_blocks_per_seq * a.block_size;
+  c.heads_per_kv = a.num_heads / a.num_kv_heads;
+  c.head_groups = head_groups;
+  {
+    const int kq = lane >> 2, quarter = lane & 3;
+    c.k_off = (uint32_t)((kq & 7) * c.slot_stride + quarter * 16);  // within an 8-row group
+    c.v_off = (uint32_t)((lane / C::pv_lanes) * c.slot_stride + (lane % C::pv_lanes) * C::pv_vec);
+  }
+  const float base_scale = a.softmax_scale * kLog2e;
+
+  uint8_t* q_w = q_lds[wave];
+  float* p_w = p_lds[wave];
+  WaveState<CT, D, GW> st;
+#pragma unroll
+  for (int h = 0; h < GW; ++h) {
+    st.m[h] = kNegBig;
+    st.l[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < C::pv_nv; ++e) st.o[h][e] = 0.0f;
+  }
+
+  // cur: chunk being computed; nxt: chunk whose loads are in flight
+  Pos cur = locate(pre, a.batch, ug, c0);
+  Pos nxt = c0 + 1 < c1 ? advance(pre, ug, cur) : cur;
+  int tbl_nxt = fetch_table(c, nxt, lane);
+  {
+    const int tbl_cur = fetch_table(c, cur, lane);
+    load_q<CT, D, GW>(q_w, a, c, cur, lane);
+    int x = c0;
+    ChunkRegs<CT, D, GW> A, B;
+    load_chunk_stream<CT, D, GW, SMALL>(A, c, cur, tbl_cur, lane);
+    float logit_scale = base_scale, out_scale = 1.0f;
+    const int g_cur = cur.gg / head_groups;
+    if constexpr (CT == kFP8) {
+      logit_scale *= a.k_scale[g_cur];
+      out_scale = a.v_scale[g_cur];
+    }
+    // One step: compute `cur` from R (while S loads `nxt`), then move on.
+    auto step = [&](ChunkRegs<CT, D, GW>& R, ChunkRegs<CT, D, GW>& S) -> bool {
+      const Pos nn = x + 2 < c1 ? advance(pre, ug, nxt) : nxt;
+      const int tbl_nn = fetch_table(c, nn, lane);
+      load_chunk_stream<CT, D, GW, SMALL>(S, c, nxt, tbl_nxt, lane);
+      compute_any<CT, D, GW>(st, R, q_w, logit_scale, cur.ch * kChunk, SeqCtx{}, lane, p_w);
+      const bool last = x + 1 == c1;
+      if (last || cur.ch + 1 == cur.nch) {
+        const int u = cur.b * ug + cur.gg;
+        const int64_t ustart = pre[cur.b] + (int64_t)cur.gg * cur.nch;
+        const bool whole = ustart >= c0 && ustart + cur.nch <= c1;
+        flush_segment<CT, D, GW>(st, a, c, cur, whole, w + u, out_scale, lane);
+      }
+      if (last) return false;
+      if (nxt.b != cur.b || nxt.gg != cur.gg) {
+        load_q<CT, D, GW>(q_w, a, c, nxt, lane);
+        if constexpr (CT == kFP8) {
+          const int g = nxt.gg / head_groups;
+          logit_scale = base_scale * a.k_scale[g];
+          out_scale = a.v_scale[g];
+        }
+      }
+      cur = nxt;
+      nxt = nn;
+      tbl_nxt = tbl_nn;
+      ++x;
+      return true;
+    };
+    for (;;) {
+      if (!step(A, B)) break;
+      if (!step(B, A)) break;
+    }
+  }
+}
+
+// Combine the partial triples of units split between waves; write zero rows
+// for empty sequences.  One wave per (sequence, q head).
+template <int QT, int D, int GW>
+__global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs a, int head_groups,
+                                                                      int W) {
+  __shared__ int32_t pre[kStreamMaxBatch + 1];
+  __shared__ int32_t part[kStreamThreads];
+  const int ug = a.num_kv_heads * head_groups;
+  build_prefix(pre, part, a, ug);
+  const int64_t T = pre[a.batch];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t bh = (int64_t)blockIdx.x * kWaves + wave;
+  if (bh >= (int64_t)a.batch * a.num_heads) return;
+  const int b = (int)(bh / a.num_heads), h = (int)(bh % a.num_heads);
+  const int G = a.num_heads / a.num_kv_heads;
+  const int gg = (h / G) * head_groups + (h % G) / GW;
+  const int hh = (h % G) % GW;
+  const int nch = (pre[b + 1] - pre[b]) / ug;
+  constexpr int NV = D / 64;
+  if (nch == 0) {
+#pragma unroll
+    for (int e = 0; e < NV; ++e) store_out<QT>(a.out, bh * D + lane * NV + e, 0.0f);
+    return;
+  }
+  const int64_t ustart = pre[b] + (int64_t)gg * nch;
+  const int wf = wave_of(ustart, T, W), wl = wave_of(ustart + nch - 1, T, W);
+  if (wf == wl) return;  // one wave processed the whole unit and wrote the row
+  const int u = b * ug + gg;
+  const float* ws_o = a.workspace;
+  const float* ws_ml = a.workspace + (int64_t)a.stream_slots * GW * D;
+  // waves between wf and wl that own no chunk at all (fewer chunks than
+  // waves) wrote nothing: skip them
+  auto owns = [&](int w) { return T * w / W < T * (w + 1) / W; };
+  float mx = kNegBig;
+  for (int w = wf; w <= wl; ++w)
+    if (owns(w)) mx = fmaxf(mx, ws_ml[((int64_t)(w + u) * GW + hh) * 2]);
+  float O[NV] = {};
+  float L = 0.0f;
+  for (int w = wf; w <= wl; ++w) {
+    if (!owns(w)) continue;
+    const int64_t slot = (int64_t)(w + u) * GW + hh;
+    const float f = fast_exp2(ws_ml[slot * 2] - mx);
+    L = fmaf(ws_ml[slot * 2 + 1], f, L);
+#pragma unroll
+    for (int e = 0; e < NV; ++e) O[e] = fmaf(ws_o[slot * D + lane * NV + e], f, O[e]);
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) store_out<QT>(a.out, bh * D + lane * NV + e, O[e] * inv);
+}
+
+// Workgroups of a persistent launch: every CU filled to the kernel's
+// occupancy, and never more waves than the workspace has slots for.
+template <typename K>
+int persistent_grid(K kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kStreamThreads, 0) != hipSuccess ||
+      cus <= 0 || per_cu <= 0) {
+    cus = 256;
+    per_cu = 1;
+  }
+  int64_t wgs = (int64_t)cus * per_cu;
+  if (wgs > kStreamMaxWaves / kWaves) wgs = kStreamMaxWaves / kWaves;
+  return (int)(wgs < 1 ? 1 : wgs);
+}
+
+template <int CT, int D, int GW, bool SMALL>
+hipError_t launch_stream_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
+  constexpr int QT = (CT == kF32) ? kF32 : kBF16;
+  static int cached_grid = 0;  // per instantiation; the CU count of one process's GPUs is fixed
+  const int64_t max_chunks = (int64_t)a.batch * a.num_kv_heads * p.head_groups *
+                             (((int64_t)a.max_blocks_per_seq * a.block_size + kChunk - 1) / kChunk);
+  if (cached_grid == 0) cached_grid = persistent_grid(decode_stream_kernel<CT, D, GW, SMALL>);
+  int64_t grid = cached_grid;
+  if (grid * kWaves > max_chunks) grid = (max_chunks + kWaves - 1) / kWaves;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL((decode_stream_kernel<CT, D, GW, SMALL>), dim3((unsigned)grid), dim3(kStreamThreads),
+                     0, stream, a, p.head_groups);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)a.batch * a.num_heads;
+  hipLaunchKernelGGL((stream_merge_kernel<QT, D, GW>), dim3((unsigned)((rows + kWaves - 1) / kWaves)),
+                     dim3(kStreamThreads), 0, stream, a, p.head_groups, (int)(grid * kWaves));
+  return hipGetLastError();
+}
+
+template <int CT, int D, int GW>
+hipError_t launch_stream(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
+  if (a.block_size < 16) return launch_stream_t<CT, D, GW, true>(a, p, stream);
+  return launch_stream_t<CT, D, GW, false>(a, p, stream);
+}
+
 template <int CT, int D, int GW>
 hipError_t launch_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
+  if (p.stream) return launch_stream<CT, D, GW>(a, p, stream);
   constexpr int QT = (CT == kF32) ? kF32 : kBF16;
   const dim3 grid(a.num_kv_heads * p.head_groups, p.num_splits, a.batch);
   if (a.block_size < 16) {

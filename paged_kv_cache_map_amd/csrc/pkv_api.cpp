@@ -229,6 +229,7 @@ int pkv_paged_decode(void* out, const void* q, int q_dtype, const void* k_cache,
   a.block_table = block_table;
   a.cache_seqlens = cache_seqlens;
   a.workspace = (float*)workspace;
+  a.stream_slots = plan.stream_slots;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.batch = batch;
   a.num_heads = num_heads;

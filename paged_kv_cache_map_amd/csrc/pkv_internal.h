@@ -31,9 +31,11 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
 // Split-K plan of the decode: keys [s * split_keys, (s+1) * split_keys) of a
 // sequence form work unit s.
 struct DecodePlan {
-  int32_t split_keys;   // multiple of kDecodeKeysPerWg
-  int32_t num_splits;   // units per sequence at the longest possible length
+  bool stream;          // stream-K kernel (automatic plan) instead of fixed splits
+  int32_t split_keys;   // fixed splits: multiple of kDecodeKeysPerWg
+  int32_t num_splits;   // fixed splits: units per sequence at the longest possible length
   int32_t head_groups;  // q-head groups of at most 8 per KV head
+  int64_t stream_slots; // stream-K: partial slots (waves + units)
   size_t workspace_bytes;
 };
 
@@ -41,6 +43,9 @@ constexpr int kDecodeWaves = 4;
 constexpr int kDecodeChunk = 32;                              // keys per wave iteration
 constexpr int kDecodeKeysPerWg = kDecodeWaves * kDecodeChunk;  // 128
 constexpr int kDecodeMaxSplitKeys = 8192;                     // bounds the LDS block table
+constexpr int kStreamThreads = 256;                           // stream-K decode workgroup
+constexpr int kStreamMaxBatch = 4096;                         // LDS chunk-count table
+constexpr int kStreamMaxWaves = 4096;                         // bounds the stream-K workspace
 
 // Fills `plan`; returns false (with a message in *why) for arguments the
 // planner cannot serve.  Pure host arithmetic, no HIP calls.
@@ -58,6 +63,7 @@ struct DecodeArgs {
   const int32_t* block_table;
   const int32_t* cache_seqlens;
   float* workspace;
+  int64_t stream_slots;  // stream-K: partial slots in the workspace
   int32_t max_blocks_per_seq;
   int32_t batch;
   int32_t num_heads;

@@ -29,6 +29,23 @@ bool plan_decode(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
   const int32_t group = num_heads / num_kv_heads;
   const int32_t head_groups = group > 8 ? group / 8 : 1;
   const int64_t max_keys = (int64_t)max_blocks_per_seq * block_size;
+  plan->head_groups = head_groups;
+  // Automatic plan: stream-K, when the batch fits its chunk-count table and
+  // the chunk count fits in 31 bits.
+  const int64_t units = (int64_t)batch * num_kv_heads * head_groups;
+  const int64_t max_chunks = units * ((max_keys + kDecodeChunk - 1) / kDecodeChunk);
+  if (split_keys == 0 && batch <= kStreamMaxBatch && max_chunks < (int64_t)1 << 31) {
+    const int64_t per_unit_heads = group / head_groups;
+    plan->stream = true;
+    plan->split_keys = 0;
+    plan->num_splits = 0;
+    plan->stream_slots = kStreamMaxWaves + units;
+    plan->workspace_bytes =
+        (size_t)plan->stream_slots * per_unit_heads * (size_t)(head_dim + 2) * sizeof(float);
+    return true;
+  }
+  plan->stream = false;
+  plan->stream_slots = 0;
   int64_t sk;
   if (split_keys == 0) {
     const int64_t units = (int64_t)batch * num_kv_heads * head_groups;
