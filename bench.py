@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--split-keys", type=int, default=0,
                     help="decode split size in keys (0: the library's automatic plan)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also time a plain 512 MiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -74,6 +76,34 @@ def prefill_flops(step):
     pre = lk - lq
     pairs = int(np.sum(lq * pre + lq * (lq + 1) // 2))
     return 4 * step.num_heads * step.head_dim * pairs
+
+
+# HBM traffic of one decode call on the headline workload, from the hardware
+# counters (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, averaged per
+# dispatch), each scaled by bytes / counter of a plain 512 MiB device copy
+# measured in the same runs.  The figures belong to the decode sources with
+# the given digest: after any change to them the traffic is reported as null
+# until the counters are taken again.
+DECODE_TRAFFIC = {"digest": "62db048fbf58d291", "read_bytes": 560387253, "write_bytes": 5786214}
+DECODE_SOURCES = ("paged_kv_cache_map_amd/csrc/paged_decode.hip",
+                  "paged_kv_cache_map_amd/csrc/pkv_device.hpp",
+                  "paged_kv_cache_map_amd/csrc/pkv_plan.cpp",
+                  "paged_kv_cache_map_amd/csrc/pkv_internal.h")
+
+
+def decode_sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_traffic():
+    if DECODE_TRAFFIC is None or DECODE_TRAFFIC["digest"] != decode_sources_digest():
+        return None
+    return DECODE_TRAFFIC["read_bytes"] + DECODE_TRAFFIC["write_bytes"]
 
 
 # ---------------------------------------------------------------------------
@@ -164,6 +194,26 @@ class Runner:
                     write_ms=float(np.mean(write)), write_ms_min=float(np.min(write)),
                     prefill_ms=float(np.mean(pre)), prefill_ms_min=float(np.min(pre)),
                     decode_ms=float(np.mean(dec)), decode_ms_min=float(np.min(dec)))
+
+
+def copy_probe(reps=5, nbytes=512 << 20):
+    """A plain device-to-device copy of a known size (torch's copy kernel)."""
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": float(np.mean(ms)),
+            "gbs": 2 * nbytes / (float(np.mean(ms)) * 1e6)}
 
 
 def copies_for(step):
@@ -257,11 +307,11 @@ def main():
                    "context": "cached lengths U{512..4096} (+1 new token)",
                    "keys_total": int(d["cache_seqlens"].sum()),
                    "step_bytes": int(step_bytes)},
-        "roofline": {"kernel": "paged_decode (split kernel + merge kernel of one call)",
+        "roofline": {"kernel": "paged_decode call (stream-K plan: decode_stream_kernel + stream_merge_kernel)",
                      "bound": "hbm", "achieved": round(main_res["decode_gbs"], 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(main_res["decode_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": decode_traffic(),
                      "algorithmic_bytes_per_launch": int(main_res["decode_bytes"]),
                      "avg_launch_ms": round(main_res["decode_ms"], 5)},
         "kernels": {"llama8b_decode": {k: (round(v, 5) if isinstance(v, float) else v)
@@ -283,6 +333,9 @@ def main():
             "mixed_fp8_decode_gbs": line["kernels"]["mixed_fp8"]["decode_gbs"],
             "mixed_fp8_prefill_tflops": line["kernels"]["mixed_fp8"]["prefill_tflops"],
         }
+    if args.copy_probe:
+        print("[bench] copy probe", flush=True)
+        line["kernels"]["copy_probe"] = copy_probe()
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", flush=True)
         line["cpu_baseline"] = cpu_baseline(step, step_bytes)
