@@ -5,12 +5,16 @@
 // [num_kv_heads, head_dim] K row and V row to cache slot slot_map[t], the slot
 // addressing row slot * (heads * head_dim) of the cache.
 //
-// Design (gfx950): one wave64 moves one row (a token's K or a token's V), so a
-// 256-thread workgroup handles two tokens.  Lanes stride the row in 16-byte
-// pieces: consecutive lanes touch consecutive bytes of both the source and the
-// destination row, every access is a full dwordx4, and all of a lane's loads
-// are issued before its stores.  The kernel is HBM-bound (it reads and writes
-// every byte once); there is no LDS and no reuse to exploit.
+// Design (gfx950): one wave64 moves one token: its K row and its V row, seen
+// as one run of 16-byte source pieces (K's pieces, then V's).  Every lane
+// issues all of its loads first, with no branch in front of them (addresses
+// are clamped into the rows), and only then learns the token's slot; the
+// stores go through buffer descriptors whose size is zero when the slot is
+// -1 or out of range, so the hardware drops them.  Consecutive lanes touch
+// consecutive bytes of source and destination, every access is a full piece,
+// and no lane waits on the slot map before its reads are in flight.  The
+// kernel is HBM-bound (every byte is read and written once); there is no LDS
+// and no reuse.
 //
 // For an fp8 cache each source element x becomes e4m3(x / scale[head]) with an
 // IEEE fp32 division (the library is built with correctly rounded division)
@@ -22,110 +26,95 @@
 namespace pkv {
 namespace {
 
-constexpr int kRowsPerWg = 4;  // one row per wave
-constexpr int kUnroll = 4;     // 16-byte pieces in flight per lane
+constexpr int kTokensPerWg = 4;  // one token per wave
+constexpr int kUnroll = 4;       // source pieces in flight per lane per pass
+constexpr int kWord3 = 0x00020000;
+constexpr int kDropped = 0x7ffffff0;  // a buffer offset past any row: the store is dropped
 
-// src and dst dtype equal: 16-byte pieces copied unchanged.
-__device__ __forceinline__ void copy_row(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                         int pieces, int lane) {
-  const uint4* s = reinterpret_cast<const uint4*>(src);
-  uint4* d = reinterpret_cast<uint4*>(dst);
-  for (int base = 0; base < pieces; base += 64 * kUnroll) {
-    uint4 buf[kUnroll];
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// 16 source bytes -> the cache's bytes for them (16, 8 or 4), as 4 words.
+template <int SRC, int DST>
+__device__ __forceinline__ u32x4_t convert_piece(uint4 x, float sc) {
+  u32x4_t o = {x.x, x.y, x.z, x.w};
+  if constexpr (SRC == kBF16 && DST == kFP8) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t out[2] = {0u, 0u};
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = base + u * 64 + lane;
-      if (p < pieces) buf[u] = s[p];
+    for (int e = 0; e < 8; ++e) {
+      const float v = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+      out[e >> 2] |= f32_to_e4m3(v / sc) << ((e & 3) * 8);
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = base + u * 64 + lane;
-      if (p < pieces) d[p] = buf[u];
-    }
+    o.x = out[0];
+    o.y = out[1];
+  } else if constexpr (SRC == kF32 && DST == kFP8) {
+    o.x = f32_to_e4m3(__uint_as_float(x.x) / sc) | (f32_to_e4m3(__uint_as_float(x.y) / sc) << 8) |
+          (f32_to_e4m3(__uint_as_float(x.z) / sc) << 16) |
+          (f32_to_e4m3(__uint_as_float(x.w) / sc) << 24);
   }
+  return o;
 }
 
-// bf16 source -> fp8 cache: 16 source bytes (8 elements) -> 8 cache bytes.
-__device__ __forceinline__ void quant_row_bf16(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                               const float* __restrict__ scale, int pieces,
-                                               int head_dim, int lane) {
-  const uint4* s = reinterpret_cast<const uint4*>(src);
-  uint2* d = reinterpret_cast<uint2*>(dst);
-  for (int base = 0; base < pieces; base += 64 * kUnroll) {
-    uint4 buf[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = base + u * 64 + lane;
-      if (p < pieces) buf[u] = s[p];
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = base + u * 64 + lane;
-      if (p < pieces) {
-        const float sc = scale[(p * 8) / head_dim];
-        const uint32_t w[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
-        uint32_t out[2] = {0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t word = w[e >> 1];
-          const float x = (e & 1) ? bf16_hi(word) : bf16_lo(word);
-          out[e >> 2] |= f32_to_e4m3(x / sc) << ((e & 3) * 8);
-        }
-        d[p] = make_uint2(out[0], out[1]);
-      }
-    }
-  }
-}
-
-// fp32 source -> fp8 cache: 16 source bytes (4 elements) -> 4 cache bytes.
-__device__ __forceinline__ void quant_row_f32(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                              const float* __restrict__ scale, int pieces,
-                                              int head_dim, int lane) {
-  const float4* s = reinterpret_cast<const float4*>(src);
-  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
-  for (int base = 0; base < pieces; base += 64 * kUnroll) {
-    float4 buf[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = base + u * 64 + lane;
-      if (p < pieces) buf[u] = s[p];
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = base + u * 64 + lane;
-      if (p < pieces) {
-        const float sc = scale[(p * 4) / head_dim];
-        d[p] = f32_to_e4m3(buf[u].x / sc) | (f32_to_e4m3(buf[u].y / sc) << 8) |
-               (f32_to_e4m3(buf[u].z / sc) << 16) | (f32_to_e4m3(buf[u].w / sc) << 24);
-      }
-    }
+template <int SRC, int DST>
+__device__ __forceinline__ void store_piece(__amdgpu_buffer_rsrc_t r, int off, u32x4_t v) {
+  if constexpr (SRC == DST) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+  } else if constexpr (SRC == kBF16) {
+    const u32x2_t w = {v.x, v.y};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(v.x, r, off, 0, 0);
   }
 }
 
 template <int SRC, int DST>
 __global__ __launch_bounds__(256) void kv_write_kernel(WriteArgs a) {
-  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerWg + wave;  // 2 * token + (0: K, 1: V)
-  if (row >= 2 * (int64_t)a.num_tokens) return;
-  const int64_t t = row >> 1;
-  const bool is_v = row & 1;
-  const int32_t slot = a.slot_map[t];
-  if (slot < 0 || (int64_t)slot >= a.num_slots) return;  // -1: no slot; others: out of range
+  const int64_t t = (int64_t)blockIdx.x * kTokensPerWg +
+                    __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= a.num_tokens) return;
 
+  constexpr int src_elt = Elt<SRC>::bytes;
+  constexpr int dst_piece = 16 * Elt<DST>::bytes / src_elt;  // cache bytes per source piece
   const int row_elems = a.num_kv_heads * a.head_dim;
-  const int src_row_bytes = row_elems * Elt<SRC>::bytes;
+  const int pieces = row_elems * src_elt / 16;               // per row
   const int dst_row_bytes = row_elems * Elt<DST>::bytes;
-  const uint8_t* src = (is_v ? a.v : a.k) + t * (is_v ? a.v_stride_bytes : a.k_stride_bytes);
-  uint8_t* dst = (is_v ? a.v_cache : a.k_cache) + (int64_t)slot * dst_row_bytes;
-  const int pieces = src_row_bytes / 16;
+  const uint4* ksrc = reinterpret_cast<const uint4*>(a.k + t * a.k_stride_bytes);
+  const uint4* vsrc = reinterpret_cast<const uint4*>(a.v + t * a.v_stride_bytes);
+  const int elems_per_piece = 16 / src_elt;
 
-  if constexpr (SRC == DST) {
-    copy_row(src, dst, pieces, lane);
-  } else if constexpr (SRC == kBF16) {
-    quant_row_bf16(src, dst, is_v ? a.v_scale : a.k_scale, pieces, a.head_dim, lane);
-  } else {
-    quant_row_f32(src, dst, is_v ? a.v_scale : a.k_scale, pieces, a.head_dim, lane);
+  for (int base = 0; base < 2 * pieces; base += 64 * kUnroll) {
+    uint4 buf[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int q = min(base + u * 64 + lane, 2 * pieces - 1);
+      buf[u] = q < pieces ? ksrc[q] : vsrc[q - pieces];
+    }
+    // the slot is needed only by the stores
+    const int32_t slot = a.slot_map[t];
+    const bool ok = slot >= 0 && (int64_t)slot < a.num_slots;
+    const int64_t dst_off = ok ? (int64_t)slot * dst_row_bytes : 0;
+    const int nrec = ok ? dst_row_bytes : 0;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_cache + dst_off), 0, nrec, kWord3);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.v_cache + dst_off), 0, nrec, kWord3);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int q = base + u * 64 + lane;
+      const bool is_k = q < pieces;
+      const bool is_v = !is_k && q < 2 * pieces;
+      float sc = 1.0f;
+      if constexpr (DST == kFP8) {
+        const int qq = min(q, 2 * pieces - 1);
+        const int e = (is_k ? qq : qq - pieces) * elems_per_piece;
+        sc = (is_k ? a.k_scale : a.v_scale)[e / a.head_dim];
+      }
+      const u32x4_t v = convert_piece<SRC, DST>(buf[u], sc);
+      store_piece<SRC, DST>(kr, is_k ? q * dst_piece : kDropped, v);
+      store_piece<SRC, DST>(vr, is_v ? (q - pieces) * dst_piece : kDropped, v);
+    }
   }
 }
 
@@ -133,9 +122,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(WriteArgs a) {
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
-  const int64_t rows = 2 * (int64_t)a.num_tokens;
-  const dim3 grid((unsigned)((rows + kRowsPerWg - 1) / kRowsPerWg));
-  const dim3 block(64 * kRowsPerWg);
+  const dim3 grid((unsigned)((a.num_tokens + kTokensPerWg - 1) / kTokensPerWg));
+  const dim3 block(64 * kTokensPerWg);
   if (a.src_dtype == kF32 && a.cache_dtype == kF32) {
     hipLaunchKernelGGL((kv_write_kernel<kF32, kF32>), grid, block, 0, stream, a);
   } else if (a.src_dtype == kBF16 && a.cache_dtype == kBF16) {

@@ -58,9 +58,10 @@ class GpuStep:
         pkv.kv_cache_write(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slot_map,
                            self.k_scale, self.v_scale)
 
-    def decode(self, split_keys=0):
+    def decode(self, split_keys=0, workspace=None):
         return pkv.paged_decode(self.dec_q, self.k_cache, self.v_cache, self.dec_bt, self.dec_len,
-                                self.s.scale, self.k_scale, self.v_scale, split_keys=split_keys)
+                                self.s.scale, self.k_scale, self.v_scale, split_keys=split_keys,
+                                workspace=workspace)
 
     def prefill(self):
         p = self.pre

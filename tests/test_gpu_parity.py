@@ -120,6 +120,39 @@ def test_decode_split_invariance_and_determinism():
     assert np.array_equal(again, outs[128]), "run-to-run results differ"
 
 
+def test_decode_workspace_reuse():
+    """One workspace, never cleared, serves calls of different shapes and plans
+    in a row (stale partials of earlier calls must not leak into results)."""
+    ws = torch.full((64 << 20,), 0xff, dtype=torch.uint8, device="cuda")   # every float NaN
+    cases = [
+        workloads.config("llama8b_decode", batch=7, len_lo=1, len_hi=2000),
+        workloads.config("llama8b_decode", batch=3, len_lo=500, len_hi=3000, num_heads=16,
+                         num_kv_heads=2),
+        workloads.config("llama8b_decode", batch=9, len_lo=0, len_hi=300, num_heads=8,
+                         num_kv_heads=8, head_dim=64, block_size=32),
+    ]
+    for rep in range(2):
+        for i, step in enumerate(cases):
+            say("workspace reuse", rep, i)
+            g = GpuStep(step)
+            g.write()
+            kc, vc = oracle_write(step)
+            want = oracle_decode(step, kc, vc)
+            for sk in (0, 256, 0):
+                out = out_f64(g.decode(sk, workspace=ws))
+                assert max_err(out, want) <= TOL["bf16"], (rep, i, sk)
+
+
+def test_stream_decode_is_deterministic():
+    step = workloads.config("llama8b_decode", batch=16, len_lo=1, len_hi=3000, num_heads=64,
+                            num_kv_heads=8)
+    g = GpuStep(step)
+    g.write()
+    a = g.decode().cpu()
+    b = g.decode().cpu()
+    assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("hq,hkv,d,bs,dtype", [
     (8, 8, 128, 16, "bf16"),     # MHA, G = 1
     (8, 1, 128, 16, "bf16"),     # MQA, G = 8
