@@ -709,6 +709,24 @@ __device__ __forceinline__ void load_q(uint8_t* q_w, const DecodeArgs& a, const 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workspace layout of the stream plan: partial outputs [slots][GW][D], then
+// (max, sum) pairs [slots][GW][2], then the chunk prefix [batch + 1].
+__device__ __forceinline__ int32_t* stream_prefix(const DecodeArgs& a, int gw, int d) {
+  return reinterpret_cast<int32_t*>(a.workspace + a.stream_slots * gw * (int64_t)(d + 2));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, shfl_xor(x, m));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += shfl_xor(x, m);
+  return x;
+}
+
 // End of a wave's segment of a unit: the final rows if the wave processed the
 // whole unit, else a partial triple in slot (wave + unit).
 template <int CT, int D, int GW>
@@ -767,6 +785,10 @@ __global__ __launch_bounds__(kStreamThreads) void decode_stream_kernel(DecodeArg
   const int lane = threadIdx.x & 63;
   const int ug = a.num_kv_heads * head_groups;  // units per sequence
   build_prefix(pre, part, a, ug);
+  if (blockIdx.x == 0) {  // the merge kernel reads the prefix instead of rebuilding it
+    int32_t* pre_g = stream_prefix(a, GW, D);
+    for (int i = threadIdx.x; i <= a.batch; i += kStreamThreads) pre_g[i] = pre[i];
+  }
   const int64_t T = pre[a.batch];
   const int W = gridDim.x * kWaves;
   const int w = blockIdx.x * kWaves + wave;
@@ -857,25 +879,27 @@ __global__ __launch_bounds__(kStreamThreads) void decode_stream_kernel(DecodeArg
   }
 }
 
-// Combine the partial triples of units split between waves; write zero rows
-// for empty sequences.  One wave per (sequence, q head).
+// Combine the partial triples of units split between waves and write zero
+// rows for empty sequences.  One wave per (sequence, q head): one round trip
+// for the prefix, one for every part's (max, sum) (a lane per part), then the
+// parts' outputs, eight in flight per lane:
+//   out = sum_w o_w 2^(m_w - m) / sum_w l_w 2^(m_w - m),  m = max_w m_w.
 template <int QT, int D, int GW>
 __global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs a, int head_groups,
                                                                       int W) {
-  __shared__ int32_t pre[kStreamMaxBatch + 1];
-  __shared__ int32_t part[kStreamThreads];
-  const int ug = a.num_kv_heads * head_groups;
-  build_prefix(pre, part, a, ug);
-  const int64_t T = pre[a.batch];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int NV = D / 64;
+  constexpr int kBatch = 8;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)blockIdx.x * kWaves + wave;
   if (bh >= (int64_t)a.batch * a.num_heads) return;
   const int b = (int)(bh / a.num_heads), h = (int)(bh % a.num_heads);
+  const int32_t* pre = stream_prefix(a, GW, D);
+  const int64_t T = pre[a.batch];
+  const int ug = a.num_kv_heads * head_groups;
   const int G = a.num_heads / a.num_kv_heads;
   const int gg = (h / G) * head_groups + (h % G) / GW;
   const int hh = (h % G) % GW;
   const int nch = (pre[b + 1] - pre[b]) / ug;
-  constexpr int NV = D / 64;
   if (nch == 0) {
 #pragma unroll
     for (int e = 0; e < NV; ++e) store_out<QT>(a.out, bh * D + lane * NV + e, 0.0f);
@@ -885,23 +909,46 @@ __global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs
   const int wf = wave_of(ustart, T, W), wl = wave_of(ustart + nch - 1, T, W);
   if (wf == wl) return;  // one wave processed the whole unit and wrote the row
   const int u = b * ug + gg;
+  const int n = wl - wf + 1;
   const float* ws_o = a.workspace;
   const float* ws_ml = a.workspace + (int64_t)a.stream_slots * GW * D;
-  // waves between wf and wl that own no chunk at all (fewer chunks than
-  // waves) wrote nothing: skip them
-  auto owns = [&](int w) { return T * w / W < T * (w + 1) / W; };
-  float mx = kNegBig;
-  for (int w = wf; w <= wl; ++w)
-    if (owns(w)) mx = fmaxf(mx, ws_ml[((int64_t)(w + u) * GW + hh) * 2]);
-  float O[NV] = {};
-  float L = 0.0f;
-  for (int w = wf; w <= wl; ++w) {
-    if (!owns(w)) continue;
-    const int64_t slot = (int64_t)(w + u) * GW + hh;
-    const float f = fast_exp2(ws_ml[slot * 2] - mx);
-    L = fmaf(ws_ml[slot * 2 + 1], f, L);
+  float mx = kNegBig, L = 0.0f, O[NV];
 #pragma unroll
-    for (int e = 0; e < NV; ++e) O[e] = fmaf(ws_o[slot * D + lane * NV + e], f, O[e]);
+  for (int e = 0; e < NV; ++e) O[e] = 0.0f;
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    // lane i: wave wf + j0 + i; waves that own no chunk at all wrote nothing
+    const int j = min(j0 + lane, n - 1);
+    const int wj = wf + j;
+    const bool has = j0 + lane < n && (T * wj / W < T * (wj + 1) / W);
+    const int64_t slot = (int64_t)(wj + u) * GW + hh;
+    const float m_raw = ws_ml[slot * 2];
+    const float l_raw = ws_ml[slot * 2 + 1];
+    const float mj = has ? m_raw : kNegBig;
+    const float mn = fmaxf(mx, wave_max(mj));
+    const float alpha = fast_exp2(mx - mn);
+    const float f = has ? fast_exp2(mj - mn) : 0.0f;
+    L = L * alpha + wave_sum(has ? l_raw * f : 0.0f);
+#pragma unroll
+    for (int e = 0; e < NV; ++e) O[e] *= alpha;
+    mx = mn;
+    const int cnt = min(64, n - j0);
+    for (int i0 = 0; i0 < cnt; i0 += kBatch) {
+      float ov[kBatch][NV];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int64_t si = (int64_t)(wf + j0 + min(i0 + i, cnt - 1) + u) * GW + hh;
+#pragma unroll
+        for (int e = 0; e < NV; ++e) ov[i][e] = ws_o[si * D + lane * NV + e];
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        // f is 0 for lanes past cnt and for waves without a part: skip those rows
+        const float fi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), min(i0 + i, 63)));
+        const bool use = i0 + i < cnt && fi > 0.0f;
+#pragma unroll
+        for (int e = 0; e < NV; ++e) O[e] = use ? fmaf(ov[i][e], fi, O[e]) : O[e];
+      }
+    }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
@@ -978,7 +1025,6 @@ hipError_t launch_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream
     case 1: return launch_t<CT, D, 1>(a, p, stream);
     case 2: return launch_t<CT, D, 2>(a, p, stream);
     case 4: return launch_t<CT, D, 4>(a, p, stream);
-    case 8: return launch_t<CT, D, 8>(a, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -27,7 +27,10 @@ bool plan_decode(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
     return false;
   }
   const int32_t group = num_heads / num_kv_heads;
-  const int32_t head_groups = group > 8 ? group / 8 : 1;
+  // q heads of one KV head are served in groups of at most 4: a wave's live
+  // state for 4 heads fits two waves per SIMD; larger groups read their KV
+  // head once per group (the repeats hit the caches)
+  const int32_t head_groups = group > 4 ? group / 4 : 1;
   const int64_t max_keys = (int64_t)max_blocks_per_seq * block_size;
   plan->head_groups = head_groups;
   // Automatic plan: stream-K, when the batch fits its chunk-count table and
@@ -40,8 +43,10 @@ bool plan_decode(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
     plan->split_keys = 0;
     plan->num_splits = 0;
     plan->stream_slots = kStreamMaxWaves + units;
+    // partial triples of every slot, then the chunk prefix of the batch
     plan->workspace_bytes =
-        (size_t)plan->stream_slots * per_unit_heads * (size_t)(head_dim + 2) * sizeof(float);
+        (size_t)plan->stream_slots * per_unit_heads * (size_t)(head_dim + 2) * sizeof(float) +
+        (size_t)(batch + 1) * sizeof(int32_t);
     return true;
   }
   plan->stream = false;

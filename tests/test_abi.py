@@ -135,13 +135,14 @@ def test_prefill_empty_batch_is_a_no_op():
 
 def test_decode_workspace_plan():
     # automatic plan (stream-K): one partial slot per wave bound (4096) and per
-    # (sequence, KV head) unit, each holding (D + 2) floats per q head of the unit
-    assert pkv.paged_decode_workspace_size(3, 8, 2, 64, 32, 4) == (4096 + 3 * 2) * 4 * 66 * 4
+    # (sequence, KV head) unit, each holding (D + 2) floats per q head of the
+    # unit, then the batch's chunk prefix (batch + 1 int32)
+    assert pkv.paged_decode_workspace_size(3, 8, 2, 64, 32, 4) == (4096 + 3 * 2) * 4 * 66 * 4 + 4 * 4
     # an explicit split covering the whole sequence needs no merge workspace
     assert pkv.paged_decode_workspace_size(3, 8, 2, 64, 32, 4, 128) == 0
     # explicit split of 128 keys over 64 blocks of 16 -> 8 splits of (D + 2) floats per (b, h)
     assert pkv.paged_decode_workspace_size(3, 8, 2, 128, 16, 64, 128) == 3 * 8 * 8 * 130 * 4
-    # G = 16 splits into two head groups of 8 per KV head
-    assert pkv.paged_decode_workspace_size(2, 32, 2, 128, 16, 8) == (4096 + 2 * 2 * 2) * 8 * 130 * 4
+    # G = 16 splits into four head groups of 4 per KV head
+    assert pkv.paged_decode_workspace_size(2, 32, 2, 128, 16, 8) == (4096 + 2 * 2 * 4) * 4 * 130 * 4 + 3 * 4
     # unsupported argument -> 0
     assert pkv.paged_decode_workspace_size(3, 8, 3, 128, 16, 4) == 0
