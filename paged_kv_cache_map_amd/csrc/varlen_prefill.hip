@@ -473,6 +473,412 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
   for (int e = 0; e < NV; ++e) op[lane * NV + e] = o[e] * inv;
 }
 
+// ---------------------------------------------------------------------------
+// bf16 cache kernel: K/V tiles move HBM -> LDS by DMA, V is read transposed
+// ---------------------------------------------------------------------------
+//
+// * workgroup = 128 query rows of one (request, q head); 4 waves x 32 rows,
+//   two workgroups per CU (at most 256 registers per lane), so one wave's
+//   softmax overlaps another's MFMA on every SIMD.
+// * a 64-key tile of K and of V is copied straight from HBM into LDS with
+//   global_load_lds_dwordx4 (1 KiB per wave instruction; no registers).  The
+//   DMA writes each KiB contiguously, so bank conflicts are avoided by
+//   permuting what each lane fetches: LDS piece position i of row r holds the
+//   row's 16-byte piece i ^ (r mod pieces).  Tiles are double-buffered in two
+//   separate LDS objects and the next tile's DMA is in flight while the
+//   current one is computed.
+// * S^T = K Q^T (keys x queries) on v_mfma_f32_32x32x16_bf16 with K rows read
+//   from LDS as the A operand and Q held in registers as the B operand.
+// * O^T += V^T P^T: V stays row-major in LDS and ds_read_b64_tr_b16 hands each
+//   lane four consecutive keys of one head_dim element, which is the A operand
+//   layout; P^T (bf16) comes straight from the lane's own S^T registers.
+// * online softmax in the log2 domain with a lazy running max: the output is
+//   rescaled only when a row's max grows by more than 2^8, so most tiles skip
+//   the rescale; the result is the same exact algebra (numerator and
+//   denominator always share one reference max).  Row sums accumulate the
+//   bf16-rounded p that the MFMA consumes.
+// * block-table entries of tile t+1 are read (scalar loads) while tile t is
+//   computed; keys past the sequence end or in invalid blocks are masked, and
+//   their V rows are zeroed in LDS so that stale cache contents never reach
+//   the output.
+namespace dma {
+
+constexpr int kBM = 128;
+constexpr int kBN = 64;
+constexpr int kWavesPerWg = 4;
+constexpr float kRescaleBits = 8.0f;  // lazy-max threshold (log2 domain)
+
+template <int D>
+struct Tile {
+  static constexpr int row_bytes = D * 2;
+  static constexpr int pieces = row_bytes / 16;          // 16-byte pieces per row
+  static constexpr int bytes = kBN * row_bytes;          // one K or V tile
+  static constexpr int rows_per_dma = 1024 / row_bytes;  // rows one DMA instruction fills
+  static constexpr int dma_per_wave = bytes / 1024 / kWavesPerWg;
+  static constexpr int rows_per_wave = dma_per_wave * rows_per_dma;  // 16
+};
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
+__device__ __forceinline__ uint2 read_tr(const uint8_t* p) {
+  const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p);
+  return __builtin_bit_cast(uint2, x);
+}
+
+// Where the keys of one tile live, in 8-key groups (block_size >= 8, so a
+// group never straddles a block): the byte offsets of the first rows of this
+// wave's two groups (2 * wave, 2 * wave + 1), and which of the tile's keys
+// exist.  Block-table entries are read with scalar loads through the
+// constant address space (the table is not written while a kernel runs), so
+// waiting for them never waits for the K/V copies in flight.
+struct TileMap {
+  int64_t off[2];  // uniform
+  uint64_t valid;  // bit k: key k of the tile exists and sits in a valid block
+};
+
+struct Entries {
+  int32_t e[8];  // block id of each 8-key group of a tile (uniform)
+};
+
+template <bool PAGED>
+__device__ __forceinline__ void fetch_entries(Entries& en, const PrefillArgs& a, const int32_t* table,
+                                              int key0, int log2bs) {
+  if constexpr (PAGED) {
+    const_i32_ptr t = (const_i32_ptr)table;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) en.e[g] = t[min((key0 + 8 * g) >> log2bs, a.max_blocks_per_seq - 1)];
+  }
+}
+
+template <bool PAGED>
+__device__ __forceinline__ void resolve(TileMap& m, const PrefillArgs& a, const Entries& en,
+                                        int64_t row_stride, int key0, int lk, int log2bs, int wave) {
+  m.valid = 0;
+  m.off[0] = m.off[1] = 0;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const int key = key0 + 8 * g;
+    const int n = min(max(lk - key, 0), 8);  // existing keys of the group
+    bool ok = true;
+    if constexpr (PAGED) {
+      const int blk = en.e[g];
+      ok = blk >= 0 && blk < a.num_blocks;
+      const int64_t off = ok ? (((int64_t)blk << log2bs) + (key & ((1 << log2bs) - 1))) * row_stride : 0;
+      if (g == 2 * wave) m.off[0] = off;
+      if (g == 2 * wave + 1) m.off[1] = off;
+    }
+    const uint64_t bits = ok ? ((n >= 8) ? 0xffull : ((1ull << n) - 1)) : 0ull;
+    m.valid |= bits << (8 * g);
+  }
+}
+
+// DMA of this wave's rows of one tile (K and V) into buffers (kbuf, vbuf).
+// Paged rows come from the tile map; packed rows are clamped to the last key
+// (lk >= 1 whenever a tile exists), so no address leaves the request.
+template <int D, bool PAGED>
+__device__ __forceinline__ void issue_tile(const TileMap& m, const uint8_t* kbase, const uint8_t* vbase,
+                                           int64_t row_stride, int key0, int lk, uint8_t* kbuf,
+                                           uint8_t* vbuf, int wave, int lane) {
+  using T = Tile<D>;
+  const int rr = lane / T::pieces;   // row within the instruction
+  const int pos = lane % T::pieces;  // LDS piece position
+#pragma unroll
+  for (int j = 0; j < T::dma_per_wave; ++j) {
+    const int chunk = wave * T::dma_per_wave + j;
+    const int r = chunk * T::rows_per_dma + rr;  // row within the tile
+    const int piece = pos ^ (r & (T::pieces - 1));
+    int64_t go;
+    if constexpr (PAGED) {
+      go = m.off[(j * T::rows_per_dma) >> 3] + (int64_t)(r & 7) * row_stride + piece * 16;
+    } else {
+      go = (int64_t)min(key0 + r, lk - 1) * row_stride + piece * 16;
+    }
+    __builtin_amdgcn_global_load_lds((const void*)(kbase + go), (lds_void_t*)(kbuf + chunk * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(vbase + go), (lds_void_t*)(vbuf + chunk * 1024), 16, 0, 0);
+  }
+}
+
+// Zero this wave's V rows of keys that do not exist (after its DMA landed).
+template <int D>
+__device__ __forceinline__ void zero_rows(uint64_t valid, uint8_t* vbuf, int wave, int lane) {
+  using T = Tile<D>;
+  const int r0 = wave * T::rows_per_wave;
+  const uint32_t bad = ~(uint32_t)(valid >> r0) & ((1u << T::rows_per_wave) - 1);
+  if (bad == 0) return;
+  constexpr int per_pass = 64 * 16 / T::row_bytes;  // rows per pass
+#pragma unroll
+  for (int i = 0; i < T::rows_per_wave; i += per_pass) {
+    const int r = i + lane / T::pieces;
+    if ((bad >> r) & 1u)
+      *reinterpret_cast<uint4*>(vbuf + (r0 + r) * T::row_bytes + (lane % T::pieces) * 16) =
+          make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+template <int D, bool PAGED>
+__global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int q_tiles, int total_wg) {
+  using T = Tile<D>;
+  constexpr int KS = D / 16;  // MFMA k-steps over head_dim
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  constexpr int R = T::pieces;
+  // two tile buffers as separate objects, so the compiler can tell the DMA
+  // into one from the reads of the other and waits only for the right one
+  __shared__ __attribute__((aligned(1024))) uint8_t k_a[T::bytes], v_a[T::bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_b[T::bytes], v_b[T::bytes];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int half = lane >> 5, col = lane & 31;
+
+  // XCD-aware renumbering (hardware workgroup i runs on XCD i % 8), then the
+  // query tiles of a (request, head) from last to first: under the causal
+  // mask the last tiles carry the most keys, so they start first.
+  const int hw = blockIdx.x;
+  const int per_xcd = (total_wg + 7) / 8;
+  const int logical = (hw % 8) * per_xcd + hw / 8;
+  if (logical >= total_wg) return;
+  const int group = a.num_heads / a.num_kv_heads;
+  const int qt = q_tiles - 1 - logical % q_tiles;
+  const int rest = logical / q_tiles;
+  const int h = rest % a.num_heads;
+  const int b = rest / a.num_heads;
+  const int g = h / group;
+
+  const int q_start = a.cu_seqlens_q[b];
+  int lq = a.cu_seqlens_q[b + 1] - q_start;
+  if (lq > a.max_seqlen_q) lq = a.max_seqlen_q;
+  if (q_start < 0 || q_start >= a.total_q) lq = 0;
+  else if (lq > a.total_q - q_start) lq = a.total_q - q_start;
+  const int q0 = qt * kBM;
+  if (q0 >= lq) return;
+  const int k_start = a.cu_seqlens_k[b];
+  int lk = a.cu_seqlens_k[b + 1] - k_start;
+  if (lk < 0) lk = 0;
+  if constexpr (PAGED) {
+    lk = min(lk, a.max_blocks_per_seq * a.block_size);
+  } else {
+    if (k_start < 0 || k_start > a.total_k) lk = 0;
+    else if (lk > a.total_k - k_start) lk = a.total_k - k_start;
+  }
+  const int offset = lk - lq;  // bottom-right causal alignment
+  const int last_row = min(q0 + kBM, lq) - 1;
+  int key_end = a.causal ? min(lk, last_row + offset + 1) : lk;
+  if (key_end < 0) key_end = 0;
+  const int n_tiles = (key_end + kBN - 1) / kBN;
+
+  const int64_t row_stride = (int64_t)a.num_kv_heads * T::row_bytes;
+  const uint8_t* kbase = a.k + g * T::row_bytes + (PAGED ? 0 : (int64_t)k_start * row_stride);
+  const uint8_t* vbase = a.v + g * T::row_bytes + (PAGED ? 0 : (int64_t)k_start * row_stride);
+  const int32_t* table = PAGED ? a.block_table + (int64_t)b * a.max_blocks_per_seq : nullptr;
+  const int log2bs = PAGED ? __builtin_ctz(a.block_size) : 0;
+
+  // this wave's query column: row q0 + 32 * wave + col
+  const int qrow = q0 + wave * 32 + col;
+  const bool qvalid = qrow < lq;
+  // The row max is taken over unscaled scores, which needs scale > 0: a
+  // negative scale is applied as |scale| to -q (bf16 negation is exact), and
+  // a zero scale as 1e-30 (every logit then rounds to exactly 0 in the
+  // exponent, as with scale 0, while masked keys stay at -inf instead of
+  // -inf * 0).
+  const uint32_t q_sign = a.softmax_scale < 0.0f ? 0x80008000u : 0u;
+  const float scale = fmaxf(fabsf(a.softmax_scale) * kLog2e, 1e-30f);
+  uint4 qf[KS];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((int64_t)(q_start + (qvalid ? qrow : 0)) * a.num_heads + h) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 x = *reinterpret_cast<const uint4*>(qp + ks * 16);
+      qf[ks] = qvalid ? make_uint4(x.x ^ q_sign, x.y ^ q_sign, x.z ^ q_sign, x.w ^ q_sign)
+                      : make_uint4(0u, 0u, 0u, 0u);
+    }
+    // resolve the q loads before the first DMA: the tile loop then never has
+    // to wait for them behind a copy
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+  }
+
+  // per-lane LDS offsets (the swizzle depends on the row, known per lane)
+  // K: row kb*32 + col, piece 2*ks + half
+  int k_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = col * T::row_bytes + (((2 * ks + half) ^ (col & (R - 1))) << 4);
+  // V (transposed reads): key kk*16 + 8x + key_l, element db*32 + dd_l .. +3
+  const int key_l = 4 * half + (lane & 15) / 4;
+  const int dd_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int v_off[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int key = 8 * x + key_l;
+      const int dd = db * 32 + dd_l;
+      v_off[db][x] = key * T::row_bytes + (((dd >> 3) ^ (key & (R - 1))) << 4) + (dd & 7) * 2;
+    }
+
+  f32x16_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
+  float m = kNegBig, l = 0.0f;
+
+  // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, lgkmcnt in 11:8)
+  constexpr int kDma = 2 * T::dma_per_wave;  // DMA instructions per tile per wave
+  constexpr int kWaitLgkm0 = 0xc07f;         // lgkmcnt(0) only
+
+  // One tile: scores, softmax, output update, reading buffers (kb_lds, vb_lds).
+  auto compute = [&](const uint8_t* kb_lds, const uint8_t* vb_lds, int key0,
+                     uint64_t valid) __attribute__((always_inline)) {
+    // S^T for two 32-key blocks, interleaved, next fragments read ahead
+    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+    {
+      uint4 k0 = *reinterpret_cast<const uint4*>(kb_lds + k_off[0]);
+      uint4 k1 = *reinterpret_cast<const uint4*>(kb_lds + 32 * T::row_bytes + k_off[0]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 n0 = k0, n1 = k1;
+        if (ks + 1 < KS) {
+          n0 = *reinterpret_cast<const uint4*>(kb_lds + k_off[ks + 1]);
+          n1 = *reinterpret_cast<const uint4*>(kb_lds + 32 * T::row_bytes + k_off[ks + 1]);
+        }
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qf[ks]), s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qf[ks]), s[1], 0, 0, 0);
+        k0 = n0;
+        k1 = n1;
+      }
+    }
+    // mask, row max
+    const bool need_mask = valid != ~0ull || (a.causal && key0 + kBN - 1 > q0 + wave * 32 + offset);
+    float mx = -INFINITY;
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kt = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);  // key within the tile
+          const bool vis = ((valid >> kt) & 1ull) && (!a.causal || key0 + kt <= qrow + offset);
+          s[kb][r] = vis ? s[kb][r] : -INFINITY;
+          mx = fmaxf(mx, s[kb][r]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    }
+    mx = fmaxf(mx, shfl_xor(mx, 32)) * scale;
+    // lazy running max: move it (and rescale) only when it grows by > 2^8
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleBits) != 0) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    const float neg_m = -m;
+    uint4 pb[2][2];  // [key block][16-key half] bf16 B operands
+    float ps = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        f32x8_t pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(s[kb][hs * 8 + e], scale, neg_m));
+        pb[kb][hs] = __builtin_bit_cast(uint4, __builtin_convertvector(pv, bf16x8_t));
+        // row sum of the bf16 values the MFMA uses: dot with (1, 1)
+        ps = dot2_bf16(pb[kb][hs].x, 0x3f803f80u, ps);
+        ps = dot2_bf16(pb[kb][hs].y, 0x3f803f80u, ps);
+        ps = dot2_bf16(pb[kb][hs].z, 0x3f803f80u, ps);
+        ps = dot2_bf16(pb[kb][hs].w, 0x3f803f80u, ps);
+      }
+    l += ps;
+    // O^T += V^T P^T over the four 16-key groups
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint2 lo = read_tr(vb_lds + kk * 16 * T::row_bytes + v_off[db][0]);
+        const uint2 hi = read_tr(vb_lds + kk * 16 * T::row_bytes + v_off[db][1]);
+        const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pb[kk >> 1][kk & 1]),
+                                                        o[db], 0, 0, 0);
+      }
+  };
+
+  // Tile t from buffer (kc, vc) while tile t + 1 is copied into (kn, vn).
+  // Every memory operation of a step is unconditional, so the compiler's wait
+  // counts stay exact; past the last tile the copy re-reads in-bounds rows
+  // into the idle buffer and is drained before the workgroup ends.
+  TileMap cur;
+  Entries ent_nxt;
+  auto step = [&](uint8_t* kc, uint8_t* vc, uint8_t* kn, uint8_t* vn, int t) __attribute__((always_inline)) {
+    const int key0 = t * kBN;
+    const uint64_t valid = cur.valid;
+    TileMap nxt;
+    resolve<PAGED>(nxt, a, ent_nxt, row_stride, key0 + kBN, lk, log2bs, wave);
+    fetch_entries<PAGED>(ent_nxt, a, table, key0 + 2 * kBN, log2bs);
+    issue_tile<D, PAGED>(nxt, kbase, vbase, row_stride, key0 + kBN, lk, kn, vn, wave, lane);
+    cur = nxt;
+    // tile t has landed once only the DMA of tile t + 1 remains in flight
+    __builtin_amdgcn_s_waitcnt(0x0f70 | kDma);
+    zero_rows<D>(valid, vc, wave, lane);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    compute(kc, vc, key0, valid);
+    // every wave is done reading (kc, vc) before tile t + 2 is copied into it
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+  };
+  if (n_tiles > 0) {
+    Entries ent0;
+    fetch_entries<PAGED>(ent0, a, table, 0, log2bs);
+    fetch_entries<PAGED>(ent_nxt, a, table, kBN, log2bs);
+    resolve<PAGED>(cur, a, ent0, row_stride, 0, lk, log2bs, wave);
+    issue_tile<D, PAGED>(cur, kbase, vbase, row_stride, 0, lk, k_a, v_a, wave, lane);
+    for (int t = 0; t < n_tiles; t += 2) {
+      step(k_a, v_a, k_b, v_b, t);
+      if (t + 1 >= n_tiles) break;
+      step(k_b, v_b, k_a, v_a, t + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // the copy past the last tile lands before LDS is released
+  }
+
+  // normalise and store: lane holds O^T rows 8*(r/4) + 4*half + r%4 of each 32-row block
+  l += shfl_xor(l, 32);
+  if (!qvalid) return;
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q_start + qrow) * a.num_heads + h) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d = db * 32 + rg * 8 + half * 4;
+      const uint32_t w0 = pack_bf16x2(o[db][rg * 4 + 0] * inv, o[db][rg * 4 + 1] * inv);
+      const uint32_t w1 = pack_bf16x2(o[db][rg * 4 + 2] * inv, o[db][rg * 4 + 3] * inv);
+      *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
+    }
+}
+
+template <int D>
+hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
+  const int q_tiles = (a.max_seqlen_q + kBM - 1) / kBM;
+  const int64_t wg = (int64_t)q_tiles * a.num_heads * a.batch;
+  if (wg > 0x7fffffff / 2) return hipErrorInvalidValue;
+  const int total = (int)wg;
+  const int grid = (total + 7) / 8 * 8;
+  if (a.block_table != nullptr) {
+    hipLaunchKernelGGL((prefill_dma_kernel<D, true>), dim3(grid), dim3(256), 0, stream, a, q_tiles, total);
+  } else {
+    hipLaunchKernelGGL((prefill_dma_kernel<D, false>), dim3(grid), dim3(256), 0, stream, a, q_tiles, total);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dma
+
 template <int KVT, int D>
 hipError_t launch_mfma(const PrefillArgs& a, hipStream_t stream) {
   const int q_tiles = (a.max_seqlen_q + BM - 1) / BM;
@@ -499,8 +905,8 @@ hipError_t launch_varlen_prefill(const PrefillArgs& a, hipStream_t stream) {
     return launch_f32<128>(a, stream);
   }
   if (a.kv_dtype == kBF16) {
-    if (a.head_dim == 64) return launch_mfma<kBF16, 64>(a, stream);
-    return launch_mfma<kBF16, 128>(a, stream);
+    if (a.head_dim == 64) return dma::launch<64>(a, stream);
+    return dma::launch<128>(a, stream);
   }
   if (a.head_dim == 64) return launch_mfma<kFP8, 64>(a, stream);
   return launch_mfma<kFP8, 128>(a, stream);

@@ -267,6 +267,27 @@ def test_prefill_noncausal_contiguous_matches_oracle():
         assert max_err(out_f64(out), want) <= TOL["bf16"], causal
 
 
+def test_negative_and_zero_scale():
+    """The softmax scale is any real: negative and zero scales match the oracle
+    for prefill (packed and paged) and decode."""
+    c = workloads.random_varlen_contig("neg", 77, [40, 130, 1], [40, 200, 65], num_heads=8,
+                                       num_kv_heads=2, head_dim=128, dtype="bf16")
+    for sc in (-0.2, 0.0):
+        say("scale", sc)
+        out = pkv.varlen_prefill(to_dev(c.q, "bf16"), to_dev(c.k, "bf16"), to_dev(c.v, "bf16"),
+                                 to_dev(c.cu_seqlens_q, "i32"), to_dev(c.cu_seqlens_k, "i32"),
+                                 c.max_seqlen_q, c.max_seqlen_k, sc, True)
+        want = paged.varlen_prefill(c.q, "bf16", c.k, c.v, "bf16", c.cu_seqlens_q, c.cu_seqlens_k,
+                                    sc, True)
+        assert max_err(out_f64(out), want) <= TOL["bf16"], sc
+    step = workloads.build_step("neg_scale", 78, num_heads=8, num_kv_heads=2, head_dim=128,
+                                block_size=16, q_dtype="bf16", cache_dtype="bf16",
+                                prefix=[100, 0, 300], new=[70, 1, 1],
+                                kinds=["prefill", "decode", "decode"])
+    step.scale = -0.15
+    run_step_and_check(step)
+
+
 # ---------------------------------------------------------------------------
 # fp8 codec through the library
 # ---------------------------------------------------------------------------
