@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--split-keys", type=int, default=0,
                     help="decode split size in keys (0: the library's automatic plan)")
+    ap.add_argument("--only", default=None,
+                    help="diagnostic: time one named workload and print its kernel times only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 512 MiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -280,6 +282,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import paged_kv_cache_map_amd as pkv
     pkv.library()
+
+    if args.only:
+        print(f"[bench] {args.only} (diagnostic)", flush=True)
+        _, res = measure(args.only, args.steps, args.warmup, args.split_keys)
+        print(json.dumps({"diagnostic": args.only,
+                          **{k: (round(v, 5) if isinstance(v, float) else v) for k, v in res.items()}}),
+              flush=True)
+        return
 
     print("[bench] llama8b_decode", flush=True)
     step, main_res = measure("llama8b_decode", args.steps, args.warmup, args.split_keys)

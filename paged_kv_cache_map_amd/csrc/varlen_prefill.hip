@@ -484,7 +484,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
 //   global_load_lds_dwordx4 (1 KiB per wave instruction; no registers).  The
 //   DMA writes each KiB contiguously, so bank conflicts are avoided by
 //   permuting what each lane fetches: LDS piece position i of row r holds the
-//   row's 16-byte piece i ^ (r mod pieces).  Tiles are double-buffered in two
+//   row's 16-byte piece i ^ swz(r).  Tiles are double-buffered in two
 //   separate LDS objects and the next tile's DMA is in flight while the
 //   current one is computed.
 // * S^T = K Q^T (keys x queries) on v_mfma_f32_32x32x16_bf16 with K rows read
@@ -518,6 +518,17 @@ struct Tile {
   static constexpr int rows_per_wave = dma_per_wave * rows_per_dma;  // 16
 };
 
+// LDS piece permutation of row r: a linear map (over GF(2)) of the row's low
+// four bits, chosen so that both reads of a tile are free of bank conflicts
+// (checked for 32 and 64 banks): the K operand reads (16 consecutive rows,
+// one piece) and the transposed V reads (4 consecutive rows x 4 pieces).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  // images of row bits 0..3
+  constexpr int b0 = D == 128 ? 4 : 2, b1 = D == 128 ? 10 : 4, b2 = 1, b3 = 2;
+  return ((r & 1) ? b0 : 0) ^ ((r & 2) ? b1 : 0) ^ ((r & 4) ? b2 : 0) ^ ((r & 8) ? b3 : 0);
+}
+
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -537,6 +548,7 @@ __device__ __forceinline__ uint2 read_tr(const uint8_t* p) {
 struct TileMap {
   int64_t off[2];  // uniform
   uint64_t valid;  // bit k: key k of the tile exists and sits in a valid block
+  bool blocks_ok;  // every block of the tile is valid (valid is then a prefix mask)
 };
 
 struct Entries {
@@ -556,22 +568,28 @@ __device__ __forceinline__ void fetch_entries(Entries& en, const PrefillArgs& a,
 template <bool PAGED>
 __device__ __forceinline__ void resolve(TileMap& m, const PrefillArgs& a, const Entries& en,
                                         int64_t row_stride, int key0, int lk, int log2bs, int wave) {
-  m.valid = 0;
-  m.off[0] = m.off[1] = 0;
+  const int n = lk - key0;  // keys of the tile that exist (clamped below)
+  const uint64_t len_mask = n >= 64 ? ~0ull : (n <= 0 ? 0ull : ((1ull << n) - 1));
+  if constexpr (PAGED) {
+    uint64_t blk_mask = 0;
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const int key = key0 + 8 * g;
-    const int n = min(max(lk - key, 0), 8);  // existing keys of the group
-    bool ok = true;
-    if constexpr (PAGED) {
-      const int blk = en.e[g];
-      ok = blk >= 0 && blk < a.num_blocks;
-      const int64_t off = ok ? (((int64_t)blk << log2bs) + (key & ((1 << log2bs) - 1))) * row_stride : 0;
-      if (g == 2 * wave) m.off[0] = off;
-      if (g == 2 * wave + 1) m.off[1] = off;
+    for (int g = 0; g < 8; ++g)
+      blk_mask |= ((uint32_t)en.e[g] < (uint32_t)a.num_blocks ? 0xffull : 0ull) << (8 * g);
+    m.valid = len_mask & blk_mask;
+    m.blocks_ok = blk_mask == ~0ull;
+    const int e0 = wave == 0 ? en.e[0] : wave == 1 ? en.e[2] : wave == 2 ? en.e[4] : en.e[6];
+    const int e1 = wave == 0 ? en.e[1] : wave == 1 ? en.e[3] : wave == 2 ? en.e[5] : en.e[7];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int blk = x ? e1 : e0;
+      const int key = key0 + 8 * (2 * wave + x);
+      const bool ok = (uint32_t)blk < (uint32_t)a.num_blocks;
+      m.off[x] = ok ? (((int64_t)blk << log2bs) + (key & ((1 << log2bs) - 1))) * row_stride : 0;
     }
-    const uint64_t bits = ok ? ((n >= 8) ? 0xffull : ((1ull << n) - 1)) : 0ull;
-    m.valid |= bits << (8 * g);
+  } else {
+    m.valid = len_mask;
+    m.blocks_ok = true;
+    m.off[0] = m.off[1] = 0;  // packed rows are addressed per lane
   }
 }
 
@@ -589,7 +607,7 @@ __device__ __forceinline__ void issue_tile(const TileMap& m, const uint8_t* kbas
   for (int j = 0; j < T::dma_per_wave; ++j) {
     const int chunk = wave * T::dma_per_wave + j;
     const int r = chunk * T::rows_per_dma + rr;  // row within the tile
-    const int piece = pos ^ (r & (T::pieces - 1));
+    const int piece = pos ^ swz<D>(r);
     int64_t go;
     if constexpr (PAGED) {
       go = m.off[(j * T::rows_per_dma) >> 3] + (int64_t)(r & 7) * row_stride + piece * 16;
@@ -623,7 +641,6 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
   using T = Tile<D>;
   constexpr int KS = D / 16;  // MFMA k-steps over head_dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  constexpr int R = T::pieces;
   // two tile buffers as separate objects, so the compiler can tell the DMA
   // into one from the reads of the other and waits only for the right one
   __shared__ __attribute__((aligned(1024))) uint8_t k_a[T::bytes], v_a[T::bytes];
@@ -704,7 +721,7 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
   // K: row kb*32 + col, piece 2*ks + half
   int k_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_off[ks] = col * T::row_bytes + (((2 * ks + half) ^ (col & (R - 1))) << 4);
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = col * T::row_bytes + (((2 * ks + half) ^ swz<D>(col)) << 4);
   // V (transposed reads): key kk*16 + 8x + key_l, element db*32 + dd_l .. +3
   const int key_l = 4 * half + (lane & 15) / 4;
   const int dd_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -715,7 +732,7 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
     for (int x = 0; x < 2; ++x) {
       const int key = 8 * x + key_l;
       const int dd = db * 32 + dd_l;
-      v_off[db][x] = key * T::row_bytes + (((dd >> 3) ^ (key & (R - 1))) << 4) + (dd & 7) * 2;
+      v_off[db][x] = key * T::row_bytes + (((dd >> 3) ^ swz<D>(key)) << 4) + (dd & 7) * 2;
     }
 
   f32x16_t o[DB];
@@ -728,8 +745,8 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
   constexpr int kWaitLgkm0 = 0xc07f;         // lgkmcnt(0) only
 
   // One tile: scores, softmax, output update, reading buffers (kb_lds, vb_lds).
-  auto compute = [&](const uint8_t* kb_lds, const uint8_t* vb_lds, int key0,
-                     uint64_t valid) __attribute__((always_inline)) {
+  auto compute = [&](const uint8_t* kb_lds, const uint8_t* vb_lds, int key0, uint64_t valid,
+                     bool blocks_ok) __attribute__((always_inline)) {
     // S^T for two 32-key blocks, interleaved, next fragments read ahead
     f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
     {
@@ -748,25 +765,33 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
         k1 = n1;
       }
     }
-    // mask, row max
-    const bool need_mask = valid != ~0ull || (a.causal && key0 + kBN - 1 > q0 + wave * 32 + offset);
-    float mx = -INFINITY;
-    if (need_mask) {
+    // mask, row max.  Key kt of the tile is visible to this lane's row iff
+    // kt < lim (sequence end, causal diagonal) and its 8-key group's block is
+    // valid.  Register r of block kb holds key kb*32 + 8*(r/4) + 4*half + r%4.
+    const int lim = min(a.causal ? qrow + offset - key0 + 1 : kBN, lk - key0);
+    const int lim_wave = min(a.causal ? q0 + wave * 32 + offset - key0 + 1 : kBN, lk - key0);
+    if (lim_wave < kBN) {
+      const int lim_h = lim - 4 * half;  // kt - 4 * half is a constant per register
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kt = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);  // key within the tile
-          const bool vis = ((valid >> kt) & 1ull) && (!a.causal || key0 + kt <= qrow + offset);
-          s[kb][r] = vis ? s[kb][r] : -INFINITY;
-          mx = fmaxf(mx, s[kb][r]);
+          const int kc = kb * 32 + 8 * (r >> 2) + (r & 3);
+          s[kb][r] = kc < lim_h ? s[kb][r] : -INFINITY;
         }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     }
+    if (!blocks_ok) {  // corrupt block table: skip the keys of invalid blocks
+#pragma unroll
+      for (int grp = 0; grp < 8; ++grp)
+        if (((valid >> (8 * grp)) & 0xffull) == 0)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[grp >> 2][4 * (grp & 3) + i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, shfl_xor(mx, 32)) * scale;
     // lazy running max: move it (and rescale) only when it grows by > 2^8
     if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleBits) != 0) {
@@ -817,6 +842,7 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
   auto step = [&](uint8_t* kc, uint8_t* vc, uint8_t* kn, uint8_t* vn, int t) __attribute__((always_inline)) {
     const int key0 = t * kBN;
     const uint64_t valid = cur.valid;
+    const bool blocks_ok = cur.blocks_ok;
     TileMap nxt;
     resolve<PAGED>(nxt, a, ent_nxt, row_stride, key0 + kBN, lk, log2bs, wave);
     fetch_entries<PAGED>(ent_nxt, a, table, key0 + 2 * kBN, log2bs);
@@ -827,7 +853,7 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
     zero_rows<D>(valid, vc, wave, lane);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
-    compute(kc, vc, key0, valid);
+    compute(kc, vc, key0, valid, blocks_ok);
     // every wave is done reading (kc, vc) before tile t + 2 is copied into it
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
