@@ -21,8 +21,9 @@
 //   flight while the current tile is computed.  fp8 caches are dequantised to
 //   bf16 (exact) while staging; the K scale folds into the logit scale, the V
 //   scale into the output.
-// * workgroups are renumbered so that the tiles of one (request, KV head) run
-//   on the same XCD and share its L2.
+// * workgroups are renumbered (work_item) so that the tiles of one (request,
+//   KV head) run on the same XCD and share its L2, with the pairs balanced
+//   over the XCDs and the longest query tiles first.
 //
 // fp32 kernel: a plain per-row wave kernel (lanes over head_dim), kept for
 // fp32 accuracy checks; it is not tuned.
@@ -87,6 +88,41 @@ __device__ __forceinline__ const uint8_t* key_row(const KeyAddr& ka, int j) {
   const int blk = ka.table[j >> ka.log2bs];
   if (blk < 0 || blk >= ka.num_blocks) return nullptr;
   return ka.base + (((int64_t)blk << ka.log2bs) + (j & ka.bs_mask)) * ka.row_stride;
+}
+
+// Work item of hardware workgroup `hw`: (request b, q head h, query tile qt).
+// Workgroup i runs on XCD i % 8.  Each (request, KV head) pair lives on one
+// XCD (pair p on XCD p % 8), so the q heads and query tiles that share its
+// K/V share that XCD's L2, and the pairs are dealt round-robin so every XCD
+// gets the same share however the lengths vary.  Within an XCD the query
+// tiles run from last to first: under the causal mask the last tiles carry
+// the most keys, so the longest work starts first.  Returns false for the
+// padding workgroups of XCDs with fewer pairs.
+struct WorkItem {
+  int b, h, g, qt;
+};
+
+__device__ __forceinline__ bool work_item(int hw, int q_tiles, int batch, int num_heads,
+                                          int num_kv_heads, WorkItem& w) {
+  const int G = num_heads / num_kv_heads;
+  const int pairs = batch * num_kv_heads;
+  const int x = hw & 7, j = hw >> 3;
+  const int px = (pairs - x + 7) >> 3;  // pairs on XCD x
+  const int per_tile = px * G;          // items per query tile on XCD x
+  if (j >= q_tiles * per_tile) return false;
+  w.qt = q_tiles - 1 - j / per_tile;
+  const int rem = j % per_tile;
+  const int pidx = x + 8 * (rem / G);
+  w.b = pidx / num_kv_heads;
+  w.g = pidx % num_kv_heads;
+  w.h = w.g * G + rem % G;
+  return true;
+}
+
+// Grid for work_item(): 8 XCDs x the largest per-XCD share.
+__host__ __forceinline__ int64_t work_grid(int q_tiles, int batch, int num_heads, int num_kv_heads) {
+  const int64_t pairs = (int64_t)batch * num_kv_heads;
+  return 8 * (int64_t)q_tiles * ((pairs + 7) / 8) * (num_heads / num_kv_heads);
 }
 
 // How the 256 threads of a workgroup move one 64-key tile from HBM to LDS.
@@ -206,7 +242,7 @@ struct Loader {
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
 
 template <int KVT, int D>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int q_tiles, int total_wg) {
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int q_tiles) {
   using L = Lds<D>;
   constexpr int KS = D / 16;   // MFMA k-steps over head_dim
   constexpr int DB = D / 32;   // 32-row blocks of O^T
@@ -216,18 +252,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int q_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
 
-  // XCD-aware renumbering: hardware workgroup i runs on XCD i % 8; give each
-  // XCD a contiguous range of logical work so one request/KV head stays on one L2.
-  const int hw = blockIdx.x;
-  const int per_xcd = (total_wg + 7) / 8;
-  const int logical = (hw % 8) * per_xcd + hw / 8;
-  if (logical >= total_wg) return;
-  const int group = a.num_heads / a.num_kv_heads;
-  const int qt = logical % q_tiles;
-  const int rest = logical / q_tiles;
-  const int h = rest % a.num_heads;  // q heads of one KV head are adjacent
-  const int b = rest / a.num_heads;
-  const int g = h / group;
+  WorkItem w;
+  if (!work_item(blockIdx.x, q_tiles, a.batch, a.num_heads, a.num_kv_heads, w)) return;
+  const int qt = w.qt, h = w.h, b = w.b, g = w.g;
 
   const int q_start = a.cu_seqlens_q[b];
   int lq = a.cu_seqlens_q[b + 1] - q_start;
@@ -637,7 +664,7 @@ __device__ __forceinline__ void zero_rows(uint64_t valid, uint8_t* vbuf, int wav
 }
 
 template <int D, bool PAGED>
-__global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int q_tiles, int total_wg) {
+__global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int q_tiles) {
   using T = Tile<D>;
   constexpr int KS = D / 16;  // MFMA k-steps over head_dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
@@ -650,19 +677,9 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
 
-  // XCD-aware renumbering (hardware workgroup i runs on XCD i % 8), then the
-  // query tiles of a (request, head) from last to first: under the causal
-  // mask the last tiles carry the most keys, so they start first.
-  const int hw = blockIdx.x;
-  const int per_xcd = (total_wg + 7) / 8;
-  const int logical = (hw % 8) * per_xcd + hw / 8;
-  if (logical >= total_wg) return;
-  const int group = a.num_heads / a.num_kv_heads;
-  const int qt = q_tiles - 1 - logical % q_tiles;
-  const int rest = logical / q_tiles;
-  const int h = rest % a.num_heads;
-  const int b = rest / a.num_heads;
-  const int g = h / group;
+  WorkItem w;
+  if (!work_item(blockIdx.x, q_tiles, a.batch, a.num_heads, a.num_kv_heads, w)) return;
+  const int qt = w.qt, h = w.h, b = w.b, g = w.g;
 
   const int q_start = a.cu_seqlens_q[b];
   int lq = a.cu_seqlens_q[b + 1] - q_start;
@@ -891,14 +908,12 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
 template <int D>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const int q_tiles = (a.max_seqlen_q + kBM - 1) / kBM;
-  const int64_t wg = (int64_t)q_tiles * a.num_heads * a.batch;
-  if (wg > 0x7fffffff / 2) return hipErrorInvalidValue;
-  const int total = (int)wg;
-  const int grid = (total + 7) / 8 * 8;
+  const int64_t grid = work_grid(q_tiles, a.batch, a.num_heads, a.num_kv_heads);
+  if (grid > 0x7fffffff / 2) return hipErrorInvalidValue;
   if (a.block_table != nullptr) {
-    hipLaunchKernelGGL((prefill_dma_kernel<D, true>), dim3(grid), dim3(256), 0, stream, a, q_tiles, total);
+    hipLaunchKernelGGL((prefill_dma_kernel<D, true>), dim3((unsigned)grid), dim3(256), 0, stream, a, q_tiles);
   } else {
-    hipLaunchKernelGGL((prefill_dma_kernel<D, false>), dim3(grid), dim3(256), 0, stream, a, q_tiles, total);
+    hipLaunchKernelGGL((prefill_dma_kernel<D, false>), dim3((unsigned)grid), dim3(256), 0, stream, a, q_tiles);
   }
   return hipGetLastError();
 }
@@ -908,11 +923,9 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
 template <int KVT, int D>
 hipError_t launch_mfma(const PrefillArgs& a, hipStream_t stream) {
   const int q_tiles = (a.max_seqlen_q + BM - 1) / BM;
-  const int64_t wg = (int64_t)q_tiles * a.num_heads * a.batch;
-  if (wg > 0x7fffffff / 2) return hipErrorInvalidValue;
-  const int total = (int)wg;
-  const int grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL((prefill_kernel<KVT, D>), dim3(grid), dim3(kThreads), 0, stream, a, q_tiles, total);
+  const int64_t grid = work_grid(q_tiles, a.batch, a.num_heads, a.num_kv_heads);
+  if (grid > 0x7fffffff / 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_kernel<KVT, D>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a, q_tiles);
   return hipGetLastError();
 }
 
