@@ -28,8 +28,19 @@
 // fp32 kernel: a plain per-row wave kernel (lanes over head_dim), kept for
 // fp32 accuracy checks; it is not tuned.
 
+#include <type_traits>
+
 #include "pkv_device.hpp"
 #include "pkv_internal.h"
+
+// Launch shape of the bf16 prefill kernel: waves per workgroup (32 query
+// rows each) and LDS stages of the K/V copy pipeline.
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 4
+#endif
+#ifndef PKV_PREFILL_STAGES
+#define PKV_PREFILL_STAGES 2
+#endif
 
 namespace pkv {
 namespace {
@@ -530,19 +541,21 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
 //   the output.
 namespace dma {
 
-constexpr int kBM = 128;
 constexpr int kBN = 64;
-constexpr int kWavesPerWg = 4;
 constexpr float kRescaleBits = 8.0f;  // lazy-max threshold (log2 domain)
 
-template <int D>
+// Tile geometry for head_dim D and W waves per workgroup (32 query rows per
+// wave): one DMA instruction fills 1 KiB of a K or V tile.
+template <int D, int W>
 struct Tile {
   static constexpr int row_bytes = D * 2;
   static constexpr int pieces = row_bytes / 16;          // 16-byte pieces per row
   static constexpr int bytes = kBN * row_bytes;          // one K or V tile
   static constexpr int rows_per_dma = 1024 / row_bytes;  // rows one DMA instruction fills
-  static constexpr int dma_per_wave = bytes / 1024 / kWavesPerWg;
-  static constexpr int rows_per_wave = dma_per_wave * rows_per_dma;  // 16
+  static constexpr int dma_per_wave = bytes / 1024 / W;  // per K (or V) tile
+  static constexpr int rows_per_wave = kBN / W;
+  static constexpr int groups_per_wave = rows_per_wave / 8;  // 8-key groups
+  static_assert(dma_per_wave >= 1 && groups_per_wave >= 1, "tile shape");
 };
 
 // LDS piece permutation of row r: a linear map (over GF(2)) of the row's low
@@ -568,14 +581,16 @@ __device__ __forceinline__ uint2 read_tr(const uint8_t* p) {
 
 // Where the keys of one tile live, in 8-key groups (block_size >= 8, so a
 // group never straddles a block): the byte offsets of the first rows of this
-// wave's two groups (2 * wave, 2 * wave + 1), and which of the tile's keys
-// exist.  Block-table entries are read with scalar loads through the
-// constant address space (the table is not written while a kernel runs), so
-// waiting for them never waits for the K/V copies in flight.
+// wave's groups, and which of the tile's keys exist.  Block-table entries are
+// read with scalar loads through the constant address space (the table is
+// not written while a kernel runs), issued after a tile's LDS reads are done:
+// scalar loads share their wait counter with LDS reads, and an outstanding
+// one would hold up every LDS wait of the next tile.
+template <int GPW>
 struct TileMap {
-  int64_t off[2];  // uniform
-  uint64_t valid;  // bit k: key k of the tile exists and sits in a valid block
-  bool blocks_ok;  // every block of the tile is valid (valid is then a prefix mask)
+  int64_t off[GPW];  // uniform
+  uint64_t valid;    // bit k: key k of the tile exists and sits in a valid block
+  bool blocks_ok;    // every block of the tile is valid (valid is then a prefix mask)
 };
 
 struct Entries {
@@ -592,8 +607,8 @@ __device__ __forceinline__ void fetch_entries(Entries& en, const PrefillArgs& a,
   }
 }
 
-template <bool PAGED>
-__device__ __forceinline__ void resolve(TileMap& m, const PrefillArgs& a, const Entries& en,
+template <bool PAGED, int GPW>
+__device__ __forceinline__ void resolve(TileMap<GPW>& m, const PrefillArgs& a, const Entries& en,
                                         int64_t row_stride, int key0, int lk, int log2bs, int wave) {
   const int n = lk - key0;  // keys of the tile that exist (clamped below)
   const uint64_t len_mask = n >= 64 ? ~0ull : (n <= 0 ? 0ull : ((1ull << n) - 1));
@@ -604,30 +619,33 @@ __device__ __forceinline__ void resolve(TileMap& m, const PrefillArgs& a, const 
       blk_mask |= ((uint32_t)en.e[g] < (uint32_t)a.num_blocks ? 0xffull : 0ull) << (8 * g);
     m.valid = len_mask & blk_mask;
     m.blocks_ok = blk_mask == ~0ull;
-    const int e0 = wave == 0 ? en.e[0] : wave == 1 ? en.e[2] : wave == 2 ? en.e[4] : en.e[6];
-    const int e1 = wave == 0 ? en.e[1] : wave == 1 ? en.e[3] : wave == 2 ? en.e[5] : en.e[7];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int blk = x ? e1 : e0;
-      const int key = key0 + 8 * (2 * wave + x);
+    for (int x = 0; x < GPW; ++x) {
+      const int grp = wave * GPW + x;
+      int blk = en.e[0];
+#pragma unroll
+      for (int g = 1; g < 8; ++g) blk = grp == g ? en.e[g] : blk;
+      const int key = key0 + 8 * grp;
       const bool ok = (uint32_t)blk < (uint32_t)a.num_blocks;
       m.off[x] = ok ? (((int64_t)blk << log2bs) + (key & ((1 << log2bs) - 1))) * row_stride : 0;
     }
   } else {
     m.valid = len_mask;
     m.blocks_ok = true;
-    m.off[0] = m.off[1] = 0;  // packed rows are addressed per lane
+#pragma unroll
+    for (int x = 0; x < GPW; ++x) m.off[x] = 0;  // packed rows are addressed per lane
   }
 }
 
 // DMA of this wave's rows of one tile (K and V) into buffers (kbuf, vbuf).
 // Paged rows come from the tile map; packed rows are clamped to the last key
 // (lk >= 1 whenever a tile exists), so no address leaves the request.
-template <int D, bool PAGED>
-__device__ __forceinline__ void issue_tile(const TileMap& m, const uint8_t* kbase, const uint8_t* vbase,
+template <int D, int W, bool PAGED>
+__device__ __forceinline__ void issue_tile(const TileMap<Tile<D, W>::groups_per_wave>& m,
+                                           const uint8_t* kbase, const uint8_t* vbase,
                                            int64_t row_stride, int key0, int lk, uint8_t* kbuf,
                                            uint8_t* vbuf, int wave, int lane) {
-  using T = Tile<D>;
+  using T = Tile<D, W>;
   const int rr = lane / T::pieces;   // row within the instruction
   const int pos = lane % T::pieces;  // LDS piece position
 #pragma unroll
@@ -647,9 +665,9 @@ __device__ __forceinline__ void issue_tile(const TileMap& m, const uint8_t* kbas
 }
 
 // Zero this wave's V rows of keys that do not exist (after its DMA landed).
-template <int D>
+template <int D, int W>
 __device__ __forceinline__ void zero_rows(uint64_t valid, uint8_t* vbuf, int wave, int lane) {
-  using T = Tile<D>;
+  using T = Tile<D, W>;
   const int r0 = wave * T::rows_per_wave;
   const uint32_t bad = ~(uint32_t)(valid >> r0) & ((1u << T::rows_per_wave) - 1);
   if (bad == 0) return;
@@ -657,21 +675,27 @@ __device__ __forceinline__ void zero_rows(uint64_t valid, uint8_t* vbuf, int wav
 #pragma unroll
   for (int i = 0; i < T::rows_per_wave; i += per_pass) {
     const int r = i + lane / T::pieces;
-    if ((bad >> r) & 1u)
+    if (r < T::rows_per_wave && ((bad >> r) & 1u))
       *reinterpret_cast<uint4*>(vbuf + (r0 + r) * T::row_bytes + (lane % T::pieces) * 16) =
           make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
-template <int D, bool PAGED>
-__global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int q_tiles) {
-  using T = Tile<D>;
+// W waves x 32 query rows per workgroup; S LDS stages (the copy of tile t+S-1
+// is in flight while tile t is computed).
+template <int D, bool PAGED, int W, int S>
+__global__ __launch_bounds__(64 * W, 2) void prefill_dma_kernel(PrefillArgs a, int q_tiles) {
+  using T = Tile<D, W>;
+  constexpr int BM = 32 * W;
   constexpr int KS = D / 16;  // MFMA k-steps over head_dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  // two tile buffers as separate objects, so the compiler can tell the DMA
-  // into one from the reads of the other and waits only for the right one
-  __shared__ __attribute__((aligned(1024))) uint8_t k_a[T::bytes], v_a[T::bytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t k_b[T::bytes], v_b[T::bytes];
+  constexpr int GPW = T::groups_per_wave;
+  static_assert(S == 2 || S == 3, "stages");
+  // the tile buffers are separate objects, so the compiler can tell the DMA
+  // into one from the reads of another and waits only for the right one
+  __shared__ __attribute__((aligned(1024))) uint8_t k0b[T::bytes], v0b[T::bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k1b[T::bytes], v1b[T::bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k2b[S == 3 ? T::bytes : 16], v2b[S == 3 ? T::bytes : 16];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -686,7 +710,7 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
   if (lq > a.max_seqlen_q) lq = a.max_seqlen_q;
   if (q_start < 0 || q_start >= a.total_q) lq = 0;
   else if (lq > a.total_q - q_start) lq = a.total_q - q_start;
-  const int q0 = qt * kBM;
+  const int q0 = qt * BM;
   if (q0 >= lq) return;
   const int k_start = a.cu_seqlens_k[b];
   int lk = a.cu_seqlens_k[b + 1] - k_start;
@@ -698,7 +722,7 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
     else if (lk > a.total_k - k_start) lk = a.total_k - k_start;
   }
   const int offset = lk - lq;  // bottom-right causal alignment
-  const int last_row = min(q0 + kBM, lq) - 1;
+  const int last_row = min(q0 + BM, lq) - 1;
   int key_end = a.causal ? min(lk, last_row + offset + 1) : lk;
   if (key_end < 0) key_end = 0;
   const int n_tiles = (key_end + kBN - 1) / kBN;
@@ -712,6 +736,7 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
   // this wave's query column: row q0 + 32 * wave + col
   const int qrow = q0 + wave * 32 + col;
   const bool qvalid = qrow < lq;
+  const bool wave_rows = q0 + wave * 32 < lq;  // the wave has a row to compute
   // The row max is taken over unscaled scores, which needs scale > 0: a
   // negative scale is applied as |scale| to -q (bf16 negation is exact), and
   // a zero scale as 1e-30 (every logit then rounds to exactly 0 in the
@@ -764,6 +789,12 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
   // One tile: scores, softmax, output update, reading buffers (kb_lds, vb_lds).
   auto compute = [&](const uint8_t* kb_lds, const uint8_t* vb_lds, int key0, uint64_t valid,
                      bool blocks_ok) __attribute__((always_inline)) {
+    // Key kt of the tile is visible to this lane's row iff kt < lim (sequence
+    // end, causal diagonal) and its 8-key group's block is valid.
+    const int lim = min(a.causal ? qrow + offset - key0 + 1 : kBN, lk - key0);
+    const int lim_first = min(a.causal ? q0 + wave * 32 + offset - key0 + 1 : kBN, lk - key0);
+    const int lim_last = min(a.causal ? q0 + wave * 32 + 32 + offset - key0 : kBN, lk - key0);
+    if (!wave_rows || lim_last <= 0) return;  // nothing of this tile reaches the wave's rows
     // S^T for two 32-key blocks, interleaved, next fragments read ahead
     f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
     {
@@ -782,12 +813,8 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
         k1 = n1;
       }
     }
-    // mask, row max.  Key kt of the tile is visible to this lane's row iff
-    // kt < lim (sequence end, causal diagonal) and its 8-key group's block is
-    // valid.  Register r of block kb holds key kb*32 + 8*(r/4) + 4*half + r%4.
-    const int lim = min(a.causal ? qrow + offset - key0 + 1 : kBN, lk - key0);
-    const int lim_wave = min(a.causal ? q0 + wave * 32 + offset - key0 + 1 : kBN, lk - key0);
-    if (lim_wave < kBN) {
+    // mask (register r of block kb holds key kb*32 + 8*(r/4) + 4*half + r%4)
+    if (lim_first < kBN) {
       const int lim_h = lim - 4 * half;  // kt - 4 * half is a constant per register
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -850,43 +877,67 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
       }
   };
 
-  // Tile t from buffer (kc, vc) while tile t + 1 is copied into (kn, vn).
-  // Every memory operation of a step is unconditional, so the compiler's wait
-  // counts stay exact; past the last tile the copy re-reads in-bounds rows
-  // into the idle buffer and is drained before the workgroup ends.
-  TileMap cur;
-  Entries ent_nxt;
+  // Tile maps and block-table entries run ahead of the copies: at step t,
+  // maps[i] is the map of tile t + i (i < S - 1, copies already issued) and
+  // ent holds the block-table entries of tile t + S - 1.
+  TileMap<GPW> maps[S - 1];
+  Entries ent;
+  // Every memory operation of a step is unconditional, so the compiler's
+  // wait counts stay exact; copies past the last tile re-read in-bounds rows
+  // into idle buffers and are drained before the workgroup ends.
+  auto next_copy = [&](uint8_t* kn, uint8_t* vn, int key0) __attribute__((always_inline)) {
+    TileMap<GPW> nw;
+    resolve<PAGED, GPW>(nw, a, ent, row_stride, key0 + (S - 1) * kBN, lk, log2bs, wave);
+    issue_tile<D, W, PAGED>(nw, kbase, vbase, row_stride, key0 + (S - 1) * kBN, lk, kn, vn, wave, lane);
+#pragma unroll
+    for (int i = 0; i + 2 < S; ++i) maps[i] = maps[i + 1];
+    maps[S - 2] = nw;
+  };
+  // S = 2: the copy of tile t + 1 goes out first, then tile t is waited for;
+  // a second barrier frees tile t's buffer for the copy of tile t + 2.
+  // S = 3: tile t is waited for, one barrier also frees the buffer of tile
+  // t - 1, which then takes the copy of tile t + 2.  The LDS reads of a tile
+  // all feed MFMAs, so they are complete when the tile's last MFMA issues and
+  // the closing barrier needs no wait of its own.
   auto step = [&](uint8_t* kc, uint8_t* vc, uint8_t* kn, uint8_t* vn, int t) __attribute__((always_inline)) {
     const int key0 = t * kBN;
-    const uint64_t valid = cur.valid;
-    const bool blocks_ok = cur.blocks_ok;
-    TileMap nxt;
-    resolve<PAGED>(nxt, a, ent_nxt, row_stride, key0 + kBN, lk, log2bs, wave);
-    fetch_entries<PAGED>(ent_nxt, a, table, key0 + 2 * kBN, log2bs);
-    issue_tile<D, PAGED>(nxt, kbase, vbase, row_stride, key0 + kBN, lk, kn, vn, wave, lane);
-    cur = nxt;
-    // tile t has landed once only the DMA of tile t + 1 remains in flight
-    __builtin_amdgcn_s_waitcnt(0x0f70 | kDma);
-    zero_rows<D>(valid, vc, wave, lane);
+    const uint64_t valid = maps[0].valid;
+    const bool blocks_ok = maps[0].blocks_ok;
+    if constexpr (S == 2) next_copy(kn, vn, key0);
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (S == 2 ? kDma : kDma));  // tile t has landed
+    zero_rows<D, W>(valid, vc, wave, lane);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
+    if constexpr (S == 3) next_copy(kn, vn, key0);
     compute(kc, vc, key0, valid, blocks_ok);
-    // every wave is done reading (kc, vc) before tile t + 2 is copied into it
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
+    fetch_entries<PAGED>(ent, a, table, key0 + S * kBN, log2bs);
+    if constexpr (S == 2) __builtin_amdgcn_s_barrier();
   };
   if (n_tiles > 0) {
-    Entries ent0;
-    fetch_entries<PAGED>(ent0, a, table, 0, log2bs);
-    fetch_entries<PAGED>(ent_nxt, a, table, kBN, log2bs);
-    resolve<PAGED>(cur, a, ent0, row_stride, 0, lk, log2bs, wave);
-    issue_tile<D, PAGED>(cur, kbase, vbase, row_stride, 0, lk, k_a, v_a, wave, lane);
-    for (int t = 0; t < n_tiles; t += 2) {
-      step(k_a, v_a, k_b, v_b, t);
-      if (t + 1 >= n_tiles) break;
-      step(k_b, v_b, k_a, v_a, t + 1);
+#pragma unroll
+    for (int i = 0; i + 1 < S; ++i) {
+      Entries e0;
+      fetch_entries<PAGED>(e0, a, table, i * kBN, log2bs);
+      resolve<PAGED, GPW>(maps[i], a, e0, row_stride, i * kBN, lk, log2bs, wave);
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // the copy past the last tile lands before LDS is released
+    fetch_entries<PAGED>(ent, a, table, (S - 1) * kBN, log2bs);
+    issue_tile<D, W, PAGED>(maps[0], kbase, vbase, row_stride, 0, lk, k0b, v0b, wave, lane);
+    if constexpr (S == 3)
+      issue_tile<D, W, PAGED>(maps[1], kbase, vbase, row_stride, kBN, lk, k1b, v1b, wave, lane);
+    for (int t = 0; t < n_tiles; t += S) {
+      if constexpr (S == 2) {
+        step(k0b, v0b, k1b, v1b, t);
+        if (t + 1 >= n_tiles) break;
+        step(k1b, v1b, k0b, v0b, t + 1);
+      } else {
+        step(k0b, v0b, k2b, v2b, t);
+        if (t + 1 >= n_tiles) break;
+        step(k1b, v1b, k0b, v0b, t + 1);
+        if (t + 2 >= n_tiles) break;
+        step(k2b, v2b, k1b, v1b, t + 2);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // copies past the last tile land before LDS is released
   }
 
   // normalise and store: lane holds O^T rows 8*(r/4) + 4*half + r%4 of each 32-row block
@@ -905,17 +956,25 @@ __global__ __launch_bounds__(256, 2) void prefill_dma_kernel(PrefillArgs a, int 
     }
 }
 
-template <int D>
-hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
-  const int q_tiles = (a.max_seqlen_q + kBM - 1) / kBM;
+// The launch shape is fixed at compile time (PKV_PREFILL_WAVES, PKV_PREFILL_STAGES).
+template <int D, int W, int S>
+hipError_t launch_ws(const PrefillArgs& a, hipStream_t stream) {
+  const int q_tiles = (a.max_seqlen_q + 32 * W - 1) / (32 * W);
   const int64_t grid = work_grid(q_tiles, a.batch, a.num_heads, a.num_kv_heads);
   if (grid > 0x7fffffff / 2) return hipErrorInvalidValue;
   if (a.block_table != nullptr) {
-    hipLaunchKernelGGL((prefill_dma_kernel<D, true>), dim3((unsigned)grid), dim3(256), 0, stream, a, q_tiles);
+    hipLaunchKernelGGL((prefill_dma_kernel<D, true, W, S>), dim3((unsigned)grid), dim3(64 * W), 0, stream, a,
+                       q_tiles);
   } else {
-    hipLaunchKernelGGL((prefill_dma_kernel<D, false>), dim3((unsigned)grid), dim3(256), 0, stream, a, q_tiles);
+    hipLaunchKernelGGL((prefill_dma_kernel<D, false, W, S>), dim3((unsigned)grid), dim3(64 * W), 0, stream,
+                       a, q_tiles);
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
+  return launch_ws<D, PKV_PREFILL_WAVES, PKV_PREFILL_STAGES>(a, stream);
 }
 
 }  // namespace dma
