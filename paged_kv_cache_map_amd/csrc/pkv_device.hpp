@@ -116,4 +116,17 @@ __device__ __forceinline__ float sum_across_quads(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes
+// 0..31 of its second.  Given x twice, the two results hold, in every lane l,
+// x[l] and x[l ^ 32] in some order: enough for a symmetric combine.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace pkv

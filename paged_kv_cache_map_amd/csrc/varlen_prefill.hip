@@ -836,7 +836,7 @@ __global__ __launch_bounds__(64 * W, 2) void prefill_dma_kernel(PrefillArgs a, i
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, shfl_xor(mx, 32)) * scale;
+    mx = max_halves(mx) * scale;
     // lazy running max: move it (and rescale) only when it grows by > 2^8
     if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleBits) != 0) {
       const float mn = fmaxf(m, mx);
@@ -941,7 +941,7 @@ __global__ __launch_bounds__(64 * W, 2) void prefill_dma_kernel(PrefillArgs a, i
   }
 
   // normalise and store: lane holds O^T rows 8*(r/4) + 4*half + r%4 of each 32-row block
-  l += shfl_xor(l, 32);
+  l = sum_halves(l);
   if (!qvalid) return;
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q_start + qrow) * a.num_heads + h) * D;
