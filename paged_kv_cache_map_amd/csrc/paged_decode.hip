@@ -972,6 +972,453 @@ int persistent_grid(K kernel) {
   return (int)(wgs < 1 ? 1 : wgs);
 }
 
+// ---------------------------------------------------------------------------
+// Stream-K decode on the matrix cores (bf16 cache).
+//
+// The G q heads that share a KV head form a [G x D] by [D x keys] product, so
+// a wave computes each 32-key chunk as S^T = K Q^T and O^T += V^T P^T on
+// v_mfma_f32_16x16x32_bf16 with the G heads as the 16 columns (q rows of
+// absent heads are zero when G < 16).  The vector ALUs only run the softmax
+// (8 exponentials per lane and chunk instead of 2 G), so the wave's time goes
+// to waiting for HBM, as it should in a memory-bound kernel.
+// * K reaches the A operand straight from HBM: lane l loads 16 bytes of key
+//   l mod 16 at head_dim 32 ks + 8 (l / 16) (a 64-byte run per key).
+// * V rows are copied to the wave's LDS region (row-major, 16-byte pieces
+//   permuted by vswz) and read back with ds_read_b64_tr_b16, which hands each
+//   lane four consecutive keys of one head_dim element: the A operand of V^T.
+//   P^T comes straight from the lane's own S^T registers once the product's
+//   key order is permuted to match (the same permutation on both operands
+//   leaves the sum unchanged).
+// * the stream-K schedule, partial triples and merge kernel are those of the
+//   vector kernel; units are whole KV heads (no head groups).
+// ---------------------------------------------------------------------------
+namespace mfd {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+template <int D>
+struct Geo {
+  static constexpr int row_bytes = D * 2;             // bf16 row of one KV head
+  static constexpr int KS = D / 32;                   // QK k-steps
+  static constexpr int DB = D / 16;                   // 16-element blocks of head_dim
+  static constexpr int pieces = row_bytes / 16;       // 16-byte pieces per row
+  static constexpr int vkeys = 64 / pieces;           // V rows per load instruction
+  static constexpr int vloads = kChunk / vkeys;       // V load instructions per chunk
+  static constexpr int vbytes = kChunk * row_bytes;   // one chunk of V in LDS
+
+};
+
+// LDS piece permutation of V row r: keeps both the row writes and the
+// transposed reads (16 consecutive rows x 2 pieces) free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? ((r & 7) << 1) : ((r & 3) << 1);
+}
+
+__device__ __forceinline__ uint2 read_tr(const uint8_t* p) {
+  const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p);
+  return __builtin_bit_cast(uint2, x);
+}
+
+__device__ __forceinline__ float max_quarters(float x) {  // over lanes l, l^16, l^32, l^48
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_halves(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
+__device__ __forceinline__ float sum_quarters(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return sum_halves(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+template <int D>
+struct Chunk {
+  uint4 k[2][Geo<D>::KS];   // [16-key block][k-step]: this lane's 8 K elements
+  uint32_t kmask;           // bit k: key k of the chunk exists and sits in a valid block
+  int64_t off[4];           // byte offsets of the chunk's four 8-key groups (uniform)
+};
+
+template <int D>
+struct VRegs {
+  uint4 v[Geo<D>::vloads];  // V: piece lane % pieces of row vkeys * i + lane / pieces
+};
+
+// Per-lane byte offsets: K operand row lane % 16 (within 16 rows, or & 7
+// within 8) with the lane's 16 bytes of each k-step; V copy row lane / pieces.
+struct Offs {
+  uint32_t k16, k8, v;
+};
+
+// Loads of chunk p's K in the A-operand layout.  Each 8-key group of the
+// chunk lies in one block (block_size >= 8; with block_size >= 16 each
+// 16-key half does) and is addressed through a buffer descriptor; keys past
+// the end or in invalid blocks read row 0 of block 0 and are masked.
+template <int D, bool SMALL>
+__device__ __forceinline__ void load_k(Chunk<D>& r, const StreamCtx& c, const Pos& p, int tbl,
+                                       const Offs& o, int lane) {
+  using G = Geo<D>;
+  const int lk = seq_len(c, p.b);
+  const int start = p.ch * kChunk;
+  const uint8_t* kbase = c.k_cache + p.gg * c.row_bytes;
+  uint32_t mask = 0;
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    const int key = start + 8 * grp;
+    const int id = __builtin_amdgcn_readlane(tbl, grp);
+    const bool ok = key < lk && id >= 0 && id < c.num_blocks;
+    r.off[grp] = ok ? (int64_t)id * c.block_bytes + (int64_t)(key & (c.bs - 1)) * c.slot_stride : 0;
+    const int n = min(max(lk - key, 0), 8);
+    mask |= (ok ? ((1u << n) - 1u) : 0u) << (8 * grp);
+  }
+  if constexpr (!SMALL) {
+    // a 16-key half lies in one block: its second group follows its first
+    r.off[1] = r.off[0] + 8 * (int64_t)c.slot_stride;
+    r.off[3] = r.off[2] + 8 * (int64_t)c.slot_stride;
+  }
+  r.kmask = mask;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    if constexpr (!SMALL) {
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(kbase + r.off[2 * kb]), 0, 16 * c.slot_stride, kBufferWord3);
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks) {
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o.k16, ks * 64, 0);
+        r.k[kb][ks] = make_uint4(x.x, x.y, x.z, x.w);
+      }
+    } else {
+      // keys 0..7 and 8..15 of the half sit in two blocks: every lane reads
+      // both (lanes that share an address merge) and keeps its own
+      const bool hi8 = (lane & 15) >= 8;
+      const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(kbase + r.off[2 * kb]), 0, 8 * c.slot_stride, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(kbase + r.off[2 * kb + 1]), 0, 8 * c.slot_stride, kBufferWord3);
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks) {
+        const u32x4_t xa = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)o.k8, ks * 64, 0);
+        const u32x4_t xb = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)o.k8, ks * 64, 0);
+        const u32x4_t x = hi8 ? xb : xa;
+        r.k[kb][ks] = make_uint4(x.x, x.y, x.z, x.w);
+      }
+    }
+  }
+}
+
+// Loads of the V rows of the chunk whose K load_k issued (same offsets).
+template <int D>
+__device__ __forceinline__ void load_v(VRegs<D>& vr, const Chunk<D>& r, const StreamCtx& c, int gg,
+                                       const Offs& o) {
+  using G = Geo<D>;
+  const uint8_t* vbase = c.v_cache + gg * c.row_bytes;
+#pragma unroll
+  for (int i = 0; i < G::vloads; ++i) {
+    const int row0 = G::vkeys * i;  // first key of the instruction (within one 8-key group)
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + r.off[row0 >> 3]), 0, 8 * c.slot_stride, kBufferWord3);
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)o.v, (row0 & 7) * c.slot_stride, 0);
+    vr.v[i] = make_uint4(x.x, x.y, x.z, x.w);
+  }
+}
+
+// V rows of the chunk (registers) -> this wave's LDS region.
+// Rows of keys that do not exist are stored as zeros: their p is 0, but the
+// cache may hold anything there (NaN included) and 0 * NaN would leak.
+template <int D>
+__device__ __forceinline__ void store_v(const VRegs<D>& vr, uint32_t kmask, uint8_t* v_w, int lane) {
+  using G = Geo<D>;
+  const bool full = kmask == 0xffffffffu;
+#pragma unroll
+  for (int i = 0; i < G::vloads; ++i) {
+    const int row = G::vkeys * i + lane / G::pieces;
+    const int pos = (lane % G::pieces) ^ vswz<D>(row);
+    const bool ok = full || ((kmask >> row) & 1u);
+    *reinterpret_cast<uint4*>(v_w + row * G::row_bytes + pos * 16) = ok ? vr.v[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+template <int D>
+struct MState {
+  f32x4_t o[Geo<D>::DB];  // O^T: rows 16 db + 4 (lane / 16) + i, column (head) lane % 16
+  float m;                // running max of this lane's head (log2 domain)
+  float l;                // this lane's share of the running sum
+};
+
+constexpr float kRescaleBits = 8.0f;  // lazy running max (log2 domain)
+
+// One chunk: S^T = K Q^T, softmax, O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void compute_chunk(MState<D>& st, const Chunk<D>& kr, const uint4 (&qf)[Geo<D>::KS],
+                                              const uint8_t* v_w, const uint32_t (&v_off)[Geo<D>::DB],
+                                              float logit_scale, int lane) {
+  using G = Geo<D>;
+  f32x4_t s[2] = {f32x4_t{}, f32x4_t{}};
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr.k[kb][ks]), as_bf16x8(qf[ks]), s[kb], 0, 0, 0);
+  // register i of block kb holds key 16 kb + 4 (lane / 16) + i
+  const int g4 = 4 * (lane >> 4);
+  if (kr.kmask != 0xffffffffu) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s[kb][i] = ((kr.kmask >> (16 * kb + g4 + i)) & 1u) ? s[kb][i] : -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  mx = max_quarters(mx) * logit_scale;
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + kRescaleBits) != 0) {
+    const float mn = fmaxf(st.m, mx);
+    const float alpha = fast_exp2(st.m - mn);
+    st.m = mn;
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) st.o[db] *= alpha;
+  }
+  // P^T operand: k-slots 8 (lane / 16) + j hold keys 4 (lane / 16) + j (j < 4)
+  // and 16 + 4 (lane / 16) + j - 4 (j >= 4): the lane's own scores
+  f32x8_t pv;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pv[i] = fast_exp2(fmaf(s[0][i], logit_scale, -st.m));
+    pv[4 + i] = fast_exp2(fmaf(s[1][i], logit_scale, -st.m));
+  }
+  const uint4 pb = __builtin_bit_cast(uint4, __builtin_convertvector(pv, bf16x8_t));
+  float ps = dot2_bf16(pb.x, 0x3f803f80u, 0.0f);
+  ps = dot2_bf16(pb.y, 0x3f803f80u, ps);
+  ps = dot2_bf16(pb.z, 0x3f803f80u, ps);
+  ps = dot2_bf16(pb.w, 0x3f803f80u, ps);
+  st.l += ps;
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db) {
+    const uint2 lo = read_tr(v_w + v_off[db]);
+    const uint2 hi = read_tr(v_w + v_off[db] + 16 * Geo<D>::row_bytes);
+    st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)),
+                                                      as_bf16x8(pb), st.o[db], 0, 0, 0);
+  }
+}
+
+// q rows of unit p's G heads into the wave's LDS region, then this lane's B
+// operand (head lane % 16, 8 elements per k-step; zero for absent heads).
+template <int D, int G>
+__device__ __forceinline__ void load_q(uint4 (&qf)[Geo<D>::KS], uint8_t* q_w, const DecodeArgs& a,
+                                       const Pos& p, uint32_t q_sign, int lane) {
+  using Ge = Geo<D>;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)p.b * a.num_heads + p.gg * G) * Ge::row_bytes;
+  for (int i = lane; i < G * Ge::row_bytes / 16; i += 64)
+    reinterpret_cast<uint4*>(q_w)[i] = reinterpret_cast<const uint4*>(src)[i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int ks = 0; ks < Ge::KS; ++ks) {
+    const int hc = (lane & 15) < G ? (lane & 15) : 0;
+    const uint4 x = *reinterpret_cast<const uint4*>(q_w + hc * Ge::row_bytes + ks * 64 + (lane >> 4) * 16);
+    qf[ks] = (lane & 15) < G ? make_uint4(x.x ^ q_sign, x.y ^ q_sign, x.z ^ q_sign, x.w ^ q_sign)
+                             : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// End of a wave's segment of a unit: the final rows if the wave processed the
+// whole unit, else a partial triple in slot (wave + unit).  Lanes l, l^16,
+// l^32, l^48 hold head l % 16's 4 x DB output rows and shares of its sum.
+template <int D, int G>
+__device__ __forceinline__ void flush(MState<D>& st, const DecodeArgs& a, const Pos& p, bool whole, int slot,
+                                      int lane) {
+  using Ge = Geo<D>;
+  const int hc = lane & 15, g4 = 4 * (lane >> 4);
+  const float l = sum_quarters(st.l);
+  if (hc < G) {
+    if (whole) {
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)p.b * a.num_heads + p.gg * G + hc) * D;
+#pragma unroll
+      for (int db = 0; db < Ge::DB; ++db) {
+        const uint32_t w0 = pack_bf16x2(st.o[db][0] * inv, st.o[db][1] * inv);
+        const uint32_t w1 = pack_bf16x2(st.o[db][2] * inv, st.o[db][3] * inv);
+        *reinterpret_cast<uint2*>(out + 16 * db + g4) = make_uint2(w0, w1);
+      }
+    } else {
+      float* ws_o = a.workspace + ((int64_t)slot * G + hc) * D;
+      float* ws_ml = a.workspace + (int64_t)a.stream_slots * G * D + ((int64_t)slot * G + hc) * 2;
+#pragma unroll
+      for (int db = 0; db < Ge::DB; ++db)
+        *reinterpret_cast<float4*>(ws_o + 16 * db + g4) = make_float4(st.o[db][0], st.o[db][1], st.o[db][2], st.o[db][3]);
+      if (g4 == 0) {
+        ws_ml[0] = st.m;
+        ws_ml[1] = l;
+      }
+    }
+  }
+  st.m = kNegBig;
+  st.l = 0.0f;
+#pragma unroll
+  for (int db = 0; db < Ge::DB; ++db) st.o[db] = f32x4_t{};
+}
+
+template <int D, int G, bool SMALL>
+__global__ __launch_bounds__(kStreamThreads, 2) void decode_mfma_kernel(DecodeArgs a) {
+  using Ge = Geo<D>;
+  __shared__ int32_t pre[kStreamMaxBatch + 1];
+  __shared__ int32_t part[kStreamThreads];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kWaves][G * Ge::row_bytes];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kWaves][Ge::vbytes];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int ug = a.num_kv_heads;  // units per sequence: one per KV head
+  build_prefix(pre, part, a, ug);
+  if (blockIdx.x == 0) {  // the merge kernel reads the prefix instead of rebuilding it
+    int32_t* pre_g = stream_prefix(a, G, D);
+    for (int i = threadIdx.x; i <= a.batch; i += kStreamThreads) pre_g[i] = pre[i];
+  }
+  const int64_t T = pre[a.batch];
+  const int W = gridDim.x * kWaves;
+  const int w = blockIdx.x * kWaves + wave;
+  const int c0 = (int)(T * w / W), c1 = (int)(T * (w + 1) / W);
+  if (c0 >= c1) return;
+
+  StreamCtx c;
+  c.k_cache = a.k_cache;
+  c.v_cache = a.v_cache;
+  c.block_table = a.block_table;
+  c.seqlens = a.cache_seqlens;
+  c.row_bytes = Ge::row_bytes;
+  c.slot_stride = a.num_kv_heads * Ge::row_bytes;
+  c.block_bytes = (int64_t)a.block_size * c.slot_stride;
+  c.max_blocks = a.max_blocks_per_seq;
+  c.num_blocks = a.num_blocks;
+  c.log2bs = __builtin_ctz(a.block_size);
+  c.bs = a.block_size;
+  c.cap = a.max_blocks_per_seq * a.block_size;
+  c.heads_per_kv = G;
+  c.head_groups = 1;
+  Offs o;
+  o.k16 = (uint32_t)((lane & 15) * c.slot_stride + (lane >> 4) * 16);
+  o.k8 = (uint32_t)((lane & 7) * c.slot_stride + (lane >> 4) * 16);
+  o.v = (uint32_t)((lane / Ge::pieces) * c.slot_stride + (lane % Ge::pieces) * 16);
+  // The chunk max is taken over unscaled scores, which needs a scale > 0: a
+  // negative scale is applied as |scale| to -q (bf16 negation is exact), a
+  // zero scale as 1e-30 (every logit then rounds to 0 in the exponent, while
+  // masked keys stay at -inf instead of -inf * 0).
+  const uint32_t q_sign = a.softmax_scale < 0.0f ? 0x80008000u : 0u;
+  const float logit_scale = fmaxf(fabsf(a.softmax_scale) * kLog2e, 1e-30f);
+
+  uint8_t* q_w = q_lds[wave];
+  uint8_t* v_w = v_lds[wave];
+  // transposed-read offsets: group lane / 16 reads keys 4 (lane / 16) + 16 x + (lane % 16) / 4,
+  // elements 16 db + 4 (lane % 4) .. + 3 (vswz does not depend on the 16 x)
+  uint32_t v_off[Ge::DB];
+  {
+    const int r = lane & 15, g = lane >> 4;
+    const int key = 4 * g + r / 4;
+#pragma unroll
+    for (int db = 0; db < Ge::DB; ++db) {
+      const int dd = 16 * db + 4 * (r & 3);
+      v_off[db] = key * Ge::row_bytes + (((dd >> 3) ^ vswz<D>(key)) << 4) + (dd & 7) * 2;
+    }
+  }
+  MState<D> st;
+  st.m = kNegBig;
+  st.l = 0.0f;
+#pragma unroll
+  for (int db = 0; db < Ge::DB; ++db) st.o[db] = f32x4_t{};
+
+  // cur: chunk being computed; nxt: chunk whose loads are in flight
+  Pos cur = locate(pre, a.batch, ug, c0);
+  Pos nxt = c0 + 1 < c1 ? advance(pre, ug, cur) : cur;
+  int tbl_nxt = fetch_table(c, nxt, lane);
+  uint4 qf[Ge::KS];
+  load_q<D, G>(qf, q_w, a, cur, q_sign, lane);
+  int x = c0;
+  Chunk<D> A, B;
+  VRegs<D> vr;
+  load_k<D, SMALL>(A, c, cur, fetch_table(c, cur, lane), o, lane);
+  load_v<D>(vr, A, c, cur.gg, o);
+  // One step: K of `nxt` into S; once `cur` (in R, vr) has landed its V goes
+  // to LDS and the V loads of `nxt` reuse vr; then `cur` is computed.
+  auto step = [&](Chunk<D>& R, Chunk<D>& S) -> bool {
+    const Pos nn = x + 2 < c1 ? advance(pre, ug, nxt) : nxt;
+    const int tbl_nn = fetch_table(c, nn, lane);
+    load_k<D, SMALL>(S, c, nxt, tbl_nxt, o, lane);
+    store_v<D>(vr, R.kmask, v_w, lane);
+    load_v<D>(vr, S, c, nxt.gg, o);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    compute_chunk<D>(st, R, qf, v_w, v_off, logit_scale, lane);
+    const bool last = x + 1 == c1;
+    if (last || cur.ch + 1 == cur.nch) {
+      const int u = cur.b * ug + cur.gg;
+      const int64_t ustart = pre[cur.b] + (int64_t)cur.gg * cur.nch;
+      const bool whole = ustart >= c0 && ustart + cur.nch <= c1;
+      flush<D, G>(st, a, cur, whole, w + u, lane);
+    }
+    if (last) return false;
+    if (nxt.b != cur.b || nxt.gg != cur.gg) load_q<D, G>(qf, q_w, a, nxt, q_sign, lane);
+    cur = nxt;
+    nxt = nn;
+    tbl_nxt = tbl_nn;
+    ++x;
+    // the next step overwrites this chunk's V in LDS: its reads are done
+    // (they fed this chunk's MFMAs)
+    return true;
+  };
+  for (;;) {
+    if (!step(A, B)) break;
+    if (!step(B, A)) break;
+  }
+}
+
+template <int D, int G>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+  static int cached_grid = 0;  // per instantiation; the CU count of one process's GPUs is fixed
+  const bool small = a.block_size < 16;
+  if (cached_grid == 0)
+    cached_grid = small ? persistent_grid(decode_mfma_kernel<D, G, true>)
+                        : persistent_grid(decode_mfma_kernel<D, G, false>);
+  const int64_t max_chunks = (int64_t)a.batch * a.num_kv_heads *
+                             (((int64_t)a.max_blocks_per_seq * a.block_size + kChunk - 1) / kChunk);
+  int64_t grid = cached_grid;
+  if (grid * kWaves > max_chunks) grid = (max_chunks + kWaves - 1) / kWaves;
+  if (grid < 1) grid = 1;
+  if (small) {
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G, true>), dim3((unsigned)grid), dim3(kStreamThreads), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G, false>), dim3((unsigned)grid), dim3(kStreamThreads), 0,
+                       stream, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)a.batch * a.num_heads;
+  hipLaunchKernelGGL((stream_merge_kernel<kBF16, D, G>), dim3((unsigned)((rows + kWaves - 1) / kWaves)),
+                     dim3(kStreamThreads), 0, stream, a, 1, (int)(grid * kWaves));
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.num_heads / a.num_kv_heads) {
+    case 1: return launch_g<D, 1>(a, stream);
+    case 2: return launch_g<D, 2>(a, stream);
+    case 4: return launch_g<D, 4>(a, stream);
+    case 8: return launch_g<D, 8>(a, stream);
+    case 16: return launch_g<D, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mfd
+
 template <int CT, int D, int GW, bool SMALL>
 hipError_t launch_stream_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
   constexpr int QT = (CT == kF32) ? kF32 : kBF16;
@@ -1039,6 +1486,11 @@ hipError_t launch_c(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream
 }  // namespace
 
 hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
+  if (p.stream && p.mfma) {
+    if (a.head_dim == 64) return mfd::launch<64>(a, stream);
+    if (a.head_dim == 128) return mfd::launch<128>(a, stream);
+    return hipErrorInvalidValue;
+  }
   if (a.cache_dtype == kF32) return launch_c<kF32>(a, p, stream);
   if (a.cache_dtype == kBF16) return launch_c<kBF16>(a, p, stream);
   if (a.cache_dtype == kFP8) return launch_c<kFP8>(a, p, stream);

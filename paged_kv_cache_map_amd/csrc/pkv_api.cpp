@@ -159,12 +159,17 @@ int pkv_kv_cache_write(const void* k, int64_t k_token_stride, const void* v, int
 size_t pkv_paged_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t block_size,
                                        int32_t max_blocks_per_seq, int32_t split_keys) {
-  pkv::DecodePlan p;
-  const char* why = nullptr;
-  if (!pkv::plan_decode(batch, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                        split_keys, &p, &why))
-    return 0;
-  return p.workspace_bytes;
+  // the size does not depend on the dtypes: the larger of the two plans
+  size_t bytes = 0;
+  for (int mfma = 0; mfma < 2; ++mfma) {
+    pkv::DecodePlan p;
+    const char* why = nullptr;
+    if (!pkv::plan_decode(batch, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                          split_keys, mfma != 0, &p, &why))
+      return 0;
+    if (p.workspace_bytes > bytes) bytes = p.workspace_bytes;
+  }
+  return bytes;
 }
 
 int pkv_paged_decode(void* out, const void* q, int q_dtype, const void* k_cache, const void* v_cache,
@@ -202,7 +207,7 @@ int pkv_paged_decode(void* out, const void* q, int q_dtype, const void* k_cache,
   pkv::DecodePlan plan;
   const char* why = nullptr;
   if (!pkv::plan_decode(batch, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                        split_keys, &plan, &why))
+                        split_keys, cache_dtype == PKV_BF16, &plan, &why))
     return fail(PKV_ERR_INVALID, "paged_decode: %s", why);
   if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes > 0 && !workspace))
     return fail(PKV_ERR_INVALID, "paged_decode: workspace of %zu bytes needed, %zu given",

@@ -32,6 +32,7 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
 // sequence form work unit s.
 struct DecodePlan {
   bool stream;          // stream-K kernel (automatic plan) instead of fixed splits
+  bool mfma;            // stream-K on the matrix cores (bf16 cache): one unit per KV head
   int32_t split_keys;   // fixed splits: multiple of kDecodeKeysPerWg
   int32_t num_splits;   // fixed splits: units per sequence at the longest possible length
   int32_t head_groups;  // q-head groups of at most 8 per KV head
@@ -49,8 +50,10 @@ constexpr int kStreamMaxWaves = 4096;                         // bounds the stre
 
 // Fills `plan`; returns false (with a message in *why) for arguments the
 // planner cannot serve.  Pure host arithmetic, no HIP calls.
+// mfma: the cache is bf16, so the automatic plan may use the matrix-core
+// kernel (whole KV heads as units).
 bool plan_decode(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                 int32_t block_size, int32_t max_blocks_per_seq, int32_t split_keys,
+                 int32_t block_size, int32_t max_blocks_per_seq, int32_t split_keys, bool mfma,
                  DecodePlan* plan, const char** why);
 
 struct DecodeArgs {

@@ -15,7 +15,7 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 }  // namespace
 
 bool plan_decode(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                 int32_t block_size, int32_t max_blocks_per_seq, int32_t split_keys,
+                 int32_t block_size, int32_t max_blocks_per_seq, int32_t split_keys, bool mfma,
                  DecodePlan* plan, const char** why) {
   if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
       block_size <= 0) {
@@ -27,10 +27,13 @@ bool plan_decode(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
     return false;
   }
   const int32_t group = num_heads / num_kv_heads;
-  // q heads of one KV head are served in groups of at most 4: a wave's live
-  // state for 4 heads fits two waves per SIMD; larger groups read their KV
-  // head once per group (the repeats hit the caches)
-  const int32_t head_groups = group > 4 ? group / 4 : 1;
+  // The matrix-core stream kernel serves all q heads of a KV head in one
+  // unit.  The vector kernels serve them in groups of at most 4: a wave's
+  // live state for 4 heads fits two waves per SIMD; larger groups read their
+  // KV head once per group (the repeats hit the caches).
+  const bool use_mfma = mfma && split_keys == 0;
+  const int32_t valu_groups = group > 4 ? group / 4 : 1;
+  int32_t head_groups = use_mfma ? 1 : valu_groups;
   const int64_t max_keys = (int64_t)max_blocks_per_seq * block_size;
   plan->head_groups = head_groups;
   // Automatic plan: stream-K, when the batch fits its chunk-count table and
@@ -40,6 +43,7 @@ bool plan_decode(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
   if (split_keys == 0 && batch <= kStreamMaxBatch && max_chunks < (int64_t)1 << 31) {
     const int64_t per_unit_heads = group / head_groups;
     plan->stream = true;
+    plan->mfma = use_mfma;
     plan->split_keys = 0;
     plan->num_splits = 0;
     plan->stream_slots = kStreamMaxWaves + units;
@@ -50,7 +54,9 @@ bool plan_decode(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
     return true;
   }
   plan->stream = false;
+  plan->mfma = false;
   plan->stream_slots = 0;
+  head_groups = valu_groups;  // the fixed-split kernel runs on the vector ALUs
   int64_t sk;
   if (split_keys == 0) {
     const int64_t units = (int64_t)batch * num_kv_heads * head_groups;

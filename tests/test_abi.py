@@ -142,7 +142,11 @@ def test_decode_workspace_plan():
     assert pkv.paged_decode_workspace_size(3, 8, 2, 64, 32, 4, 128) == 0
     # explicit split of 128 keys over 64 blocks of 16 -> 8 splits of (D + 2) floats per (b, h)
     assert pkv.paged_decode_workspace_size(3, 8, 2, 128, 16, 64, 128) == 3 * 8 * 8 * 130 * 4
-    # G = 16 splits into four head groups of 4 per KV head
-    assert pkv.paged_decode_workspace_size(2, 32, 2, 128, 16, 8) == (4096 + 2 * 2 * 4) * 4 * 130 * 4 + 3 * 4
+    # G = 16: the size covers both automatic plans; the matrix-core plan (bf16
+    # caches: one unit of 16 heads per KV head) needs more than the vector one
+    # (four head groups of 4 per KV head)
+    mfma = (4096 + 2 * 2) * 16 * 130 * 4 + 3 * 4
+    valu = (4096 + 2 * 2 * 4) * 4 * 130 * 4 + 3 * 4
+    assert pkv.paged_decode_workspace_size(2, 32, 2, 128, 16, 8) == max(mfma, valu)
     # unsupported argument -> 0
     assert pkv.paged_decode_workspace_size(3, 8, 3, 128, 16, 4) == 0
