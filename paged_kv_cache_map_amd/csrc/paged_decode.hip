@@ -37,6 +37,10 @@
 #include "pkv_device.hpp"
 #include "pkv_internal.h"
 
+#ifndef PKV_DECODE_DEPTH
+#define PKV_DECODE_DEPTH 3
+#endif
+
 namespace pkv {
 namespace {
 
@@ -1036,22 +1040,23 @@ __device__ __forceinline__ float sum_quarters(float x) {
   return sum_halves(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
+// One chunk in flight: its K (A-operand layout), V (row pieces) and q (the
+// B operand of its unit; loaded with every chunk so that a change of unit
+// never waits) registers, and where its keys live.
 template <int D>
 struct Chunk {
   uint4 k[2][Geo<D>::KS];   // [16-key block][k-step]: this lane's 8 K elements
+  uint4 v[Geo<D>::vloads];  // V: piece lane % pieces of row vkeys * i + lane / pieces
+  uint4 q[Geo<D>::KS];      // q of head lane % 16 (zero for absent heads), 8 elements per k-step
   uint32_t kmask;           // bit k: key k of the chunk exists and sits in a valid block
   int64_t off[4];           // byte offsets of the chunk's four 8-key groups (uniform)
 };
 
-template <int D>
-struct VRegs {
-  uint4 v[Geo<D>::vloads];  // V: piece lane % pieces of row vkeys * i + lane / pieces
-};
-
 // Per-lane byte offsets: K operand row lane % 16 (within 16 rows, or & 7
-// within 8) with the lane's 16 bytes of each k-step; V copy row lane / pieces.
+// within 8) with the lane's 16 bytes of each k-step; V copy row lane / pieces;
+// q row lane % 16 (past the unit's rows for absent heads, which read 0).
 struct Offs {
-  uint32_t k16, k8, v;
+  uint32_t k16, k8, v, q;
 };
 
 // Loads of chunk p's K in the A-operand layout.  Each 8-key group of the
@@ -1112,7 +1117,7 @@ __device__ __forceinline__ void load_k(Chunk<D>& r, const StreamCtx& c, const Po
 
 // Loads of the V rows of the chunk whose K load_k issued (same offsets).
 template <int D>
-__device__ __forceinline__ void load_v(VRegs<D>& vr, const Chunk<D>& r, const StreamCtx& c, int gg,
+__device__ __forceinline__ void load_v(Chunk<D>& vr, const Chunk<D>& r, const StreamCtx& c, int gg,
                                        const Offs& o) {
   using G = Geo<D>;
   const uint8_t* vbase = c.v_cache + gg * c.row_bytes;
@@ -1127,10 +1132,23 @@ __device__ __forceinline__ void load_v(VRegs<D>& vr, const Chunk<D>& r, const St
 }
 
 // V rows of the chunk (registers) -> this wave's LDS region.
+// q rows of chunk p's unit (G heads) as the B operand.
+template <int D, int G>
+__device__ __forceinline__ void load_qf(Chunk<D>& r, const DecodeArgs& a, const Pos& p, const Offs& o) {
+  using Ge = Geo<D>;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)p.b * a.num_heads + p.gg * G) * Ge::row_bytes;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, G * Ge::row_bytes, kBufferWord3);
+#pragma unroll
+  for (int ks = 0; ks < Ge::KS; ++ks) {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)o.q, ks * 64, 0);
+    r.q[ks] = make_uint4(x.x, x.y, x.z, x.w);
+  }
+}
+
 // Rows of keys that do not exist are stored as zeros: their p is 0, but the
 // cache may hold anything there (NaN included) and 0 * NaN would leak.
 template <int D>
-__device__ __forceinline__ void store_v(const VRegs<D>& vr, uint32_t kmask, uint8_t* v_w, int lane) {
+__device__ __forceinline__ void store_v(const Chunk<D>& vr, uint32_t kmask, uint8_t* v_w, int lane) {
   using G = Geo<D>;
   const bool full = kmask == 0xffffffffu;
 #pragma unroll
@@ -1150,27 +1168,35 @@ struct MState {
 };
 
 constexpr float kRescaleBits = 8.0f;  // lazy running max (log2 domain)
+constexpr int kMfmaDepth = PKV_DECODE_DEPTH;  // chunks in flight per wave
 
-// One chunk: S^T = K Q^T, softmax, O^T += V^T P^T.
+// S^T = K Q^T for the chunk in r: register i of block kb holds the score of
+// key 16 kb + 4 (lane / 16) + i for head lane % 16.
 template <int D>
-__device__ __forceinline__ void compute_chunk(MState<D>& st, const Chunk<D>& kr, const uint4 (&qf)[Geo<D>::KS],
-                                              const uint8_t* v_w, const uint32_t (&v_off)[Geo<D>::DB],
-                                              float logit_scale, int lane) {
+__device__ __forceinline__ void chunk_scores(f32x4_t (&s)[2], const Chunk<D>& r, uint32_t q_sign) {
   using G = Geo<D>;
-  f32x4_t s[2] = {f32x4_t{}, f32x4_t{}};
+  s[0] = f32x4_t{};
+  s[1] = f32x4_t{};
 #pragma unroll
-  for (int ks = 0; ks < G::KS; ++ks)
+  for (int ks = 0; ks < G::KS; ++ks) {
+    const uint4 q = make_uint4(r.q[ks].x ^ q_sign, r.q[ks].y ^ q_sign, r.q[ks].z ^ q_sign, r.q[ks].w ^ q_sign);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr.k[kb][ks]), as_bf16x8(qf[ks]), s[kb], 0, 0, 0);
-  // register i of block kb holds key 16 kb + 4 (lane / 16) + i
+      s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[kb][ks]), as_bf16x8(q), s[kb], 0, 0, 0);
+  }
+}
+
+// Softmax update and O^T += V^T P^T for one chunk's scores (V in LDS).
+template <int D>
+__device__ __forceinline__ void chunk_update(MState<D>& st, f32x4_t (&s)[2], uint32_t kmask, const uint8_t* v_w,
+                                             const uint32_t (&v_off)[Geo<D>::DB], float logit_scale, int lane) {
+  using G = Geo<D>;
   const int g4 = 4 * (lane >> 4);
-  if (kr.kmask != 0xffffffffu) {
+  if (kmask != 0xffffffffu) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s[kb][i] = ((kr.kmask >> (16 * kb + g4 + i)) & 1u) ? s[kb][i] : -INFINITY;
+      for (int i = 0; i < 4; ++i) s[kb][i] = ((kmask >> (16 * kb + g4 + i)) & 1u) ? s[kb][i] : -INFINITY;
   }
   float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                    fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
@@ -1200,30 +1226,9 @@ __device__ __forceinline__ void compute_chunk(MState<D>& st, const Chunk<D>& kr,
 #pragma unroll
   for (int db = 0; db < G::DB; ++db) {
     const uint2 lo = read_tr(v_w + v_off[db]);
-    const uint2 hi = read_tr(v_w + v_off[db] + 16 * Geo<D>::row_bytes);
+    const uint2 hi = read_tr(v_w + v_off[db] + 16 * G::row_bytes);
     st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)),
                                                       as_bf16x8(pb), st.o[db], 0, 0, 0);
-  }
-}
-
-// q rows of unit p's G heads into the wave's LDS region, then this lane's B
-// operand (head lane % 16, 8 elements per k-step; zero for absent heads).
-template <int D, int G>
-__device__ __forceinline__ void load_q(uint4 (&qf)[Geo<D>::KS], uint8_t* q_w, const DecodeArgs& a,
-                                       const Pos& p, uint32_t q_sign, int lane) {
-  using Ge = Geo<D>;
-  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)p.b * a.num_heads + p.gg * G) * Ge::row_bytes;
-  for (int i = lane; i < G * Ge::row_bytes / 16; i += 64)
-    reinterpret_cast<uint4*>(q_w)[i] = reinterpret_cast<const uint4*>(src)[i];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-  for (int ks = 0; ks < Ge::KS; ++ks) {
-    const int hc = (lane & 15) < G ? (lane & 15) : 0;
-    const uint4 x = *reinterpret_cast<const uint4*>(q_w + hc * Ge::row_bytes + ks * 64 + (lane >> 4) * 16);
-    qf[ks] = (lane & 15) < G ? make_uint4(x.x ^ q_sign, x.y ^ q_sign, x.z ^ q_sign, x.w ^ q_sign)
-                             : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
@@ -1264,12 +1269,14 @@ __device__ __forceinline__ void flush(MState<D>& st, const DecodeArgs& a, const 
   for (int db = 0; db < Ge::DB; ++db) st.o[db] = f32x4_t{};
 }
 
-template <int D, int G, bool SMALL>
-__global__ __launch_bounds__(kStreamThreads, 2) void decode_mfma_kernel(DecodeArgs a) {
+// N chunks in flight per wave; with N = 4 a wave holds 4 x 16 KiB of K, V and
+// q in registers, so one wave per SIMD (512 registers) keeps as many bytes in
+// flight per CU as two waves with two chunks each would, without spilling.
+template <int D, int G, bool SMALL, int N>
+__global__ __launch_bounds__(kStreamThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
   using Ge = Geo<D>;
   __shared__ int32_t pre[kStreamMaxBatch + 1];
   __shared__ int32_t part[kStreamThreads];
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kWaves][G * Ge::row_bytes];
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[kWaves][Ge::vbytes];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1305,6 +1312,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_mfma_kernel(DecodeAr
   o.k16 = (uint32_t)((lane & 15) * c.slot_stride + (lane >> 4) * 16);
   o.k8 = (uint32_t)((lane & 7) * c.slot_stride + (lane >> 4) * 16);
   o.v = (uint32_t)((lane / Ge::pieces) * c.slot_stride + (lane % Ge::pieces) * 16);
+  o.q = (lane & 15) < G ? (uint32_t)((lane & 15) * Ge::row_bytes + (lane >> 4) * 16) : 0x7ffffff0u;
   // The chunk max is taken over unscaled scores, which needs a scale > 0: a
   // negative scale is applied as |scale| to -q (bf16 negation is exact), a
   // zero scale as 1e-30 (every logit then rounds to 0 in the exponent, while
@@ -1312,7 +1320,6 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_mfma_kernel(DecodeAr
   const uint32_t q_sign = a.softmax_scale < 0.0f ? 0x80008000u : 0u;
   const float logit_scale = fmaxf(fabsf(a.softmax_scale) * kLog2e, 1e-30f);
 
-  uint8_t* q_w = q_lds[wave];
   uint8_t* v_w = v_lds[wave];
   // transposed-read offsets: group lane / 16 reads keys 4 (lane / 16) + 16 x + (lane % 16) / 4,
   // elements 16 db + 4 (lane % 4) .. + 3 (vswz does not depend on the 16 x)
@@ -1332,29 +1339,41 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_mfma_kernel(DecodeAr
 #pragma unroll
   for (int db = 0; db < Ge::DB; ++db) st.o[db] = f32x4_t{};
 
-  // cur: chunk being computed; nxt: chunk whose loads are in flight
+  // N chunks in flight: at the step of chunk x the ring slot R holds x and
+  // the other slots x + 1 .. x + N - 1 (loading); as soon as x's K has fed
+  // its MFMAs and its V has gone to LDS, R is refilled with x + N.  Positions
+  // past the wave's last chunk repeat it (loaded, never used), so every step
+  // issues the same loads.
+  auto clamp_next = [&](const Pos& p, int xp) __attribute__((always_inline)) {
+    return xp + 1 < c1 ? advance(pre, ug, p) : p;
+  };
+  auto issue = [&](Chunk<D>& r, const Pos& p, int tbl) __attribute__((always_inline)) {
+    load_k<D, SMALL>(r, c, p, tbl, o, lane);
+    load_v<D>(r, r, c, p.gg, o);
+    load_qf<D, G>(r, a, p, o);
+  };
+  Chunk<D> ring[N];
   Pos cur = locate(pre, a.batch, ug, c0);
-  Pos nxt = c0 + 1 < c1 ? advance(pre, ug, cur) : cur;
-  int tbl_nxt = fetch_table(c, nxt, lane);
-  uint4 qf[Ge::KS];
-  load_q<D, G>(qf, q_w, a, cur, q_sign, lane);
+  Pos ip = cur;  // next chunk to load: c0 + N after the prologue
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    issue(ring[j], ip, fetch_table(c, ip, lane));
+    ip = clamp_next(ip, c0 + j);
+  }
+  int tbl_ip = fetch_table(c, ip, lane);
   int x = c0;
-  Chunk<D> A, B;
-  VRegs<D> vr;
-  load_k<D, SMALL>(A, c, cur, fetch_table(c, cur, lane), o, lane);
-  load_v<D>(vr, A, c, cur.gg, o);
-  // One step: K of `nxt` into S; once `cur` (in R, vr) has landed its V goes
-  // to LDS and the V loads of `nxt` reuse vr; then `cur` is computed.
-  auto step = [&](Chunk<D>& R, Chunk<D>& S) -> bool {
-    const Pos nn = x + 2 < c1 ? advance(pre, ug, nxt) : nxt;
-    const int tbl_nn = fetch_table(c, nn, lane);
-    load_k<D, SMALL>(S, c, nxt, tbl_nxt, o, lane);
-    store_v<D>(vr, R.kmask, v_w, lane);
-    load_v<D>(vr, S, c, nxt.gg, o);
+  auto step = [&](Chunk<D>& R) __attribute__((always_inline)) -> bool {
+    const Pos ipn = clamp_next(ip, x + N);
+    const int tbl_ipn = fetch_table(c, ipn, lane);
+    store_v<D>(R, R.kmask, v_w, lane);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    compute_chunk<D>(st, R, qf, v_w, v_off, logit_scale, lane);
+    f32x4_t s[2];
+    chunk_scores<D>(s, R, q_sign);
+    const uint32_t kmask = R.kmask;
+    issue(R, ip, tbl_ip);
+    chunk_update<D>(st, s, kmask, v_w, v_off, logit_scale, lane);
     const bool last = x + 1 == c1;
     if (last || cur.ch + 1 == cur.nch) {
       const int u = cur.b * ug + cur.gg;
@@ -1363,19 +1382,25 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_mfma_kernel(DecodeAr
       flush<D, G>(st, a, cur, whole, w + u, lane);
     }
     if (last) return false;
-    if (nxt.b != cur.b || nxt.gg != cur.gg) load_q<D, G>(qf, q_w, a, nxt, q_sign, lane);
-    cur = nxt;
-    nxt = nn;
-    tbl_nxt = tbl_nn;
+    cur = advance(pre, ug, cur);
+    ip = ipn;
+    tbl_ip = tbl_ipn;
     ++x;
     // the next step overwrites this chunk's V in LDS: its reads are done
     // (they fed this chunk's MFMAs)
     return true;
   };
   for (;;) {
-    if (!step(A, B)) break;
-    if (!step(B, A)) break;
+    if (!step(ring[0])) break;
+    if (!step(ring[1])) break;
+    if constexpr (N > 2) {
+      if (!step(ring[2])) break;
+    }
+    if constexpr (N > 3) {
+      if (!step(ring[3])) break;
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // loads past the last chunk land before the wave ends
 }
 
 template <int D, int G>
@@ -1383,19 +1408,19 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   static int cached_grid = 0;  // per instantiation; the CU count of one process's GPUs is fixed
   const bool small = a.block_size < 16;
   if (cached_grid == 0)
-    cached_grid = small ? persistent_grid(decode_mfma_kernel<D, G, true>)
-                        : persistent_grid(decode_mfma_kernel<D, G, false>);
+    cached_grid = small ? persistent_grid(decode_mfma_kernel<D, G, true, kMfmaDepth>)
+                        : persistent_grid(decode_mfma_kernel<D, G, false, kMfmaDepth>);
   const int64_t max_chunks = (int64_t)a.batch * a.num_kv_heads *
                              (((int64_t)a.max_blocks_per_seq * a.block_size + kChunk - 1) / kChunk);
   int64_t grid = cached_grid;
   if (grid * kWaves > max_chunks) grid = (max_chunks + kWaves - 1) / kWaves;
   if (grid < 1) grid = 1;
   if (small) {
-    hipLaunchKernelGGL((decode_mfma_kernel<D, G, true>), dim3((unsigned)grid), dim3(kStreamThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G, true, kMfmaDepth>), dim3((unsigned)grid), dim3(kStreamThreads),
+                       0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<D, G, false>), dim3((unsigned)grid), dim3(kStreamThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G, false, kMfmaDepth>), dim3((unsigned)grid), dim3(kStreamThreads),
+                       0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
