@@ -40,6 +40,9 @@
 #ifndef PKV_DECODE_DEPTH
 #define PKV_DECODE_DEPTH 3
 #endif
+#ifndef PKV_DECODE_DEPTH_FP8
+#define PKV_DECODE_DEPTH_FP8 5
+#endif
 
 namespace pkv {
 namespace {
@@ -1006,16 +1009,24 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
 
-template <int D>
+// Geometry for cache type CT (bf16 or fp8) and head_dim D.  V always sits in
+// LDS as bf16 rows; fp8 K and V are dequantised on the way (exactly).
+template <int CT, int D>
 struct Geo {
-  static constexpr int row_bytes = D * 2;             // bf16 row of one KV head
+  static constexpr int elt = Elt<CT>::bytes;
+  static constexpr int row_bytes = D * elt;           // cache row of one KV head
+  static constexpr int lds_row = D * 2;               // bf16 V row in LDS
   static constexpr int KS = D / 32;                   // QK k-steps
+  static constexpr int KL = CT == kFP8 ? KS / 2 : KS;  // K loads per 16-key block
   static constexpr int DB = D / 16;                   // 16-element blocks of head_dim
-  static constexpr int pieces = row_bytes / 16;       // 16-byte pieces per row
-  static constexpr int vkeys = 64 / pieces;           // V rows per load instruction
+  static constexpr int pieces = row_bytes / 16;       // 16-byte pieces per cache row
+  // V rows per load instruction: at most 8, so that an instruction stays in
+  // one 8-key group (with fp8 and D = 64 half of the lanes then idle)
+  static constexpr int vkeys = 64 / pieces < 8 ? 64 / pieces : 8;
+  static constexpr int vlanes = vkeys * pieces;       // lanes that move V
   static constexpr int vloads = kChunk / vkeys;       // V load instructions per chunk
-  static constexpr int vbytes = kChunk * row_bytes;   // one chunk of V in LDS
-
+  static constexpr int vbytes = kChunk * lds_row;     // one chunk of V in LDS
+  static constexpr int qrow = D * 2;                  // bf16 q row
 };
 
 // LDS piece permutation of V row r: keeps both the row writes and the
@@ -1040,20 +1051,37 @@ __device__ __forceinline__ float sum_quarters(float x) {
   return sum_halves(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
+// Sixteen E4M3 codes -> sixteen bf16 (exact), as two 8-element operands.
+__device__ __forceinline__ void e4m3x16_to_bf16(const uint4& x, uint4& lo, uint4& hi) {
+  lo = make_uint4(e4m3x2_to_bf16x2<false>(x.x), e4m3x2_to_bf16x2<true>(x.x), e4m3x2_to_bf16x2<false>(x.y),
+                  e4m3x2_to_bf16x2<true>(x.y));
+  hi = make_uint4(e4m3x2_to_bf16x2<false>(x.z), e4m3x2_to_bf16x2<true>(x.z), e4m3x2_to_bf16x2<false>(x.w),
+                  e4m3x2_to_bf16x2<true>(x.w));
+}
+
 // One chunk in flight: its K (A-operand layout), V (row pieces) and q (the
 // B operand of its unit; loaded with every chunk so that a change of unit
-// never waits) registers, and where its keys live.
-template <int D>
+// never waits) registers, where its keys live, and its unit's scales.
+//
+// Which head_dim elements sit in k-slot j of k-step ks for lane group
+// g = lane / 16 is a free choice as long as K and q agree:
+//   bf16: element 32 ks + 8 g + j (one 16-byte K load per k-step);
+//   fp8:  element 64 (ks / 2) + 16 g + 8 (ks % 2) + j (one 16-byte load of
+//         sixteen codes feeds two k-steps).
+template <int CT, int D>
 struct Chunk {
-  uint4 k[2][Geo<D>::KS];   // [16-key block][k-step]: this lane's 8 K elements
-  uint4 v[Geo<D>::vloads];  // V: piece lane % pieces of row vkeys * i + lane / pieces
-  uint4 q[Geo<D>::KS];      // q of head lane % 16 (zero for absent heads), 8 elements per k-step
-  uint32_t kmask;           // bit k: key k of the chunk exists and sits in a valid block
-  int64_t off[4];           // byte offsets of the chunk's four 8-key groups (uniform)
+  uint4 k[2][Geo<CT, D>::KL];   // [16-key block][load]: this lane's K bytes
+  uint4 v[Geo<CT, D>::vloads];  // V: piece lane % pieces of row vkeys * i + lane / pieces
+  uint4 q[Geo<CT, D>::KS];      // q of head lane % 16 (zero for absent heads), 8 elements per k-step
+  uint32_t kmask;               // bit k: key k of the chunk exists and sits in a valid block
+  int64_t off[4];               // byte offsets of the chunk's four 8-key groups (uniform)
+  float ls;                     // |softmax scale x K scale| x log2 e of the chunk's unit
+  float vs;                     // V scale of the chunk's unit
+  uint32_t qs;                  // sign flip applied to q (negative scale)
 };
 
 // Per-lane byte offsets: K operand row lane % 16 (within 16 rows, or & 7
-// within 8) with the lane's 16 bytes of each k-step; V copy row lane / pieces;
+// within 8) with the lane's 16 bytes of each load; V copy row lane / pieces;
 // q row lane % 16 (past the unit's rows for absent heads, which read 0).
 struct Offs {
   uint32_t k16, k8, v, q;
@@ -1063,10 +1091,10 @@ struct Offs {
 // chunk lies in one block (block_size >= 8; with block_size >= 16 each
 // 16-key half does) and is addressed through a buffer descriptor; keys past
 // the end or in invalid blocks read row 0 of block 0 and are masked.
-template <int D, bool SMALL>
-__device__ __forceinline__ void load_k(Chunk<D>& r, const StreamCtx& c, const Pos& p, int tbl,
+template <int CT, int D, bool SMALL>
+__device__ __forceinline__ void load_k(Chunk<CT, D>& r, const StreamCtx& c, const Pos& p, int tbl,
                                        const Offs& o, int lane) {
-  using G = Geo<D>;
+  using G = Geo<CT, D>;
   const int lk = seq_len(c, p.b);
   const int start = p.ch * kChunk;
   const uint8_t* kbase = c.k_cache + p.gg * c.row_bytes;
@@ -1092,9 +1120,9 @@ __device__ __forceinline__ void load_k(Chunk<D>& r, const StreamCtx& c, const Po
       const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(kbase + r.off[2 * kb]), 0, 16 * c.slot_stride, kBufferWord3);
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) {
-        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o.k16, ks * 64, 0);
-        r.k[kb][ks] = make_uint4(x.x, x.y, x.z, x.w);
+      for (int j = 0; j < G::KL; ++j) {
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o.k16, j * 64, 0);
+        r.k[kb][j] = make_uint4(x.x, x.y, x.z, x.w);
       }
     } else {
       // keys 0..7 and 8..15 of the half sit in two blocks: every lane reads
@@ -1105,21 +1133,20 @@ __device__ __forceinline__ void load_k(Chunk<D>& r, const StreamCtx& c, const Po
       const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(kbase + r.off[2 * kb + 1]), 0, 8 * c.slot_stride, kBufferWord3);
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) {
-        const u32x4_t xa = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)o.k8, ks * 64, 0);
-        const u32x4_t xb = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)o.k8, ks * 64, 0);
+      for (int j = 0; j < G::KL; ++j) {
+        const u32x4_t xa = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)o.k8, j * 64, 0);
+        const u32x4_t xb = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)o.k8, j * 64, 0);
         const u32x4_t x = hi8 ? xb : xa;
-        r.k[kb][ks] = make_uint4(x.x, x.y, x.z, x.w);
+        r.k[kb][j] = make_uint4(x.x, x.y, x.z, x.w);
       }
     }
   }
 }
 
 // Loads of the V rows of the chunk whose K load_k issued (same offsets).
-template <int D>
-__device__ __forceinline__ void load_v(Chunk<D>& vr, const Chunk<D>& r, const StreamCtx& c, int gg,
-                                       const Offs& o) {
-  using G = Geo<D>;
+template <int CT, int D>
+__device__ __forceinline__ void load_v(Chunk<CT, D>& r, const StreamCtx& c, int gg, const Offs& o) {
+  using G = Geo<CT, D>;
   const uint8_t* vbase = c.v_cache + gg * c.row_bytes;
 #pragma unroll
   for (int i = 0; i < G::vloads; ++i) {
@@ -1127,70 +1154,102 @@ __device__ __forceinline__ void load_v(Chunk<D>& vr, const Chunk<D>& r, const St
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vbase + r.off[row0 >> 3]), 0, 8 * c.slot_stride, kBufferWord3);
     const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)o.v, (row0 & 7) * c.slot_stride, 0);
-    vr.v[i] = make_uint4(x.x, x.y, x.z, x.w);
+    r.v[i] = make_uint4(x.x, x.y, x.z, x.w);
   }
 }
 
-// V rows of the chunk (registers) -> this wave's LDS region.
-// q rows of chunk p's unit (G heads) as the B operand.
-template <int D, int G>
-__device__ __forceinline__ void load_qf(Chunk<D>& r, const DecodeArgs& a, const Pos& p, const Offs& o) {
-  using Ge = Geo<D>;
-  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)p.b * a.num_heads + p.gg * G) * Ge::row_bytes;
-  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, G * Ge::row_bytes, kBufferWord3);
+// q rows of chunk p's unit (G heads) as the B operand, and the unit's scales.
+template <int CT, int D, int G>
+__device__ __forceinline__ void load_qf(Chunk<CT, D>& r, const DecodeArgs& a, const Pos& p, const Offs& o) {
+  using Ge = Geo<CT, D>;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)p.b * a.num_heads + p.gg * G) * Ge::qrow;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, G * Ge::qrow, kBufferWord3);
 #pragma unroll
   for (int ks = 0; ks < Ge::KS; ++ks) {
-    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)o.q, ks * 64, 0);
+    const int imm = CT == kFP8 ? 128 * (ks / 2) + 16 * (ks % 2) : 64 * ks;
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)o.q, imm, 0);
     r.q[ks] = make_uint4(x.x, x.y, x.z, x.w);
   }
+  // The chunk max is taken over unscaled scores, which needs a scale > 0: a
+  // negative scale is applied as |scale| to -q (bf16 negation is exact), a
+  // zero scale as 1e-30 (every logit then rounds to 0 in the exponent, while
+  // masked keys stay at -inf instead of -inf * 0).
+  float sc = a.softmax_scale;
+  r.vs = 1.0f;
+  if constexpr (CT == kFP8) {
+    sc *= a.k_scale[p.gg];
+    r.vs = a.v_scale[p.gg];
+  }
+  r.qs = sc < 0.0f ? 0x80008000u : 0u;
+  r.ls = fmaxf(fabsf(sc) * kLog2e, 1e-30f);
 }
 
-// Rows of keys that do not exist are stored as zeros: their p is 0, but the
-// cache may hold anything there (NaN included) and 0 * NaN would leak.
-template <int D>
-__device__ __forceinline__ void store_v(const Chunk<D>& vr, uint32_t kmask, uint8_t* v_w, int lane) {
-  using G = Geo<D>;
-  const bool full = kmask == 0xffffffffu;
+// V rows of the chunk (registers) -> this wave's LDS region as bf16.  Rows of
+// keys that do not exist are stored as zeros: their p is 0, but the cache may
+// hold anything there (NaN included) and 0 * NaN would leak.
+template <int CT, int D>
+__device__ __forceinline__ void store_v(const Chunk<CT, D>& r, uint8_t* v_w, int lane) {
+  using G = Geo<CT, D>;
+  const bool full = r.kmask == 0xffffffffu;
+  if (G::vlanes < 64 && lane >= G::vlanes) return;
 #pragma unroll
   for (int i = 0; i < G::vloads; ++i) {
     const int row = G::vkeys * i + lane / G::pieces;
-    const int pos = (lane % G::pieces) ^ vswz<D>(row);
-    const bool ok = full || ((kmask >> row) & 1u);
-    *reinterpret_cast<uint4*>(v_w + row * G::row_bytes + pos * 16) = ok ? vr.v[i] : make_uint4(0u, 0u, 0u, 0u);
+    const bool ok = full || ((r.kmask >> row) & 1u);
+    const uint4 x = ok ? r.v[i] : make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (CT == kFP8) {
+      uint4 lo, hi;
+      e4m3x16_to_bf16(x, lo, hi);
+      const int p0 = 2 * (lane % G::pieces);  // bf16 pieces of the sixteen elements
+      *reinterpret_cast<uint4*>(v_w + row * G::lds_row + ((p0 ^ vswz<D>(row)) << 4)) = lo;
+      *reinterpret_cast<uint4*>(v_w + row * G::lds_row + (((p0 + 1) ^ vswz<D>(row)) << 4)) = hi;
+    } else {
+      const int pos = (lane % G::pieces) ^ vswz<D>(row);
+      *reinterpret_cast<uint4*>(v_w + row * G::lds_row + pos * 16) = x;
+    }
   }
 }
 
 template <int D>
 struct MState {
-  f32x4_t o[Geo<D>::DB];  // O^T: rows 16 db + 4 (lane / 16) + i, column (head) lane % 16
-  float m;                // running max of this lane's head (log2 domain)
-  float l;                // this lane's share of the running sum
+  f32x4_t o[D / 16];  // O^T: rows 16 db + 4 (lane / 16) + i, column (head) lane % 16
+  float m;            // running max of this lane's head (log2 domain)
+  float l;            // this lane's share of the running sum
 };
 
 constexpr float kRescaleBits = 8.0f;  // lazy running max (log2 domain)
-constexpr int kMfmaDepth = PKV_DECODE_DEPTH;  // chunks in flight per wave
 
 // S^T = K Q^T for the chunk in r: register i of block kb holds the score of
 // key 16 kb + 4 (lane / 16) + i for head lane % 16.
-template <int D>
-__device__ __forceinline__ void chunk_scores(f32x4_t (&s)[2], const Chunk<D>& r, uint32_t q_sign) {
-  using G = Geo<D>;
+template <int CT, int D>
+__device__ __forceinline__ void chunk_scores(f32x4_t (&s)[2], const Chunk<CT, D>& r) {
+  using G = Geo<CT, D>;
   s[0] = f32x4_t{};
   s[1] = f32x4_t{};
+  const uint32_t qs = r.qs;
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) {
-    const uint4 q = make_uint4(r.q[ks].x ^ q_sign, r.q[ks].y ^ q_sign, r.q[ks].z ^ q_sign, r.q[ks].w ^ q_sign);
+    const uint4 q = make_uint4(r.q[ks].x ^ qs, r.q[ks].y ^ qs, r.q[ks].z ^ qs, r.q[ks].w ^ qs);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[kb][ks]), as_bf16x8(q), s[kb], 0, 0, 0);
+    for (int kb = 0; kb < 2; ++kb) {
+      uint4 kf;
+      if constexpr (CT == kFP8) {
+        uint4 lo, hi;
+        e4m3x16_to_bf16(r.k[kb][ks / 2], lo, hi);
+        kf = (ks & 1) ? hi : lo;
+      } else {
+        kf = r.k[kb][ks];
+      }
+      s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(q), s[kb], 0, 0, 0);
+    }
   }
 }
 
 // Softmax update and O^T += V^T P^T for one chunk's scores (V in LDS).
 template <int D>
 __device__ __forceinline__ void chunk_update(MState<D>& st, f32x4_t (&s)[2], uint32_t kmask, const uint8_t* v_w,
-                                             const uint32_t (&v_off)[Geo<D>::DB], float logit_scale, int lane) {
-  using G = Geo<D>;
+                                             const uint32_t (&v_off)[D / 16], float logit_scale, int lane) {
+  constexpr int DB = D / 16;
   const int g4 = 4 * (lane >> 4);
   if (kmask != 0xffffffffu) {
 #pragma unroll
@@ -1207,7 +1266,7 @@ __device__ __forceinline__ void chunk_update(MState<D>& st, f32x4_t (&s)[2], uin
     st.m = mn;
     st.l *= alpha;
 #pragma unroll
-    for (int db = 0; db < G::DB; ++db) st.o[db] *= alpha;
+    for (int db = 0; db < DB; ++db) st.o[db] *= alpha;
   }
   // P^T operand: k-slots 8 (lane / 16) + j hold keys 4 (lane / 16) + j (j < 4)
   // and 16 + 4 (lane / 16) + j - 4 (j >= 4): the lane's own scores
@@ -1224,9 +1283,9 @@ __device__ __forceinline__ void chunk_update(MState<D>& st, f32x4_t (&s)[2], uin
   ps = dot2_bf16(pb.w, 0x3f803f80u, ps);
   st.l += ps;
 #pragma unroll
-  for (int db = 0; db < G::DB; ++db) {
+  for (int db = 0; db < DB; ++db) {
     const uint2 lo = read_tr(v_w + v_off[db]);
-    const uint2 hi = read_tr(v_w + v_off[db] + 16 * G::row_bytes);
+    const uint2 hi = read_tr(v_w + v_off[db] + 16 * D * 2);
     st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)),
                                                       as_bf16x8(pb), st.o[db], 0, 0, 0);
   }
@@ -1237,16 +1296,16 @@ __device__ __forceinline__ void chunk_update(MState<D>& st, f32x4_t (&s)[2], uin
 // l^32, l^48 hold head l % 16's 4 x DB output rows and shares of its sum.
 template <int D, int G>
 __device__ __forceinline__ void flush(MState<D>& st, const DecodeArgs& a, const Pos& p, bool whole, int slot,
-                                      int lane) {
-  using Ge = Geo<D>;
+                                      float out_scale, int lane) {
+  constexpr int DB = D / 16;
   const int hc = lane & 15, g4 = 4 * (lane >> 4);
   const float l = sum_quarters(st.l);
   if (hc < G) {
     if (whole) {
-      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      const float inv = l > 0.0f ? out_scale / l : 0.0f;
       uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)p.b * a.num_heads + p.gg * G + hc) * D;
 #pragma unroll
-      for (int db = 0; db < Ge::DB; ++db) {
+      for (int db = 0; db < DB; ++db) {
         const uint32_t w0 = pack_bf16x2(st.o[db][0] * inv, st.o[db][1] * inv);
         const uint32_t w1 = pack_bf16x2(st.o[db][2] * inv, st.o[db][3] * inv);
         *reinterpret_cast<uint2*>(out + 16 * db + g4) = make_uint2(w0, w1);
@@ -1255,8 +1314,10 @@ __device__ __forceinline__ void flush(MState<D>& st, const DecodeArgs& a, const 
       float* ws_o = a.workspace + ((int64_t)slot * G + hc) * D;
       float* ws_ml = a.workspace + (int64_t)a.stream_slots * G * D + ((int64_t)slot * G + hc) * 2;
 #pragma unroll
-      for (int db = 0; db < Ge::DB; ++db)
-        *reinterpret_cast<float4*>(ws_o + 16 * db + g4) = make_float4(st.o[db][0], st.o[db][1], st.o[db][2], st.o[db][3]);
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<float4*>(ws_o + 16 * db + g4) =
+            make_float4(st.o[db][0] * out_scale, st.o[db][1] * out_scale, st.o[db][2] * out_scale,
+                        st.o[db][3] * out_scale);
       if (g4 == 0) {
         ws_ml[0] = st.m;
         ws_ml[1] = l;
@@ -1266,15 +1327,15 @@ __device__ __forceinline__ void flush(MState<D>& st, const DecodeArgs& a, const 
   st.m = kNegBig;
   st.l = 0.0f;
 #pragma unroll
-  for (int db = 0; db < Ge::DB; ++db) st.o[db] = f32x4_t{};
+  for (int db = 0; db < DB; ++db) st.o[db] = f32x4_t{};
 }
 
-// N chunks in flight per wave; with N = 4 a wave holds 4 x 16 KiB of K, V and
-// q in registers, so one wave per SIMD (512 registers) keeps as many bytes in
-// flight per CU as two waves with two chunks each would, without spilling.
-template <int D, int G, bool SMALL, int N>
+// N chunks in flight per wave, held in registers at one wave per SIMD (up to
+// 512 registers): as many bytes in flight per CU as two waves with half the
+// depth, without spilling.
+template <int CT, int D, int G, bool SMALL, int N>
 __global__ __launch_bounds__(kStreamThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
-  using Ge = Geo<D>;
+  using Ge = Geo<CT, D>;
   __shared__ int32_t pre[kStreamMaxBatch + 1];
   __shared__ int32_t part[kStreamThreads];
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[kWaves][Ge::vbytes];
@@ -1311,14 +1372,9 @@ __global__ __launch_bounds__(kStreamThreads, 1) void decode_mfma_kernel(DecodeAr
   Offs o;
   o.k16 = (uint32_t)((lane & 15) * c.slot_stride + (lane >> 4) * 16);
   o.k8 = (uint32_t)((lane & 7) * c.slot_stride + (lane >> 4) * 16);
-  o.v = (uint32_t)((lane / Ge::pieces) * c.slot_stride + (lane % Ge::pieces) * 16);
-  o.q = (lane & 15) < G ? (uint32_t)((lane & 15) * Ge::row_bytes + (lane >> 4) * 16) : 0x7ffffff0u;
-  // The chunk max is taken over unscaled scores, which needs a scale > 0: a
-  // negative scale is applied as |scale| to -q (bf16 negation is exact), a
-  // zero scale as 1e-30 (every logit then rounds to 0 in the exponent, while
-  // masked keys stay at -inf instead of -inf * 0).
-  const uint32_t q_sign = a.softmax_scale < 0.0f ? 0x80008000u : 0u;
-  const float logit_scale = fmaxf(fabsf(a.softmax_scale) * kLog2e, 1e-30f);
+  o.v = lane < Ge::vlanes ? (uint32_t)((lane / Ge::pieces) * c.slot_stride + (lane % Ge::pieces) * 16)
+                         : 0x7ffffff0u;  // idle lanes read nothing
+  o.q = (lane & 15) < G ? (uint32_t)((lane & 15) * Ge::qrow + (lane >> 4) * (CT == kFP8 ? 32 : 16)) : 0x7ffffff0u;
 
   uint8_t* v_w = v_lds[wave];
   // transposed-read offsets: group lane / 16 reads keys 4 (lane / 16) + 16 x + (lane % 16) / 4,
@@ -1330,7 +1386,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void decode_mfma_kernel(DecodeAr
 #pragma unroll
     for (int db = 0; db < Ge::DB; ++db) {
       const int dd = 16 * db + 4 * (r & 3);
-      v_off[db] = key * Ge::row_bytes + (((dd >> 3) ^ vswz<D>(key)) << 4) + (dd & 7) * 2;
+      v_off[db] = key * Ge::lds_row + (((dd >> 3) ^ vswz<D>(key)) << 4) + (dd & 7) * 2;
     }
   }
   MState<D> st;
@@ -1347,12 +1403,12 @@ __global__ __launch_bounds__(kStreamThreads, 1) void decode_mfma_kernel(DecodeAr
   auto clamp_next = [&](const Pos& p, int xp) __attribute__((always_inline)) {
     return xp + 1 < c1 ? advance(pre, ug, p) : p;
   };
-  auto issue = [&](Chunk<D>& r, const Pos& p, int tbl) __attribute__((always_inline)) {
-    load_k<D, SMALL>(r, c, p, tbl, o, lane);
-    load_v<D>(r, r, c, p.gg, o);
-    load_qf<D, G>(r, a, p, o);
+  auto issue = [&](Chunk<CT, D>& r, const Pos& p, int tbl) __attribute__((always_inline)) {
+    load_k<CT, D, SMALL>(r, c, p, tbl, o, lane);
+    load_v<CT, D>(r, c, p.gg, o);
+    load_qf<CT, D, G>(r, a, p, o);
   };
-  Chunk<D> ring[N];
+  Chunk<CT, D> ring[N];
   Pos cur = locate(pre, a.batch, ug, c0);
   Pos ip = cur;  // next chunk to load: c0 + N after the prologue
 #pragma unroll
@@ -1362,24 +1418,25 @@ __global__ __launch_bounds__(kStreamThreads, 1) void decode_mfma_kernel(DecodeAr
   }
   int tbl_ip = fetch_table(c, ip, lane);
   int x = c0;
-  auto step = [&](Chunk<D>& R) __attribute__((always_inline)) -> bool {
+  auto step = [&](Chunk<CT, D>& R) __attribute__((always_inline)) -> bool {
     const Pos ipn = clamp_next(ip, x + N);
     const int tbl_ipn = fetch_table(c, ipn, lane);
-    store_v<D>(R, R.kmask, v_w, lane);
+    store_v<CT, D>(R, v_w, lane);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     f32x4_t s[2];
-    chunk_scores<D>(s, R, q_sign);
+    chunk_scores<CT, D>(s, R);
     const uint32_t kmask = R.kmask;
+    const float ls = R.ls, vs = R.vs;
     issue(R, ip, tbl_ip);
-    chunk_update<D>(st, s, kmask, v_w, v_off, logit_scale, lane);
+    chunk_update<D>(st, s, kmask, v_w, v_off, ls, lane);
     const bool last = x + 1 == c1;
     if (last || cur.ch + 1 == cur.nch) {
       const int u = cur.b * ug + cur.gg;
       const int64_t ustart = pre[cur.b] + (int64_t)cur.gg * cur.nch;
       const bool whole = ustart >= c0 && ustart + cur.nch <= c1;
-      flush<D, G>(st, a, cur, whole, w + u, lane);
+      flush<D, G>(st, a, cur, whole, w + u, vs, lane);
     }
     if (last) return false;
     cur = advance(pre, ug, cur);
@@ -1399,28 +1456,41 @@ __global__ __launch_bounds__(kStreamThreads, 1) void decode_mfma_kernel(DecodeAr
     if constexpr (N > 3) {
       if (!step(ring[3])) break;
     }
+    if constexpr (N > 4) {
+      if (!step(ring[4])) break;
+    }
+    if constexpr (N > 5) {
+      if (!step(ring[5])) break;
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // loads past the last chunk land before the wave ends
 }
 
-template <int D, int G>
+// Chunks in flight per wave: about 48 KiB of K and V either way.
+template <int CT>
+constexpr int depth() {
+  return CT == kFP8 ? PKV_DECODE_DEPTH_FP8 : PKV_DECODE_DEPTH;
+}
+
+template <int CT, int D, int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int N = depth<CT>();
   static int cached_grid = 0;  // per instantiation; the CU count of one process's GPUs is fixed
   const bool small = a.block_size < 16;
   if (cached_grid == 0)
-    cached_grid = small ? persistent_grid(decode_mfma_kernel<D, G, true, kMfmaDepth>)
-                        : persistent_grid(decode_mfma_kernel<D, G, false, kMfmaDepth>);
+    cached_grid = small ? persistent_grid(decode_mfma_kernel<CT, D, G, true, N>)
+                        : persistent_grid(decode_mfma_kernel<CT, D, G, false, N>);
   const int64_t max_chunks = (int64_t)a.batch * a.num_kv_heads *
                              (((int64_t)a.max_blocks_per_seq * a.block_size + kChunk - 1) / kChunk);
   int64_t grid = cached_grid;
   if (grid * kWaves > max_chunks) grid = (max_chunks + kWaves - 1) / kWaves;
   if (grid < 1) grid = 1;
   if (small) {
-    hipLaunchKernelGGL((decode_mfma_kernel<D, G, true, kMfmaDepth>), dim3((unsigned)grid), dim3(kStreamThreads),
-                       0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, G, true, N>), dim3((unsigned)grid), dim3(kStreamThreads), 0,
+                       stream, a);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<D, G, false, kMfmaDepth>), dim3((unsigned)grid), dim3(kStreamThreads),
-                       0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, G, false, N>), dim3((unsigned)grid), dim3(kStreamThreads), 0,
+                       stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1430,16 +1500,23 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
+template <int CT, int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   switch (a.num_heads / a.num_kv_heads) {
-    case 1: return launch_g<D, 1>(a, stream);
-    case 2: return launch_g<D, 2>(a, stream);
-    case 4: return launch_g<D, 4>(a, stream);
-    case 8: return launch_g<D, 8>(a, stream);
-    case 16: return launch_g<D, 16>(a, stream);
+    case 1: return launch_g<CT, D, 1>(a, stream);
+    case 2: return launch_g<CT, D, 2>(a, stream);
+    case 4: return launch_g<CT, D, 4>(a, stream);
+    case 8: return launch_g<CT, D, 8>(a, stream);
+    case 16: return launch_g<CT, D, 16>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int CT>
+hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
+  if (a.head_dim == 64) return launch_d<CT, 64>(a, stream);
+  if (a.head_dim == 128) return launch_d<CT, 128>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace mfd
@@ -1512,8 +1589,8 @@ hipError_t launch_c(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream
 
 hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
   if (p.stream && p.mfma) {
-    if (a.head_dim == 64) return mfd::launch<64>(a, stream);
-    if (a.head_dim == 128) return mfd::launch<128>(a, stream);
+    if (a.cache_dtype == kBF16) return mfd::launch<kBF16>(a, stream);
+    if (a.cache_dtype == kFP8) return mfd::launch<kFP8>(a, stream);
     return hipErrorInvalidValue;
   }
   if (a.cache_dtype == kF32) return launch_c<kF32>(a, p, stream);

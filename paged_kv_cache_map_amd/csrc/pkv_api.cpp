@@ -207,7 +207,7 @@ int pkv_paged_decode(void* out, const void* q, int q_dtype, const void* k_cache,
   pkv::DecodePlan plan;
   const char* why = nullptr;
   if (!pkv::plan_decode(batch, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                        split_keys, cache_dtype == PKV_BF16, &plan, &why))
+                        split_keys, cache_dtype != PKV_F32, &plan, &why))
     return fail(PKV_ERR_INVALID, "paged_decode: %s", why);
   if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes > 0 && !workspace))
     return fail(PKV_ERR_INVALID, "paged_decode: workspace of %zu bytes needed, %zu given",
