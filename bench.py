@@ -169,8 +169,10 @@ class Runner:
             pkv.varlen_prefill(self.pq, kc, vc, self.pcq, self.pck, p["max_seqlen_q"],
                                p["max_seqlen_k"], s.scale, True, self.pbt, self.k_scale,
                                self.v_scale, out=self.pout)
-        if ev is not None:
+        if ev is not None and self.has_prefill:
             ev[2].record()
+        elif ev is not None:
+            ev[2] = ev[1]
         if self.has_decode:
             pkv.paged_decode(self.dq, kc, vc, self.dbt, self.dlen, s.scale, self.k_scale,
                              self.v_scale, out=self.dout, split_keys=self.split_keys,
@@ -179,19 +181,25 @@ class Runner:
             ev[3].record()
 
     def time(self, steps, warmup):
+        """ms_per_step from K back-to-back steps with nothing else enqueued,
+        then per-kernel times from a second pass with HIP events around each
+        call (recorded on the library's stream)."""
         torch = self.torch
         for i in range(warmup):
             self.run(i)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         t0 = time.perf_counter()
         for i in range(steps):
-            self.run(warmup + i, evs[i])
+            self.run(warmup + i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for i in range(steps):
+            self.run(warmup + steps + i, evs[i])
+        torch.cuda.synchronize()
         write = [e[0].elapsed_time(e[1]) for e in evs]
-        pre = [e[1].elapsed_time(e[2]) for e in evs]
-        dec = [e[2].elapsed_time(e[3]) for e in evs]
+        pre = [e[1].elapsed_time(e[2]) for e in evs] if self.has_prefill else [0.0]
+        dec = [e[2].elapsed_time(e[3]) for e in evs] if self.has_decode else [0.0]
         return dict(ms_per_step=wall * 1e3 / steps,
                     write_ms=float(np.mean(write)), write_ms_min=float(np.min(write)),
                     prefill_ms=float(np.mean(pre)), prefill_ms_min=float(np.min(pre)),

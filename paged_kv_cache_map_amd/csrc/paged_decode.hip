@@ -38,10 +38,16 @@
 #include "pkv_internal.h"
 
 #ifndef PKV_DECODE_DEPTH
-#define PKV_DECODE_DEPTH 3
+#define PKV_DECODE_DEPTH 2
 #endif
 #ifndef PKV_DECODE_DEPTH_FP8
-#define PKV_DECODE_DEPTH_FP8 5
+#define PKV_DECODE_DEPTH_FP8 2
+#endif
+#ifndef PKV_DECODE_OCC
+#define PKV_DECODE_OCC 1
+#endif
+#ifndef PKV_DECODE_OCC_FP8
+#define PKV_DECODE_OCC_FP8 2
 #endif
 
 namespace pkv {
@@ -624,6 +630,7 @@ __device__ __forceinline__ int wave_of(int64_t x, int64_t T, int W) {
 struct Pos {
   int b, gg;    // sequence, unit (KV head group) within the sequence
   int ch, nch;  // chunk within the unit, chunks per unit of this sequence
+  int len;      // keys of the sequence (kept by the matrix-core kernel only)
 };
 
 __device__ __forceinline__ Pos locate(const int32_t* pre, int B, int ug, int x) {
@@ -1017,7 +1024,6 @@ struct Geo {
   static constexpr int row_bytes = D * elt;           // cache row of one KV head
   static constexpr int lds_row = D * 2;               // bf16 V row in LDS
   static constexpr int KS = D / 32;                   // QK k-steps
-  static constexpr int KL = CT == kFP8 ? KS / 2 : KS;  // K loads per 16-key block
   static constexpr int DB = D / 16;                   // 16-element blocks of head_dim
   static constexpr int pieces = row_bytes / 16;       // 16-byte pieces per cache row
   // V rows per load instruction: at most 8, so that an instruction stays in
@@ -1025,7 +1031,7 @@ struct Geo {
   static constexpr int vkeys = 64 / pieces < 8 ? 64 / pieces : 8;
   static constexpr int vlanes = vkeys * pieces;       // lanes that move V
   static constexpr int vloads = kChunk / vkeys;       // V load instructions per chunk
-  static constexpr int vbytes = kChunk * lds_row;     // one chunk of V in LDS
+  static constexpr int vbytes = kChunk * lds_row;     // one chunk of K or V in LDS
   static constexpr int qrow = D * 2;                  // bf16 q row
 };
 
@@ -1034,6 +1040,13 @@ struct Geo {
 template <int D>
 __device__ __forceinline__ int vswz(int r) {
   return D == 128 ? ((r & 7) << 1) : ((r & 3) << 1);
+}
+
+// LDS piece permutation of K row r: the A-operand reads (16 consecutive rows,
+// one piece) and the row writes are free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r & 15) : (r & 7);
 }
 
 __device__ __forceinline__ uint2 read_tr(const uint8_t* p) {
@@ -1059,20 +1072,40 @@ __device__ __forceinline__ void e4m3x16_to_bf16(const uint4& x, uint4& lo, uint4
                   e4m3x2_to_bf16x2<true>(x.w));
 }
 
-// One chunk in flight: its K (A-operand layout), V (row pieces) and q (the
-// B operand of its unit; loaded with every chunk so that a change of unit
-// never waits) registers, where its keys live, and its unit's scales.
-//
-// Which head_dim elements sit in k-slot j of k-step ks for lane group
-// g = lane / 16 is a free choice as long as K and q agree:
-//   bf16: element 32 ks + 8 g + j (one 16-byte K load per k-step);
-//   fp8:  element 64 (ks / 2) + 16 g + 8 (ks % 2) + j (one 16-byte load of
-//         sixteen codes feeds two k-steps).
+// Values every lane of a wave needs (lengths, block-table entries, scales)
+// are read with scalar loads through the constant address space: none of
+// them is written while a kernel runs.  Scalar loads wait on their own
+// counter (shared with LDS), so they never make a wave wait for the K and V
+// loads in flight, as a vector load would (vector loads complete in order).
+typedef const __attribute__((address_space(4))) int32_t* sptr_i32;
+typedef const __attribute__((address_space(4))) float* sptr_f32;
+
+__device__ __forceinline__ int seq_len_s(const StreamCtx& c, int b) {
+  const int lk = ((sptr_i32)c.seqlens)[b];
+  return lk < 0 ? 0 : (lk > c.cap ? c.cap : lk);
+}
+
+// Block ids of the four 8-key groups of a chunk.
+struct Tbl {
+  int32_t e[4];
+};
+
+__device__ __forceinline__ Tbl fetch_tbl(const StreamCtx& c, const Pos& p) {
+  const sptr_i32 row = (sptr_i32)c.block_table + (int64_t)p.b * c.max_blocks;
+  Tbl t;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) t.e[g] = row[min((p.ch * kChunk + 8 * g) >> c.log2bs, c.max_blocks - 1)];
+  return t;
+}
+
+// One chunk in flight: its K and V registers (row pieces, as loaded), where
+// its keys live, and its unit's scales.  K and V go through LDS (as bf16):
+// every load instruction then reads whole 128-byte lines of a few rows, and
+// the MFMA operands come from LDS reads.
 template <int CT, int D>
 struct Chunk {
-  uint4 k[2][Geo<CT, D>::KL];   // [16-key block][load]: this lane's K bytes
-  uint4 v[Geo<CT, D>::vloads];  // V: piece lane % pieces of row vkeys * i + lane / pieces
-  uint4 q[Geo<CT, D>::KS];      // q of head lane % 16 (zero for absent heads), 8 elements per k-step
+  uint4 k[Geo<CT, D>::vloads];  // K: piece lane % pieces of row vkeys * i + lane / pieces
+  uint4 v[Geo<CT, D>::vloads];  // V: the same pieces
   uint32_t kmask;               // bit k: key k of the chunk exists and sits in a valid block
   int64_t off[4];               // byte offsets of the chunk's four 8-key groups (uniform)
   float ls;                     // |softmax scale x K scale| x log2 e of the chunk's unit
@@ -1080,96 +1113,71 @@ struct Chunk {
   uint32_t qs;                  // sign flip applied to q (negative scale)
 };
 
-// Per-lane byte offsets: K operand row lane % 16 (within 16 rows, or & 7
-// within 8) with the lane's 16 bytes of each load; V copy row lane / pieces;
+// Per-lane byte offsets: row lane / pieces of a load instruction (K and V),
 // q row lane % 16 (past the unit's rows for absent heads, which read 0).
 struct Offs {
-  uint32_t k16, k8, v, q;
+  uint32_t row, q;
 };
 
-// Loads of chunk p's K in the A-operand layout.  Each 8-key group of the
-// chunk lies in one block (block_size >= 8; with block_size >= 16 each
-// 16-key half does) and is addressed through a buffer descriptor; keys past
-// the end or in invalid blocks read row 0 of block 0 and are masked.
-template <int CT, int D, bool SMALL>
-__device__ __forceinline__ void load_k(Chunk<CT, D>& r, const StreamCtx& c, const Pos& p, int tbl,
-                                       const Offs& o, int lane) {
+// Loads of chunk p's K and V rows.  Each 8-key group of the chunk lies in
+// one block (block_size >= 8) and one load instruction covers at most 8 rows
+// of one group, addressed through a buffer descriptor; keys past the end or
+// in invalid blocks read row 0 of block 0 and are masked.
+template <int CT, int D>
+__device__ __forceinline__ void load_kv(Chunk<CT, D>& r, const StreamCtx& c, const Pos& p, const Tbl& tbl,
+                                        const Offs& o) {
   using G = Geo<CT, D>;
-  const int lk = seq_len(c, p.b);
+  const int lk = p.len;
   const int start = p.ch * kChunk;
-  const uint8_t* kbase = c.k_cache + p.gg * c.row_bytes;
   uint32_t mask = 0;
 #pragma unroll
   for (int grp = 0; grp < 4; ++grp) {
     const int key = start + 8 * grp;
-    const int id = __builtin_amdgcn_readlane(tbl, grp);
+    const int id = tbl.e[grp];
     const bool ok = key < lk && id >= 0 && id < c.num_blocks;
     r.off[grp] = ok ? (int64_t)id * c.block_bytes + (int64_t)(key & (c.bs - 1)) * c.slot_stride : 0;
     const int n = min(max(lk - key, 0), 8);
     mask |= (ok ? ((1u << n) - 1u) : 0u) << (8 * grp);
   }
-  if constexpr (!SMALL) {
-    // a 16-key half lies in one block: its second group follows its first
-    r.off[1] = r.off[0] + 8 * (int64_t)c.slot_stride;
-    r.off[3] = r.off[2] + 8 * (int64_t)c.slot_stride;
-  }
   r.kmask = mask;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    if constexpr (!SMALL) {
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(kbase + r.off[2 * kb]), 0, 16 * c.slot_stride, kBufferWord3);
-#pragma unroll
-      for (int j = 0; j < G::KL; ++j) {
-        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o.k16, j * 64, 0);
-        r.k[kb][j] = make_uint4(x.x, x.y, x.z, x.w);
-      }
-    } else {
-      // keys 0..7 and 8..15 of the half sit in two blocks: every lane reads
-      // both (lanes that share an address merge) and keeps its own
-      const bool hi8 = (lane & 15) >= 8;
-      const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(kbase + r.off[2 * kb]), 0, 8 * c.slot_stride, kBufferWord3);
-      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(kbase + r.off[2 * kb + 1]), 0, 8 * c.slot_stride, kBufferWord3);
-#pragma unroll
-      for (int j = 0; j < G::KL; ++j) {
-        const u32x4_t xa = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)o.k8, j * 64, 0);
-        const u32x4_t xb = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)o.k8, j * 64, 0);
-        const u32x4_t x = hi8 ? xb : xa;
-        r.k[kb][j] = make_uint4(x.x, x.y, x.z, x.w);
-      }
-    }
-  }
-}
-
-// Loads of the V rows of the chunk whose K load_k issued (same offsets).
-template <int CT, int D>
-__device__ __forceinline__ void load_v(Chunk<CT, D>& r, const StreamCtx& c, int gg, const Offs& o) {
-  using G = Geo<CT, D>;
-  const uint8_t* vbase = c.v_cache + gg * c.row_bytes;
+  const uint8_t* kbase = c.k_cache + p.gg * c.row_bytes;
+  const uint8_t* vbase = c.v_cache + p.gg * c.row_bytes;
 #pragma unroll
   for (int i = 0; i < G::vloads; ++i) {
     const int row0 = G::vkeys * i;  // first key of the instruction (within one 8-key group)
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + r.off[row0 >> 3]), 0, 8 * c.slot_stride, kBufferWord3);
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o.row, (row0 & 7) * c.slot_stride, 0);
+    r.k[i] = make_uint4(x.x, x.y, x.z, x.w);
+  }
+#pragma unroll
+  for (int i = 0; i < G::vloads; ++i) {
+    const int row0 = G::vkeys * i;
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vbase + r.off[row0 >> 3]), 0, 8 * c.slot_stride, kBufferWord3);
-    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)o.v, (row0 & 7) * c.slot_stride, 0);
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)o.row, (row0 & 7) * c.slot_stride, 0);
     r.v[i] = make_uint4(x.x, x.y, x.z, x.w);
   }
 }
 
-// q rows of chunk p's unit (G heads) as the B operand, and the unit's scales.
+// q rows of unit p (G heads) as the B operand: head lane % 16 (zero for
+// absent heads), 8 elements per k-step.
 template <int CT, int D, int G>
-__device__ __forceinline__ void load_qf(Chunk<CT, D>& r, const DecodeArgs& a, const Pos& p, const Offs& o) {
+__device__ __forceinline__ void load_q(uint4 (&q)[D / 32], const DecodeArgs& a, const Pos& p,
+                                       const Offs& o) {
   using Ge = Geo<CT, D>;
   const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)p.b * a.num_heads + p.gg * G) * Ge::qrow;
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, G * Ge::qrow, kBufferWord3);
 #pragma unroll
   for (int ks = 0; ks < Ge::KS; ++ks) {
-    const int imm = CT == kFP8 ? 128 * (ks / 2) + 16 * (ks % 2) : 64 * ks;
-    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)o.q, imm, 0);
-    r.q[ks] = make_uint4(x.x, x.y, x.z, x.w);
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)o.q, 64 * ks, 0);
+    q[ks] = make_uint4(x.x, x.y, x.z, x.w);
   }
+}
+
+// The scales of unit p.
+template <int CT, int D>
+__device__ __forceinline__ void unit_scales(Chunk<CT, D>& r, const DecodeArgs& a, const Pos& p) {
   // The chunk max is taken over unscaled scores, which needs a scale > 0: a
   // negative scale is applied as |scale| to -q (bf16 negation is exact), a
   // zero scale as 1e-30 (every logit then rounds to 0 in the exponent, while
@@ -1177,36 +1185,43 @@ __device__ __forceinline__ void load_qf(Chunk<CT, D>& r, const DecodeArgs& a, co
   float sc = a.softmax_scale;
   r.vs = 1.0f;
   if constexpr (CT == kFP8) {
-    sc *= a.k_scale[p.gg];
-    r.vs = a.v_scale[p.gg];
+    sc *= ((sptr_f32)a.k_scale)[p.gg];
+    r.vs = ((sptr_f32)a.v_scale)[p.gg];
   }
   r.qs = sc < 0.0f ? 0x80008000u : 0u;
   r.ls = fmaxf(fabsf(sc) * kLog2e, 1e-30f);
 }
 
-// V rows of the chunk (registers) -> this wave's LDS region as bf16.  Rows of
-// keys that do not exist are stored as zeros: their p is 0, but the cache may
-// hold anything there (NaN included) and 0 * NaN would leak.
+// K and V rows of the chunk (registers) -> this wave's LDS regions as bf16.
+// V rows of keys that do not exist are stored as zeros: their p is 0, but the
+// cache may hold anything there (NaN included) and 0 * NaN would leak (their
+// scores are masked, so K rows need no such care).
+template <int CT, int D, int SW>
+__device__ __forceinline__ void store_rows(const uint4& x, uint8_t* w, int row, int piece) {
+  using G = Geo<CT, D>;
+  const int sw = SW == 0 ? kswz<D>(row) : vswz<D>(row);
+  if constexpr (CT == kFP8) {
+    uint4 lo, hi;
+    e4m3x16_to_bf16(x, lo, hi);
+    *reinterpret_cast<uint4*>(w + row * G::lds_row + (((2 * piece) ^ sw) << 4)) = lo;
+    *reinterpret_cast<uint4*>(w + row * G::lds_row + (((2 * piece + 1) ^ sw) << 4)) = hi;
+  } else {
+    *reinterpret_cast<uint4*>(w + row * G::lds_row + ((piece ^ sw) << 4)) = x;
+  }
+}
+
 template <int CT, int D>
-__device__ __forceinline__ void store_v(const Chunk<CT, D>& r, uint8_t* v_w, int lane) {
+__device__ __forceinline__ void store_kv(const Chunk<CT, D>& r, uint8_t* k_w, uint8_t* v_w, int lane) {
   using G = Geo<CT, D>;
   const bool full = r.kmask == 0xffffffffu;
   if (G::vlanes < 64 && lane >= G::vlanes) return;
+  const int piece = lane % G::pieces;
 #pragma unroll
   for (int i = 0; i < G::vloads; ++i) {
     const int row = G::vkeys * i + lane / G::pieces;
     const bool ok = full || ((r.kmask >> row) & 1u);
-    const uint4 x = ok ? r.v[i] : make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (CT == kFP8) {
-      uint4 lo, hi;
-      e4m3x16_to_bf16(x, lo, hi);
-      const int p0 = 2 * (lane % G::pieces);  // bf16 pieces of the sixteen elements
-      *reinterpret_cast<uint4*>(v_w + row * G::lds_row + ((p0 ^ vswz<D>(row)) << 4)) = lo;
-      *reinterpret_cast<uint4*>(v_w + row * G::lds_row + (((p0 + 1) ^ vswz<D>(row)) << 4)) = hi;
-    } else {
-      const int pos = (lane % G::pieces) ^ vswz<D>(row);
-      *reinterpret_cast<uint4*>(v_w + row * G::lds_row + pos * 16) = x;
-    }
+    store_rows<CT, D, 0>(r.k[i], k_w, row, piece);
+    store_rows<CT, D, 1>(ok ? r.v[i] : make_uint4(0u, 0u, 0u, 0u), v_w, row, piece);
   }
 }
 
@@ -1219,27 +1234,21 @@ struct MState {
 
 constexpr float kRescaleBits = 8.0f;  // lazy running max (log2 domain)
 
-// S^T = K Q^T for the chunk in r: register i of block kb holds the score of
-// key 16 kb + 4 (lane / 16) + i for head lane % 16.
+// S^T = K Q^T for the chunk (K in LDS, q in r): register i of block kb holds
+// the score of key 16 kb + 4 (lane / 16) + i for head lane % 16.  k_off[ks]:
+// this lane's A-operand piece (row lane % 16, elements 32 ks + 8 (lane / 16)).
 template <int CT, int D>
-__device__ __forceinline__ void chunk_scores(f32x4_t (&s)[2], const Chunk<CT, D>& r) {
+__device__ __forceinline__ void chunk_scores(f32x4_t (&s)[2], const uint4 (&qf)[D / 32], uint32_t qs,
+                                             const uint8_t* k_w, const uint32_t (&k_off)[D / 32]) {
   using G = Geo<CT, D>;
   s[0] = f32x4_t{};
   s[1] = f32x4_t{};
-  const uint32_t qs = r.qs;
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) {
-    const uint4 q = make_uint4(r.q[ks].x ^ qs, r.q[ks].y ^ qs, r.q[ks].z ^ qs, r.q[ks].w ^ qs);
+    const uint4 q = make_uint4(qf[ks].x ^ qs, qf[ks].y ^ qs, qf[ks].z ^ qs, qf[ks].w ^ qs);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      uint4 kf;
-      if constexpr (CT == kFP8) {
-        uint4 lo, hi;
-        e4m3x16_to_bf16(r.k[kb][ks / 2], lo, hi);
-        kf = (ks & 1) ? hi : lo;
-      } else {
-        kf = r.k[kb][ks];
-      }
+      const uint4 kf = *reinterpret_cast<const uint4*>(k_w + kb * 16 * G::lds_row + k_off[ks]);
       s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(q), s[kb], 0, 0, 0);
     }
   }
@@ -1330,14 +1339,14 @@ __device__ __forceinline__ void flush(MState<D>& st, const DecodeArgs& a, const 
   for (int db = 0; db < DB; ++db) st.o[db] = f32x4_t{};
 }
 
-// N chunks in flight per wave, held in registers at one wave per SIMD (up to
-// 512 registers): as many bytes in flight per CU as two waves with half the
-// depth, without spilling.
-template <int CT, int D, int G, bool SMALL, int N>
-__global__ __launch_bounds__(kStreamThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
+// N chunks in flight per wave, held in registers, OCC waves per SIMD (up to
+// 512 / OCC registers per lane).
+template <int CT, int D, int G, int N, int OCC>
+__global__ __launch_bounds__(kStreamThreads, OCC) void decode_mfma_kernel(DecodeArgs a) {
   using Ge = Geo<CT, D>;
   __shared__ int32_t pre[kStreamMaxBatch + 1];
   __shared__ int32_t part[kStreamThreads];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kWaves][Ge::vbytes];
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[kWaves][Ge::vbytes];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1370,13 +1379,16 @@ __global__ __launch_bounds__(kStreamThreads, 1) void decode_mfma_kernel(DecodeAr
   c.heads_per_kv = G;
   c.head_groups = 1;
   Offs o;
-  o.k16 = (uint32_t)((lane & 15) * c.slot_stride + (lane >> 4) * 16);
-  o.k8 = (uint32_t)((lane & 7) * c.slot_stride + (lane >> 4) * 16);
-  o.v = lane < Ge::vlanes ? (uint32_t)((lane / Ge::pieces) * c.slot_stride + (lane % Ge::pieces) * 16)
-                         : 0x7ffffff0u;  // idle lanes read nothing
-  o.q = (lane & 15) < G ? (uint32_t)((lane & 15) * Ge::qrow + (lane >> 4) * (CT == kFP8 ? 32 : 16)) : 0x7ffffff0u;
+  o.row = lane < Ge::vlanes ? (uint32_t)((lane / Ge::pieces) * c.slot_stride + (lane % Ge::pieces) * 16)
+                           : 0x7ffffff0u;  // idle lanes read nothing
+  o.q = (lane & 15) < G ? (uint32_t)((lane & 15) * Ge::qrow + (lane >> 4) * 16) : 0x7ffffff0u;
 
+  uint8_t* k_w = k_lds[wave];
   uint8_t* v_w = v_lds[wave];
+  uint32_t k_off[Ge::KS];
+#pragma unroll
+  for (int ks = 0; ks < Ge::KS; ++ks)
+    k_off[ks] = (lane & 15) * Ge::lds_row + (((4 * ks + (lane >> 4)) ^ kswz<D>(lane & 15)) << 4);
   // transposed-read offsets: group lane / 16 reads keys 4 (lane / 16) + 16 x + (lane % 16) / 4,
   // elements 16 db + 4 (lane % 4) .. + 3 (vswz does not depend on the 16 x)
   uint32_t v_off[Ge::DB];
@@ -1395,41 +1407,56 @@ __global__ __launch_bounds__(kStreamThreads, 1) void decode_mfma_kernel(DecodeAr
 #pragma unroll
   for (int db = 0; db < Ge::DB; ++db) st.o[db] = f32x4_t{};
 
-  // N chunks in flight: at the step of chunk x the ring slot R holds x and
-  // the other slots x + 1 .. x + N - 1 (loading); as soon as x's K has fed
-  // its MFMAs and its V has gone to LDS, R is refilled with x + N.  Positions
-  // past the wave's last chunk repeat it (loaded, never used), so every step
-  // issues the same loads.
-  auto clamp_next = [&](const Pos& p, int xp) __attribute__((always_inline)) {
-    return xp + 1 < c1 ? advance(pre, ug, p) : p;
+  // N chunks in flight: at the step of chunk x ring slot x % N holds x and
+  // the other slots x + 1 .. x + N - 1 (loading).  Once x's K and V are in
+  // LDS and its scores are taken, the slot is refilled with x + N.  q of a
+  // chunk's unit is loaded before the loads of the chunk after it (N - 1
+  // buffers: q of x + N - 1 goes into x's buffer once its scores are taken).
+  // Vector loads complete in order, so every wait is for the oldest chunk
+  // only.  Positions past the wave's last chunk repeat it (loaded, never
+  // used), so every step issues the same loads.
+  constexpr int NQ = N > 1 ? N - 1 : 1;
+  auto next_pos = [&](const Pos& p, int xp) __attribute__((always_inline)) {
+    if (xp + 1 >= c1) return p;
+    Pos n = advance(pre, ug, p);
+    n.len = n.b == p.b ? p.len : seq_len_s(c, n.b);
+    return n;
   };
-  auto issue = [&](Chunk<CT, D>& r, const Pos& p, int tbl) __attribute__((always_inline)) {
-    load_k<CT, D, SMALL>(r, c, p, tbl, o, lane);
-    load_v<CT, D>(r, c, p.gg, o);
-    load_qf<CT, D, G>(r, a, p, o);
+  auto issue = [&](Chunk<CT, D>& r, const Pos& p, const Tbl& t) __attribute__((always_inline)) {
+    load_kv<CT, D>(r, c, p, t, o);
+    unit_scales<CT, D>(r, a, p);
   };
   Chunk<CT, D> ring[N];
+  uint4 qbuf[NQ][Ge::KS];
   Pos cur = locate(pre, a.batch, ug, c0);
-  Pos ip = cur;  // next chunk to load: c0 + N after the prologue
+  cur.len = seq_len_s(c, cur.b);
+  Pos ip = cur, lp = cur;  // next chunk to load, last chunk loaded
 #pragma unroll
   for (int j = 0; j < N; ++j) {
-    issue(ring[j], ip, fetch_table(c, ip, lane));
-    ip = clamp_next(ip, c0 + j);
+    if (j < NQ) load_q<CT, D, G>(qbuf[j], a, ip, o);
+    issue(ring[j], ip, fetch_tbl(c, ip));
+    lp = ip;
+    ip = next_pos(ip, c0 + j);
   }
-  int tbl_ip = fetch_table(c, ip, lane);
+  Tbl tb = fetch_tbl(c, ip);
   int x = c0;
-  auto step = [&](Chunk<CT, D>& R) __attribute__((always_inline)) -> bool {
-    const Pos ipn = clamp_next(ip, x + N);
-    const int tbl_ipn = fetch_table(c, ipn, lane);
-    store_v<CT, D>(R, v_w, lane);
+  auto step = [&](Chunk<CT, D>& R, uint4 (&Q)[Ge::KS]) __attribute__((always_inline)) -> bool {
+    const Pos ipn = next_pos(ip, x + N);
+    const Tbl tbn = fetch_tbl(c, ipn);
+    store_kv<CT, D>(R, k_w, v_w, lane);
+    const uint32_t kmask = R.kmask;
+    const float ls = R.ls, vs = R.vs;
+    const uint32_t qs = R.qs;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     f32x4_t s[2];
-    chunk_scores<CT, D>(s, R);
-    const uint32_t kmask = R.kmask;
-    const float ls = R.ls, vs = R.vs;
-    issue(R, ip, tbl_ip);
+    chunk_scores<CT, D>(s, Q, qs, k_w, k_off);
+    load_q<CT, D, G>(Q, a, lp, o);
+    issue(R, ip, tb);
+    lp = ip;
+    ip = ipn;
+    tb = tbn;
     chunk_update<D>(st, s, kmask, v_w, v_off, ls, lane);
     const bool last = x + 1 == c1;
     if (last || cur.ch + 1 == cur.nch) {
@@ -1439,59 +1466,58 @@ __global__ __launch_bounds__(kStreamThreads, 1) void decode_mfma_kernel(DecodeAr
       flush<D, G>(st, a, cur, whole, w + u, vs, lane);
     }
     if (last) return false;
-    cur = advance(pre, ug, cur);
-    ip = ipn;
-    tbl_ip = tbl_ipn;
+    cur = next_pos(cur, x);
     ++x;
-    // the next step overwrites this chunk's V in LDS: its reads are done
-    // (they fed this chunk's MFMAs)
+    // the next step overwrites this chunk's K and V in LDS: their reads are
+    // done (they fed this chunk's MFMAs)
     return true;
   };
+  // rounds of lcm(N, NQ) steps (every ring and q index a compile-time
+  // constant, so all stay in registers).  Each step that ends the wave's
+  // range leaves the loop directly: no path from such a step reaches the
+  // loop head, whose waits would otherwise be sized for it.
+  constexpr int R = N * NQ / (N % NQ == 0 ? NQ : 1);
+  static_assert(R <= 6, "ring depth");
   for (;;) {
-    if (!step(ring[0])) break;
-    if (!step(ring[1])) break;
-    if constexpr (N > 2) {
-      if (!step(ring[2])) break;
+    if (!step(ring[0], qbuf[0])) break;
+    if (!step(ring[1 % N], qbuf[1 % NQ])) break;
+    if constexpr (R > 2) {
+      if (!step(ring[2 % N], qbuf[2 % NQ])) break;
+      if (!step(ring[3 % N], qbuf[3 % NQ])) break;
     }
-    if constexpr (N > 3) {
-      if (!step(ring[3])) break;
-    }
-    if constexpr (N > 4) {
-      if (!step(ring[4])) break;
-    }
-    if constexpr (N > 5) {
-      if (!step(ring[5])) break;
+    if constexpr (R > 4) {
+      if (!step(ring[4 % N], qbuf[4 % NQ])) break;
+      if (!step(ring[5 % N], qbuf[5 % NQ])) break;
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // loads past the last chunk land before the wave ends
 }
 
-// Chunks in flight per wave: about 48 KiB of K and V either way.
+// Chunks in flight per wave and waves per SIMD: bf16 chunks (16 KiB of K and
+// V at head_dim 128) take 64 registers a lane, so two of them fit one wave
+// per SIMD; fp8 chunks take half that, and two of them fit two waves.
 template <int CT>
 constexpr int depth() {
   return CT == kFP8 ? PKV_DECODE_DEPTH_FP8 : PKV_DECODE_DEPTH;
+}
+
+// Waves per SIMD the kernel is compiled for.
+template <int CT>
+constexpr int occupancy() {
+  return CT == kFP8 ? PKV_DECODE_OCC_FP8 : PKV_DECODE_OCC;
 }
 
 template <int CT, int D, int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   constexpr int N = depth<CT>();
   static int cached_grid = 0;  // per instantiation; the CU count of one process's GPUs is fixed
-  const bool small = a.block_size < 16;
-  if (cached_grid == 0)
-    cached_grid = small ? persistent_grid(decode_mfma_kernel<CT, D, G, true, N>)
-                        : persistent_grid(decode_mfma_kernel<CT, D, G, false, N>);
+  if (cached_grid == 0) cached_grid = persistent_grid(decode_mfma_kernel<CT, D, G, N, occupancy<CT>()>);
   const int64_t max_chunks = (int64_t)a.batch * a.num_kv_heads *
                              (((int64_t)a.max_blocks_per_seq * a.block_size + kChunk - 1) / kChunk);
   int64_t grid = cached_grid;
   if (grid * kWaves > max_chunks) grid = (max_chunks + kWaves - 1) / kWaves;
   if (grid < 1) grid = 1;
-  if (small) {
-    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, G, true, N>), dim3((unsigned)grid), dim3(kStreamThreads), 0,
-                       stream, a);
-  } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, G, false, N>), dim3((unsigned)grid), dim3(kStreamThreads), 0,
-                       stream, a);
-  }
+  hipLaunchKernelGGL((decode_mfma_kernel<CT, D, G, N, occupancy<CT>()>), dim3((unsigned)grid), dim3(kStreamThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)a.batch * a.num_heads;

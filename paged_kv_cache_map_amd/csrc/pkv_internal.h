@@ -45,7 +45,7 @@ constexpr int kDecodeChunk = 32;                              // keys per wave i
 constexpr int kDecodeKeysPerWg = kDecodeWaves * kDecodeChunk;  // 128
 constexpr int kDecodeMaxSplitKeys = 8192;                     // bounds the LDS block table
 constexpr int kStreamThreads = 256;                           // stream-K decode workgroup
-constexpr int kStreamMaxBatch = 4096;                         // LDS chunk-count table
+constexpr int kStreamMaxBatch = 2048;                         // LDS chunk-count table
 constexpr int kStreamMaxWaves = 4096;                         // bounds the stream-K workspace
 
 // Fills `plan`; returns false (with a message in *why) for arguments the
