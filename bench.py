@@ -86,7 +86,7 @@ def prefill_flops(step):
 # measured in the same runs.  The figures belong to the decode sources with
 # the given digest: after any change to them the traffic is reported as null
 # until the counters are taken again.
-DECODE_TRAFFIC = {"digest": "62db048fbf58d291", "read_bytes": 560387253, "write_bytes": 5786214}
+DECODE_TRAFFIC = {"digest": "1f3498aa5041adef", "read_bytes": 551602841, "write_bytes": 3628768}
 DECODE_SOURCES = ("paged_kv_cache_map_amd/csrc/paged_decode.hip",
                   "paged_kv_cache_map_amd/csrc/pkv_device.hpp",
                   "paged_kv_cache_map_amd/csrc/pkv_plan.cpp",
@@ -325,7 +325,7 @@ def main():
                    "context": "cached lengths U{512..4096} (+1 new token)",
                    "keys_total": int(d["cache_seqlens"].sum()),
                    "step_bytes": int(step_bytes)},
-        "roofline": {"kernel": "paged_decode call (stream-K plan: decode_stream_kernel + stream_merge_kernel)",
+        "roofline": {"kernel": "paged_decode call (stream-K plan on the matrix cores: decode_mfma_kernel + stream_merge_kernel)",
                      "bound": "hbm", "achieved": round(main_res["decode_gbs"], 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(main_res["decode_gbs"] / HBM_PEAK_GBS, 4),
