@@ -9,7 +9,14 @@
 // "KV cache / batching / paged attention", section "FlashAttention：注意計算そのも
 // のを速く": tiles stay on chip and the result equals plain attention.
 //
-// bf16 / fp8-cache kernel (gfx950 MFMA, v_mfma_f32_32x32x16_bf16):
+// Main kernel (prefill16_kernel; bf16 caches, and paged fp8 caches at
+// head_dim 128): 128 query rows of one (request, q head) per workgroup, 8
+// waves x 16 rows on v_mfma_f32_16x16x32_bf16, four waves per SIMD; K and V
+// tiles copied HBM -> LDS by DMA (buffer loads with the lds bit, 1 KiB per
+// wave instruction, no registers), two stages.  Details at the kernel.
+//
+// Register-staged kernel (prefill_kernel; fp8 caches at head_dim 64), on
+// v_mfma_f32_32x32x16_bf16:
 // * workgroup = 128 query rows of one (request, q head); 4 waves x 32 rows.
 // * per 64-key tile: S^T = K Q^T on MFMA (keys x queries), so each lane owns
 //   one query column and 16 of its 32 scores per 32-key block; the row max and
@@ -21,9 +28,10 @@
 //   flight while the current tile is computed.  fp8 caches are dequantised to
 //   bf16 (exact) while staging; the K scale folds into the logit scale, the V
 //   scale into the output.
-// * workgroups are renumbered (work_item) so that the tiles of one (request,
-//   KV head) run on the same XCD and share its L2, with the pairs balanced
-//   over the XCDs and the longest query tiles first.
+//
+// Both renumber workgroups (work_item) so that the tiles of one (request,
+// KV head) run on the same XCD and share its L2, with the pairs balanced
+// over the XCDs and the longest query tiles first.
 //
 // fp32 kernel: a plain per-row wave kernel (lanes over head_dim), kept for
 // fp32 accuracy checks; it is not tuned.
@@ -32,15 +40,6 @@
 
 #include "pkv_device.hpp"
 #include "pkv_internal.h"
-
-// Launch shape of the bf16 prefill kernel: waves per workgroup (32 query
-// rows each) and LDS stages of the K/V copy pipeline.
-#ifndef PKV_PREFILL_WAVES
-#define PKV_PREFILL_WAVES 4
-#endif
-#ifndef PKV_PREFILL_STAGES
-#define PKV_PREFILL_STAGES 2
-#endif
 
 namespace pkv {
 namespace {
@@ -512,43 +511,34 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 cache kernel: K/V tiles move HBM -> LDS by DMA, V is read transposed
+// DMA-fed kernel: K/V tiles move HBM -> LDS by DMA, V is read transposed
 // ---------------------------------------------------------------------------
 //
-// * workgroup = 128 query rows of one (request, q head); 4 waves x 32 rows,
-//   two workgroups per CU (at most 256 registers per lane), so one wave's
-//   softmax overlaps another's MFMA on every SIMD.
-// * a 64-key tile of K and of V is copied straight from HBM into LDS with
-//   global_load_lds_dwordx4 (1 KiB per wave instruction; no registers).  The
-//   DMA writes each KiB contiguously, so bank conflicts are avoided by
-//   permuting what each lane fetches: LDS piece position i of row r holds the
-//   row's 16-byte piece i ^ swz(r).  Tiles are double-buffered in two
-//   separate LDS objects and the next tile's DMA is in flight while the
-//   current one is computed.
-// * S^T = K Q^T (keys x queries) on v_mfma_f32_32x32x16_bf16 with K rows read
-//   from LDS as the A operand and Q held in registers as the B operand.
-// * O^T += V^T P^T: V stays row-major in LDS and ds_read_b64_tr_b16 hands each
-//   lane four consecutive keys of one head_dim element, which is the A operand
-//   layout; P^T (bf16) comes straight from the lane's own S^T registers.
+// * a 64-key tile of K and of V is copied straight from HBM into LDS (1 KiB
+//   per wave instruction; no registers).  The DMA writes each KiB
+//   contiguously, so bank conflicts are avoided by permuting what each lane
+//   fetches: LDS piece position i of row r holds the row's 16-byte piece
+//   i ^ swz(r).  fp8 tiles are copied as they are and dequantised by the wave
+//   that copied them into bf16 tiles with the same permutations.
 // * online softmax in the log2 domain with a lazy running max: the output is
 //   rescaled only when a row's max grows by more than 2^8, so most tiles skip
 //   the rescale; the result is the same exact algebra (numerator and
 //   denominator always share one reference max).  Row sums accumulate the
 //   bf16-rounded p that the MFMA consumes.
-// * block-table entries of tile t+1 are read (scalar loads) while tile t is
-//   computed; keys past the sequence end or in invalid blocks are masked, and
-//   their V rows are zeroed in LDS so that stale cache contents never reach
-//   the output.
+// * keys past the sequence end or in invalid blocks are masked, and their V
+//   rows are zeroed in LDS so that stale cache contents never reach the
+//   output.
 namespace dma {
 
 constexpr int kBN = 64;
 constexpr float kRescaleBits = 8.0f;  // lazy-max threshold (log2 domain)
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor, dword 3
 
 // Tile geometry for head_dim D and W waves per workgroup (32 query rows per
 // wave): one DMA instruction fills 1 KiB of a K or V tile.
-template <int D, int W>
+template <int D, int W, int E = 2>
 struct Tile {
-  static constexpr int row_bytes = D * 2;
+  static constexpr int row_bytes = D * E;  // E: bytes per element
   static constexpr int pieces = row_bytes / 16;          // 16-byte pieces per row
   static constexpr int bytes = kBN * row_bytes;          // one K or V tile
   static constexpr int rows_per_dma = 1024 / row_bytes;  // rows one DMA instruction fills
@@ -557,17 +547,6 @@ struct Tile {
   static constexpr int groups_per_wave = rows_per_wave / 8;  // 8-key groups
   static_assert(dma_per_wave >= 1 && groups_per_wave >= 1, "tile shape");
 };
-
-// LDS piece permutation of row r: a linear map (over GF(2)) of the row's low
-// four bits, chosen so that both reads of a tile are free of bank conflicts
-// (checked for 32 and 64 banks): the K operand reads (16 consecutive rows,
-// one piece) and the transposed V reads (4 consecutive rows x 4 pieces).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  // images of row bits 0..3
-  constexpr int b0 = D == 128 ? 4 : 2, b1 = D == 128 ? 10 : 4, b2 = 1, b3 = 2;
-  return ((r & 1) ? b0 : 0) ^ ((r & 2) ? b1 : 0) ^ ((r & 4) ? b2 : 0) ^ ((r & 8) ? b3 : 0);
-}
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -637,33 +616,6 @@ __device__ __forceinline__ void resolve(TileMap<GPW>& m, const PrefillArgs& a, c
   }
 }
 
-// DMA of this wave's rows of one tile (K and V) into buffers (kbuf, vbuf).
-// Paged rows come from the tile map; packed rows are clamped to the last key
-// (lk >= 1 whenever a tile exists), so no address leaves the request.
-template <int D, int W, bool PAGED>
-__device__ __forceinline__ void issue_tile(const TileMap<Tile<D, W>::groups_per_wave>& m,
-                                           const uint8_t* kbase, const uint8_t* vbase,
-                                           int64_t row_stride, int key0, int lk, uint8_t* kbuf,
-                                           uint8_t* vbuf, int wave, int lane) {
-  using T = Tile<D, W>;
-  const int rr = lane / T::pieces;   // row within the instruction
-  const int pos = lane % T::pieces;  // LDS piece position
-#pragma unroll
-  for (int j = 0; j < T::dma_per_wave; ++j) {
-    const int chunk = wave * T::dma_per_wave + j;
-    const int r = chunk * T::rows_per_dma + rr;  // row within the tile
-    const int piece = pos ^ swz<D>(r);
-    int64_t go;
-    if constexpr (PAGED) {
-      go = m.off[(j * T::rows_per_dma) >> 3] + (int64_t)(r & 7) * row_stride + piece * 16;
-    } else {
-      go = (int64_t)min(key0 + r, lk - 1) * row_stride + piece * 16;
-    }
-    __builtin_amdgcn_global_load_lds((const void*)(kbase + go), (lds_void_t*)(kbuf + chunk * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(vbase + go), (lds_void_t*)(vbuf + chunk * 1024), 16, 0, 0);
-  }
-}
-
 // Zero this wave's V rows of keys that do not exist (after its DMA landed).
 template <int D, int W>
 __device__ __forceinline__ void zero_rows(uint64_t valid, uint8_t* vbuf, int wave, int lane) {
@@ -681,25 +633,112 @@ __device__ __forceinline__ void zero_rows(uint64_t valid, uint8_t* vbuf, int wav
   }
 }
 
-// W waves x 32 query rows per workgroup; S LDS stages (the copy of tile t+S-1
-// is in flight while tile t is computed).
-template <int D, bool PAGED, int W, int S>
-__global__ __launch_bounds__(64 * W, 2) void prefill_dma_kernel(PrefillArgs a, int q_tiles) {
-  using T = Tile<D, W>;
-  constexpr int BM = 32 * W;
-  constexpr int KS = D / 16;  // MFMA k-steps over head_dim
-  constexpr int DB = D / 32;  // 32-row blocks of O^T
+// Piece permutations of the 16-query-row kernel (K read as 16 consecutive
+// rows x one piece for the A operand; V read transposed, 16 consecutive rows
+// x 2 pieces): both free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int kswz16(int r) {
+  return D == 128 ? (r & 15) : (r & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz16(int r) {
+  return D == 128 ? ((r & 7) << 1) : ((r & 3) << 1);
+}
+
+// An LDS address whose object the compiler cannot see.  The pipelined
+// kernel waits for its copies itself (s_waitcnt before a barrier); the
+// compiler does not track copies made through such an address, where it
+// would otherwise make some LDS reads wait for every copy in flight (its
+// record of which copy feeds which buffer does not survive the loop).
+__device__ __forceinline__ lds_void_t* lds_opaque(uint8_t* p) {
+  uint32_t x = (uint32_t)(uintptr_t)(lds_void_t*)p;
+  asm volatile("" : "+s"(x));
+  return (lds_void_t*)(uintptr_t)x;
+}
+
+// DMA of this wave's rows of one K or V tile into buf, through buffer
+// descriptors: paged rows by the 8-key group's block, packed rows from the
+// tile's first key with the descriptor ending at the request's last key, so
+// rows past it read zeros.  SW picks the piece permutation (0: none, 1: the
+// K operand's, 2: the transposed V reads'); E is the element size.
+template <int D, int W, bool PAGED, int SW, int E = 2>
+__device__ __forceinline__ void issue_rows(const TileMap<Tile<D, W, E>::groups_per_wave>& m, const uint8_t* base,
+                                           int64_t row_stride, int key0, int lk, uint8_t* buf, int wave,
+                                           int lane) {
+  using T = Tile<D, W, E>;
+  const int rr = lane / T::pieces;
+  const int pos = lane % T::pieces;
+  __amdgpu_buffer_rsrc_t rs[PAGED ? T::groups_per_wave : 1];
+  if constexpr (PAGED) {
+#pragma unroll
+    for (int x = 0; x < T::groups_per_wave; ++x)
+      rs[x] = __builtin_amdgcn_make_buffer_rsrc((void*)(base + m.off[x]), 0, (int)(8 * row_stride), kBufferWord3);
+  } else {
+    const int rows = min(lk - key0, kBN);  // >= 1: only tiles that hold a key are copied
+    rs[0] = __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)key0 * row_stride), 0,
+                                              (int)((rows - 1) * row_stride + T::row_bytes), kBufferWord3);
+  }
+#pragma unroll
+  for (int j = 0; j < T::dma_per_wave; ++j) {
+    const int chunk = wave * T::dma_per_wave + j;
+    const int r = chunk * T::rows_per_dma + rr;
+    const int piece = pos ^ (SW == 0 ? 0 : (SW == 1 ? kswz16<D>(r) : vswz16<D>(r)));
+    if constexpr (PAGED) {
+      const int voff = (int)((r & 7) * row_stride) + piece * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[(j * T::rows_per_dma) >> 3], lds_opaque(buf + chunk * 1024), 16,
+                                               voff, 0, 0, 0);
+    } else {
+      const int voff = (int)(r * row_stride) + piece * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[0], lds_opaque(buf + chunk * 1024), 16, voff, 0, 0, 0);
+    }
+  }
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float max_quarters(float x) {  // over lanes l, l^16, l^32, l^48
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_halves(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
+__device__ __forceinline__ float sum_quarters(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return sum_halves(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+// 16 query rows per wave, 8 waves per workgroup (128 rows), on
+// v_mfma_f32_16x16x32_bf16: a wave's registers (about a hundred) allow four
+// waves per SIMD, so one wave's softmax, another's MFMAs and the copies
+// overlap.  Per 64-key tile: S^T = K Q^T as four 16-key blocks (lane l holds
+// keys 16 kb + 4 (l / 16) + i of query column l % 16), online softmax per
+// column (max and sum over the lane's 16 scores, then over lanes l ^ 16,
+// l ^ 32), O^T += V^T P^T per 32-key half with P^T's k-slot 8 (l / 16) + j
+// holding key 4 (l / 16) + j (j < 4) or 16 + 4 (l / 16) + j - 4 (j >= 4) of
+// the half: the lane's own scores, so P^T needs no exchange; the transposed V
+// reads put the same keys in the same k-slots.  Two LDS stages of K and V
+// tiles copied by DMA through buffer descriptors.
+template <int KVT, int D, bool PAGED>
+__global__ __launch_bounds__(512, 4) void prefill16_kernel(PrefillArgs a, int q_tiles) {
+  constexpr int W = 8;
+  constexpr bool F8 = KVT == kFP8;
+  static_assert(!F8 || (PAGED && D == 128), "fp8 caches: paged, head_dim 128");
+  using T = Tile<D, W>;              // bf16 tiles the MFMAs read
+  using TC = Tile<D, W, F8 ? 1 : 2>;  // tiles as copied from the cache
+  constexpr int BM = 16 * W;
+  constexpr int KS = D / 32;  // MFMA k-steps over head_dim
+  constexpr int DB = D / 16;  // 16-row blocks of O^T
   constexpr int GPW = T::groups_per_wave;
-  static_assert(S == 2 || S == 3, "stages");
-  // the tile buffers are separate objects, so the compiler can tell the DMA
-  // into one from the reads of another and waits only for the right one
-  __shared__ __attribute__((aligned(1024))) uint8_t k0b[T::bytes], v0b[T::bytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t k1b[T::bytes], v1b[T::bytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t k2b[S == 3 ? T::bytes : 16], v2b[S == 3 ? T::bytes : 16];
+  constexpr int kDma = TC::dma_per_wave;
+  constexpr int kWaitLgkm0 = 0xc07f;
+  static_assert(GPW == 1 && TC::groups_per_wave == 1, "one 8-key group per wave");
+  // copy targets (two stages); with fp8 caches, bf16 tiles dequantised from them
+  __shared__ __attribute__((aligned(1024))) uint8_t k0b[TC::bytes], v0b[TC::bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k1b[TC::bytes], v1b[TC::bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t kxb[F8 ? T::bytes : 16], vxb[F8 ? T::bytes : 16];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int half = lane >> 5, col = lane & 31;
+  const int col = lane & 15, grp4 = lane >> 4;
 
   WorkItem w;
   if (!work_item(blockIdx.x, q_tiles, a.batch, a.num_heads, a.num_kv_heads, w)) return;
@@ -727,116 +766,97 @@ __global__ __launch_bounds__(64 * W, 2) void prefill_dma_kernel(PrefillArgs a, i
   if (key_end < 0) key_end = 0;
   const int n_tiles = (key_end + kBN - 1) / kBN;
 
-  const int64_t row_stride = (int64_t)a.num_kv_heads * T::row_bytes;
-  const uint8_t* kbase = a.k + g * T::row_bytes + (PAGED ? 0 : (int64_t)k_start * row_stride);
-  const uint8_t* vbase = a.v + g * T::row_bytes + (PAGED ? 0 : (int64_t)k_start * row_stride);
+  const int64_t row_stride = (int64_t)a.num_kv_heads * TC::row_bytes;
+  const uint8_t* kbase = a.k + g * TC::row_bytes + (PAGED ? 0 : (int64_t)k_start * row_stride);
+  const uint8_t* vbase = a.v + g * TC::row_bytes + (PAGED ? 0 : (int64_t)k_start * row_stride);
   const int32_t* table = PAGED ? a.block_table + (int64_t)b * a.max_blocks_per_seq : nullptr;
   const int log2bs = PAGED ? __builtin_ctz(a.block_size) : 0;
 
-  // this wave's query column: row q0 + 32 * wave + col
-  const int qrow = q0 + wave * 32 + col;
+  // this lane's query column: row q0 + 16 * wave + col
+  const int qrow = q0 + wave * 16 + col;
   const bool qvalid = qrow < lq;
-  const bool wave_rows = q0 + wave * 32 < lq;  // the wave has a row to compute
+  const bool wave_rows = q0 + wave * 16 < lq;
   // The row max is taken over unscaled scores, which needs scale > 0: a
   // negative scale is applied as |scale| to -q (bf16 negation is exact), and
   // a zero scale as 1e-30 (every logit then rounds to exactly 0 in the
   // exponent, as with scale 0, while masked keys stay at -inf instead of
   // -inf * 0).
-  const uint32_t q_sign = a.softmax_scale < 0.0f ? 0x80008000u : 0u;
-  const float scale = fmaxf(fabsf(a.softmax_scale) * kLog2e, 1e-30f);
+  // With fp8 caches the K scale folds into the logit scale and the V scale
+  // into the output.
+  const float sc = F8 ? a.softmax_scale * a.k_scale[g] : a.softmax_scale;
+  const uint32_t q_sign = sc < 0.0f ? 0x80008000u : 0u;
+  const float scale = fmaxf(fabsf(sc) * kLog2e, 1e-30f);
+  // q[qrow][32 ks + 8 (lane / 16) .. + 8], as loaded (rows past the request
+  // read row 0); the sign and the zeroing of those rows are applied once the
+  // first tile has landed, so that the q loads and the first copy are in
+  // flight together
   uint4 qf[KS];
   {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         ((int64_t)(q_start + (qvalid ? qrow : 0)) * a.num_heads + h) * D + half * 8;
+                         ((int64_t)(q_start + (qvalid ? qrow : 0)) * a.num_heads + h) * D + grp4 * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 x = *reinterpret_cast<const uint4*>(qp + ks * 16);
-      qf[ks] = qvalid ? make_uint4(x.x ^ q_sign, x.y ^ q_sign, x.z ^ q_sign, x.w ^ q_sign)
-                      : make_uint4(0u, 0u, 0u, 0u);
-    }
-    // resolve the q loads before the first DMA: the tile loop then never has
-    // to wait for them behind a copy
-    __builtin_amdgcn_s_waitcnt(0x0f70);
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(qp + ks * 32);
   }
 
-  // per-lane LDS offsets (the swizzle depends on the row, known per lane)
-  // K: row kb*32 + col, piece 2*ks + half
+  // K A operand: row 16 kb + col, piece 4 ks + lane / 16
   int k_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_off[ks] = col * T::row_bytes + (((2 * ks + half) ^ swz<D>(col)) << 4);
-  // V (transposed reads): key kk*16 + 8x + key_l, element db*32 + dd_l .. +3
-  const int key_l = 4 * half + (lane & 15) / 4;
-  const int dd_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  int v_off[DB][2];
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = col * T::row_bytes + (((4 * ks + grp4) ^ kswz16<D>(col)) << 4);
+  // V transposed reads: lane group lane / 16 reads keys 4 (lane / 16) + (lane % 16) / 4 (and + 16),
+  // elements 16 db + 4 (lane % 4) .. + 3
+  int v_off[DB];
+  {
+    const int key = 4 * grp4 + col / 4;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int key = 8 * x + key_l;
-      const int dd = db * 32 + dd_l;
-      v_off[db][x] = key * T::row_bytes + (((dd >> 3) ^ swz<D>(key)) << 4) + (dd & 7) * 2;
+    for (int db = 0; db < DB; ++db) {
+      const int dd = 16 * db + 4 * (col & 3);
+      v_off[db] = key * T::row_bytes + (((dd >> 3) ^ vswz16<D>(key)) << 4) + (dd & 7) * 2;
     }
+  }
 
-  f32x16_t o[DB];
+  f32x4_t o[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
+  for (int db = 0; db < DB; ++db) o[db] = f32x4_t{};
   float m = kNegBig, l = 0.0f;
 
-  // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, lgkmcnt in 11:8)
-  constexpr int kDma = 2 * T::dma_per_wave;  // DMA instructions per tile per wave
-  constexpr int kWaitLgkm0 = 0xc07f;         // lgkmcnt(0) only
-
-  // One tile: scores, softmax, output update, reading buffers (kb_lds, vb_lds).
-  auto compute = [&](const uint8_t* kb_lds, const uint8_t* vb_lds, int key0, uint64_t valid,
-                     bool blocks_ok) __attribute__((always_inline)) {
-    // Key kt of the tile is visible to this lane's row iff kt < lim (sequence
-    // end, causal diagonal) and its 8-key group's block is valid.
+  auto compute = [&](const uint8_t* kb_lds, const uint8_t* vb_lds, int key0, uint64_t valid, bool blocks_ok)
+                     __attribute__((always_inline)) {
     const int lim = min(a.causal ? qrow + offset - key0 + 1 : kBN, lk - key0);
-    const int lim_first = min(a.causal ? q0 + wave * 32 + offset - key0 + 1 : kBN, lk - key0);
-    const int lim_last = min(a.causal ? q0 + wave * 32 + 32 + offset - key0 : kBN, lk - key0);
+    const int lim_first = min(a.causal ? q0 + wave * 16 + offset - key0 + 1 : kBN, lk - key0);
+    const int lim_last = min(a.causal ? q0 + wave * 16 + 16 + offset - key0 : kBN, lk - key0);
     if (!wave_rows || lim_last <= 0) return;  // nothing of this tile reaches the wave's rows
-    // S^T for two 32-key blocks, interleaved, next fragments read ahead
-    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
-    {
-      uint4 k0 = *reinterpret_cast<const uint4*>(kb_lds + k_off[0]);
-      uint4 k1 = *reinterpret_cast<const uint4*>(kb_lds + 32 * T::row_bytes + k_off[0]);
+    f32x4_t s[4];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        uint4 n0 = k0, n1 = k1;
-        if (ks + 1 < KS) {
-          n0 = *reinterpret_cast<const uint4*>(kb_lds + k_off[ks + 1]);
-          n1 = *reinterpret_cast<const uint4*>(kb_lds + 32 * T::row_bytes + k_off[ks + 1]);
-        }
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qf[ks]), s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qf[ks]), s[1], 0, 0, 0);
-        k0 = n0;
-        k1 = n1;
+    for (int kb = 0; kb < 4; ++kb) s[kb] = f32x4_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint4 kf = *reinterpret_cast<const uint4*>(kb_lds + kb * 16 * T::row_bytes + k_off[ks]);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), s[kb], 0, 0, 0);
       }
-    }
-    // mask (register r of block kb holds key kb*32 + 8*(r/4) + 4*half + r%4)
+    // mask (register i of block kb holds key 16 kb + 4 (lane / 16) + i)
     if (lim_first < kBN) {
-      const int lim_h = lim - 4 * half;  // kt - 4 * half is a constant per register
+      const int lim_g = lim - 4 * grp4;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kc = kb * 32 + 8 * (r >> 2) + (r & 3);
-          s[kb][r] = kc < lim_h ? s[kb][r] : -INFINITY;
-        }
+        for (int i = 0; i < 4; ++i) s[kb][i] = 16 * kb + i < lim_g ? s[kb][i] : -INFINITY;
     }
     if (!blocks_ok) {  // corrupt block table: skip the keys of invalid blocks
 #pragma unroll
-      for (int grp = 0; grp < 8; ++grp)
-        if (((valid >> (8 * grp)) & 0xffull) == 0)
+      for (int kb = 0; kb < 4; ++kb) {
+        const bool ok = ((valid >> (16 * kb + 4 * grp4)) & 0xfull) != 0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s[grp >> 2][4 * (grp & 3) + i] = -INFINITY;
+        for (int i = 0; i < 4; ++i) s[kb][i] = ok ? s[kb][i] : -INFINITY;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_halves(mx) * scale;
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = max_quarters(mx) * scale;
     // lazy running max: move it (and rescale) only when it grows by > 2^8
     if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleBits) != 0) {
       const float mn = fmaxf(m, mx);
@@ -847,134 +867,130 @@ __global__ __launch_bounds__(64 * W, 2) void prefill_dma_kernel(PrefillArgs a, i
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
     const float neg_m = -m;
-    uint4 pb[2][2];  // [key block][16-key half] bf16 B operands
     float ps = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x8_t pv;
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        f32x8_t pv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(s[kb][hs * 8 + e], scale, neg_m));
-        pb[kb][hs] = __builtin_bit_cast(uint4, __builtin_convertvector(pv, bf16x8_t));
-        // row sum of the bf16 values the MFMA uses: dot with (1, 1)
-        ps = dot2_bf16(pb[kb][hs].x, 0x3f803f80u, ps);
-        ps = dot2_bf16(pb[kb][hs].y, 0x3f803f80u, ps);
-        ps = dot2_bf16(pb[kb][hs].z, 0x3f803f80u, ps);
-        ps = dot2_bf16(pb[kb][hs].w, 0x3f803f80u, ps);
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = fast_exp2(fmaf(s[2 * hf][i], scale, neg_m));
+        pv[4 + i] = fast_exp2(fmaf(s[2 * hf + 1][i], scale, neg_m));
       }
+      const uint4 pb = __builtin_bit_cast(uint4, __builtin_convertvector(pv, bf16x8_t));
+      ps = dot2_bf16(pb.x, 0x3f803f80u, ps);
+      ps = dot2_bf16(pb.y, 0x3f803f80u, ps);
+      ps = dot2_bf16(pb.z, 0x3f803f80u, ps);
+      ps = dot2_bf16(pb.w, 0x3f803f80u, ps);
+      const uint8_t* vh = vb_lds + hf * 32 * T::row_bytes;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint2 lo = read_tr(vh + v_off[db]);
+        const uint2 hi = read_tr(vh + 16 * T::row_bytes + v_off[db]);
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)),
+                                                        as_bf16x8(pb), o[db], 0, 0, 0);
+      }
+    }
     l += ps;
-    // O^T += V^T P^T over the four 16-key groups
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint2 lo = read_tr(vb_lds + kk * 16 * T::row_bytes + v_off[db][0]);
-        const uint2 hi = read_tr(vb_lds + kk * 16 * T::row_bytes + v_off[db][1]);
-        const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pb[kk >> 1][kk & 1]),
-                                                        o[db], 0, 0, 0);
-      }
   };
 
-  // Tile maps and block-table entries run ahead of the copies: at step t,
-  // maps[i] is the map of tile t + i (i < S - 1, copies already issued) and
-  // ent holds the block-table entries of tile t + S - 1.
-  TileMap<GPW> maps[S - 1];
-  Entries ent;
-  // Every memory operation of a step is unconditional, so the compiler's
-  // wait counts stay exact; copies past the last tile re-read in-bounds rows
-  // into idle buffers and are drained before the workgroup ends.
-  auto next_copy = [&](uint8_t* kn, uint8_t* vn, int key0) __attribute__((always_inline)) {
-    TileMap<GPW> nw;
-    resolve<PAGED, GPW>(nw, a, ent, row_stride, key0 + (S - 1) * kBN, lk, log2bs, wave);
-    issue_tile<D, W, PAGED>(nw, kbase, vbase, row_stride, key0 + (S - 1) * kBN, lk, kn, vn, wave, lane);
-#pragma unroll
-    for (int i = 0; i + 2 < S; ++i) maps[i] = maps[i + 1];
-    maps[S - 2] = nw;
-  };
-  // S = 2: the copy of tile t + 1 goes out first, then tile t is waited for;
-  // a second barrier frees tile t's buffer for the copy of tile t + 2.
-  // S = 3: tile t is waited for, one barrier also frees the buffer of tile
-  // t - 1, which then takes the copy of tile t + 2.  The LDS reads of a tile
-  // all feed MFMAs, so they are complete when the tile's last MFMA issues and
-  // the closing barrier needs no wait of its own.
-  auto step = [&](uint8_t* kc, uint8_t* vc, uint8_t* kn, uint8_t* vn, int t) __attribute__((always_inline)) {
-    const int key0 = t * kBN;
-    const uint64_t valid = maps[0].valid;
-    const bool blocks_ok = maps[0].blocks_ok;
-    if constexpr (S == 2) next_copy(kn, vn, key0);
-    __builtin_amdgcn_s_waitcnt(0x0f70 | (S == 2 ? kDma : kDma));  // tile t has landed
-    zero_rows<D, W>(valid, vc, wave, lane);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-    if constexpr (S == 3) next_copy(kn, vn, key0);
-    compute(kc, vc, key0, valid, blocks_ok);
-    fetch_entries<PAGED>(ent, a, table, key0 + S * kBN, log2bs);
-    if constexpr (S == 2) __builtin_amdgcn_s_barrier();
-  };
+  // Two stages: the copy of tile t + 1 is in flight while tile t is computed.
+  // Copies are issued for tile indices clamped to the last tile, so every
+  // step issues the same memory operations and the wait counts stay exact.
   if (n_tiles > 0) {
-#pragma unroll
-    for (int i = 0; i + 1 < S; ++i) {
-      Entries e0;
-      fetch_entries<PAGED>(e0, a, table, i * kBN, log2bs);
-      resolve<PAGED, GPW>(maps[i], a, e0, row_stride, i * kBN, lk, log2bs, wave);
+    const int last = n_tiles - 1;
+    TileMap<GPW> mc, mn;  // maps of tiles t and t + 1
+    Entries ent;          // block-table entries of tile t + 2
+    {
+      Entries e;
+      fetch_entries<PAGED>(e, a, table, 0, log2bs);
+      resolve<PAGED, GPW>(mc, a, e, row_stride, 0, lk, log2bs, wave);
+      fetch_entries<PAGED>(e, a, table, min(1, last) * kBN, log2bs);
+      resolve<PAGED, GPW>(mn, a, e, row_stride, min(1, last) * kBN, lk, log2bs, wave);
+      fetch_entries<PAGED>(ent, a, table, min(2, last) * kBN, log2bs);
     }
-    fetch_entries<PAGED>(ent, a, table, (S - 1) * kBN, log2bs);
-    issue_tile<D, W, PAGED>(maps[0], kbase, vbase, row_stride, 0, lk, k0b, v0b, wave, lane);
-    if constexpr (S == 3)
-      issue_tile<D, W, PAGED>(maps[1], kbase, vbase, row_stride, kBN, lk, k1b, v1b, wave, lane);
-    for (int t = 0; t < n_tiles; t += S) {
-      if constexpr (S == 2) {
-        step(k0b, v0b, k1b, v1b, t);
-        if (t + 1 >= n_tiles) break;
-        step(k1b, v1b, k0b, v0b, t + 1);
+    constexpr int kSwK = F8 ? 0 : 1, kSwV = F8 ? 0 : 2, kE = F8 ? 1 : 2;
+    issue_rows<D, W, PAGED, kSwK, kE>(mc, kbase, row_stride, 0, lk, k0b, wave, lane);
+    issue_rows<D, W, PAGED, kSwV, kE>(mc, vbase, row_stride, 0, lk, v0b, wave, lane);
+    bool q_fresh = true;
+    auto step = [&](uint8_t* kc, uint8_t* vc, uint8_t* kn, uint8_t* vn, int t) __attribute__((always_inline)) {
+      // the copy of t + 1 into the other buffers (freed by the previous step's closing barrier)
+      issue_rows<D, W, PAGED, kSwK, kE>(mn, kbase, row_stride, min(t + 1, last) * kBN, lk, kn, wave, lane);
+      issue_rows<D, W, PAGED, kSwV, kE>(mn, vbase, row_stride, min(t + 1, last) * kBN, lk, vn, wave, lane);
+      __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * kDma));  // tile t (and the q rows) have landed
+      __builtin_amdgcn_sched_barrier(0);  // the compiler does not see the copies: keep LDS accesses below
+      if constexpr (F8) {
+        // this wave's 8 copied rows (one 16-code piece per lane) -> bf16
+        // tiles in the layouts the MFMA reads; V rows of keys that do not
+        // exist become zeros
+        const int r = wave * 8 + (lane >> 3), pc = lane & 7;
+        const uint4 k8 = *reinterpret_cast<const uint4*>(kc + r * TC::row_bytes + pc * 16);
+        const uint4 v8 = *reinterpret_cast<const uint4*>(vc + r * TC::row_bytes + pc * 16);
+        const bool ok = (mc.valid >> r) & 1ull;
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(kxb + r * T::row_bytes + (((2 * pc) ^ kswz16<D>(r)) << 4)) =
+            e4m3x8_to_bf16x8(k8.x, k8.y);
+        *reinterpret_cast<uint4*>(kxb + r * T::row_bytes + (((2 * pc + 1) ^ kswz16<D>(r)) << 4)) =
+            e4m3x8_to_bf16x8(k8.z, k8.w);
+        *reinterpret_cast<uint4*>(vxb + r * T::row_bytes + (((2 * pc) ^ vswz16<D>(r)) << 4)) =
+            ok ? e4m3x8_to_bf16x8(v8.x, v8.y) : z;
+        *reinterpret_cast<uint4*>(vxb + r * T::row_bytes + (((2 * pc + 1) ^ vswz16<D>(r)) << 4)) =
+            ok ? e4m3x8_to_bf16x8(v8.z, v8.w) : z;
       } else {
-        step(k0b, v0b, k2b, v2b, t);
-        if (t + 1 >= n_tiles) break;
-        step(k1b, v1b, k0b, v0b, t + 1);
-        if (t + 2 >= n_tiles) break;
-        step(k2b, v2b, k1b, v1b, t + 2);
+        zero_rows<D, W>(mc.valid, vc, wave, lane);
       }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+      if (q_fresh) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qf[ks] = qvalid ? make_uint4(qf[ks].x ^ q_sign, qf[ks].y ^ q_sign, qf[ks].z ^ q_sign, qf[ks].w ^ q_sign)
+                          : make_uint4(0u, 0u, 0u, 0u);
+        q_fresh = false;
+      }
+      if constexpr (F8) compute(kxb, vxb, t * kBN, mc.valid, mc.blocks_ok);
+      else compute(kc, vc, t * kBN, mc.valid, mc.blocks_ok);
+      mc = mn;
+      resolve<PAGED, GPW>(mn, a, ent, row_stride, min(t + 2, last) * kBN, lk, log2bs, wave);
+      fetch_entries<PAGED>(ent, a, table, min(t + 3, last) * kBN, log2bs);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();  // every wave is done with tile t's buffers
+      return t < last;
+    };
+    for (int t = 0;; t += 2) {
+      if (!step(k0b, v0b, k1b, v1b, t)) break;
+      if (!step(k1b, v1b, k0b, v0b, t + 1)) break;
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // copies past the last tile land before LDS is released
   }
 
-  // normalise and store: lane holds O^T rows 8*(r/4) + 4*half + r%4 of each 32-row block
-  l = sum_halves(l);
+  // normalise and store: lane holds O^T rows 16 db + 4 (lane / 16) + i of column col
+  l = sum_quarters(l);
   if (!qvalid) return;
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const float inv = l > 0.0f ? (F8 ? a.v_scale[g] : 1.0f) / l : 0.0f;
   uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q_start + qrow) * a.num_heads + h) * D;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d = db * 32 + rg * 8 + half * 4;
-      const uint32_t w0 = pack_bf16x2(o[db][rg * 4 + 0] * inv, o[db][rg * 4 + 1] * inv);
-      const uint32_t w1 = pack_bf16x2(o[db][rg * 4 + 2] * inv, o[db][rg * 4 + 3] * inv);
-      *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
-    }
+  for (int db = 0; db < DB; ++db) {
+    const uint32_t w0 = pack_bf16x2(o[db][0] * inv, o[db][1] * inv);
+    const uint32_t w1 = pack_bf16x2(o[db][2] * inv, o[db][3] * inv);
+    *reinterpret_cast<uint2*>(op + 16 * db + 4 * grp4) = make_uint2(w0, w1);
+  }
 }
 
-// The launch shape is fixed at compile time (PKV_PREFILL_WAVES, PKV_PREFILL_STAGES).
-template <int D, int W, int S>
-hipError_t launch_ws(const PrefillArgs& a, hipStream_t stream) {
-  const int q_tiles = (a.max_seqlen_q + 32 * W - 1) / (32 * W);
+template <int KVT, int D>
+hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
+  const int q_tiles = (a.max_seqlen_q + 127) / 128;
   const int64_t grid = work_grid(q_tiles, a.batch, a.num_heads, a.num_kv_heads);
   if (grid > 0x7fffffff / 2) return hipErrorInvalidValue;
-  if (a.block_table != nullptr) {
-    hipLaunchKernelGGL((prefill_dma_kernel<D, true, W, S>), dim3((unsigned)grid), dim3(64 * W), 0, stream, a,
+  if constexpr (KVT == kFP8) {
+    hipLaunchKernelGGL((prefill16_kernel<kFP8, D, true>), dim3((unsigned)grid), dim3(512), 0, stream, a, q_tiles);
+  } else if (a.block_table != nullptr) {
+    hipLaunchKernelGGL((prefill16_kernel<kBF16, D, true>), dim3((unsigned)grid), dim3(512), 0, stream, a,
                        q_tiles);
   } else {
-    hipLaunchKernelGGL((prefill_dma_kernel<D, false, W, S>), dim3((unsigned)grid), dim3(64 * W), 0, stream,
-                       a, q_tiles);
+    hipLaunchKernelGGL((prefill16_kernel<kBF16, D, false>), dim3((unsigned)grid), dim3(512), 0, stream, a,
+                       q_tiles);
   }
   return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
-  return launch_ws<D, PKV_PREFILL_WAVES, PKV_PREFILL_STAGES>(a, stream);
 }
 
 }  // namespace dma
@@ -1003,11 +1019,12 @@ hipError_t launch_varlen_prefill(const PrefillArgs& a, hipStream_t stream) {
     return launch_f32<128>(a, stream);
   }
   if (a.kv_dtype == kBF16) {
-    if (a.head_dim == 64) return dma::launch<64>(a, stream);
-    return dma::launch<128>(a, stream);
+    if (a.head_dim == 64) return dma::launch<kBF16, 64>(a, stream);
+    return dma::launch<kBF16, 128>(a, stream);
   }
+  // fp8 caches are paged (the entry point requires a block table)
   if (a.head_dim == 64) return launch_mfma<kFP8, 64>(a, stream);
-  return launch_mfma<kFP8, 128>(a, stream);
+  return dma::launch<kFP8, 128>(a, stream);
 }
 
 }  // namespace pkv
