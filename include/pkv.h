@@ -138,14 +138,19 @@ size_t pkv_paged_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t
  *   k_cache, v_cache of cache_dtype (F32 with F32 q; BF16 or FP8 with BF16 q).
  *   k_scale, v_scale [num_kv_heads] fp32, required iff FP8.
  *   block_table [batch, max_blocks_per_seq], row-major; entries past the
- *               sequence's last block are never read (may be -1).
- *   cache_seqlens [batch] keys per sequence (0 -> output row of zeros).
+ *               sequence's last block are never read (may be -1).  An entry
+ *               inside the sequence that is negative or >= num_blocks is read
+ *               as an empty block: its keys are left out of the softmax.
+ *   cache_seqlens [batch] keys per sequence (0 -> output row of zeros;
+ *               values above max_blocks_per_seq * block_size are clamped).
  * out[b, h] = sum_j softmax_j(scale * q[b,h] . k_j) v_j over the sequence's
  * keys j < cache_seqlens[b], with k_j, v_j read from KV head h / G (q heads
  * are grouped contiguously).
  *   split_keys  keys per work unit of the split-K plan: 0 = automatic, else a
  *               multiple of 128.  Long contexts are cut into units processed
  *               in parallel; a second kernel merges their partial results.
+ *               The automatic plan deals equal shares of 32-key chunks to a
+ *               persistent grid (batch <= 2048), else uses fixed splits.
  *   workspace   device scratch of at least pkv_paged_decode_workspace_size()
  *               bytes for the same arguments (NULL allowed when that is 0).
  *               Its contents on entry do not matter.

@@ -213,6 +213,48 @@ def test_block_permutation_gives_identical_bits():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("cache_dtype,split", [("bf16", 0), ("bf16", 128), ("fp8", 0)])
+def test_decode_bad_block_ids_read_as_empty_blocks(cache_dtype, split):
+    """A block id past the pool or negative inside a sequence's range: the
+    kernels stay in their buffers and leave that block's keys out (the method
+    defines no result for it; the library documents this behaviour).  Expected
+    values: the oracle's attention over the remaining keys."""
+    step = workloads.config("llama8b_decode", batch=3, len_lo=100, len_hi=300, cache_dtype=cache_dtype)
+    say("bad block ids", cache_dtype, split)
+    g = GpuStep(step)
+    g.write()
+    kc, vc = oracle_write(step)
+    d = step.decode_inputs()
+    bt = d["block_table"].copy()
+    bs, hkv, hd = step.block_size, step.num_kv_heads, step.head_dim
+    bt[1, 1] = step.num_blocks + 7
+    bt[2, 0] = -1
+    g.dec_bt = to_dev(bt, "i32")
+    out = out_f64(g.decode(split))
+    q64 = paged.to_f64(d["q"], step.q_dtype)
+    want = np.zeros_like(out)
+    for b in range(3):
+        lk = int(d["cache_seqlens"][b])
+        keys = [j for j in range(lk) if 0 <= bt[b, j // bs] < step.num_blocks]
+        slots = np.array([bt[b, j // bs] * bs + j % bs for j in keys], dtype=np.int64)
+        k_rows = kc.reshape(-1, hkv, hd)[slots]
+        v_rows = vc.reshape(-1, hkv, hd)[slots]
+        k64 = np.stack([paged._rows_to_f64(k_rows[:, gi:gi + 1], cache_dtype, step.k_scale, gi)[:, 0]
+                        for gi in range(hkv)], axis=1)
+        v64 = np.stack([paged._rows_to_f64(v_rows[:, gi:gi + 1], cache_dtype, step.v_scale, gi)[:, 0]
+                        for gi in range(hkv)], axis=1)
+        want[b] = paged.attention(q64[b][None], k64, v64, step.scale, True)[0]
+    assert max_err(out, want) <= TOL[cache_dtype]
+
+
+def test_decode_batch_past_the_stream_table():
+    """More sequences than the stream plan's LDS chunk table holds: the
+    library takes the fixed-split plan (vector kernels)."""
+    step = workloads.config("llama8b_decode", batch=2100, len_lo=1, len_hi=40)
+    rng = np.random.default_rng(31)
+    run_step_and_check(step, full=False, pairs=sample_pairs(rng, 2100, step.num_heads, 300))
+
+
 # ---------------------------------------------------------------------------
 # prefill: the page-2 example, shapes, non-causal
 # ---------------------------------------------------------------------------
