@@ -10,10 +10,11 @@
 // のを速く": tiles stay on chip and the result equals plain attention.
 //
 // Main kernel (prefill16_kernel; bf16 caches, and paged fp8 caches at
-// head_dim 128): 128 query rows of one (request, q head) per workgroup, 8
-// waves x 16 rows on v_mfma_f32_16x16x32_bf16, four waves per SIMD; K and V
-// tiles copied HBM -> LDS by DMA (buffer loads with the lds bit, 1 KiB per
-// wave instruction, no registers), two stages.  Details at the kernel.
+// head_dim 128): 128 query rows of one (request, q head) per workgroup, 4
+// waves x 32 rows (two 16-column blocks) on v_mfma_f32_16x16x32_bf16, two
+// waves per SIMD; K and V tiles copied HBM -> LDS by DMA (buffer loads with
+// the lds bit, 1 KiB per wave instruction, no registers), two stages.
+// Details at the kernel.
 //
 // Register-staged kernel (prefill_kernel; fp8 caches at head_dim 64), on
 // v_mfma_f32_32x32x16_bf16:
@@ -40,6 +41,13 @@
 
 #include "pkv_device.hpp"
 #include "pkv_internal.h"
+
+#ifndef PKV_PREFILL_CB
+#define PKV_PREFILL_CB 2  // 16-row column blocks per wave (1 or 2)
+#endif
+#ifndef PKV_PREFILL_QK_SCHED
+#define PKV_PREFILL_QK_SCHED 1
+#endif
 
 namespace pkv {
 namespace {
@@ -706,31 +714,34 @@ __device__ __forceinline__ float sum_quarters(float x) {
   return sum_halves(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
-// 16 query rows per wave, 8 waves per workgroup (128 rows), on
-// v_mfma_f32_16x16x32_bf16: a wave's registers (about a hundred) allow four
-// waves per SIMD, so one wave's softmax, another's MFMAs and the copies
-// overlap.  Per 64-key tile: S^T = K Q^T as four 16-key blocks (lane l holds
-// keys 16 kb + 4 (l / 16) + i of query column l % 16), online softmax per
-// column (max and sum over the lane's 16 scores, then over lanes l ^ 16,
-// l ^ 32), O^T += V^T P^T per 32-key half with P^T's k-slot 8 (l / 16) + j
-// holding key 4 (l / 16) + j (j < 4) or 16 + 4 (l / 16) + j - 4 (j >= 4) of
-// the half: the lane's own scores, so P^T needs no exchange; the transposed V
+// 16 or 32 query rows per wave (CB = 1 or 2 column blocks of 16), 128 rows
+// per workgroup, on v_mfma_f32_16x16x32_bf16.  With CB = 1 a wave's
+// registers (about a hundred) allow four waves per SIMD; with CB = 2 each K
+// and V fragment read from LDS feeds two MFMAs (one per column block), which
+// halves the LDS reads per flop, at two waves per SIMD.  Per 64-key tile and
+// column block: S^T = K Q^T as four 16-key blocks (lane l holds keys
+// 16 kb + 4 (l / 16) + i of query column l % 16), online softmax per column
+// (max and sum over the lane's 16 scores, then over lanes l ^ 16, l ^ 32),
+// O^T += V^T P^T per 32-key half with P^T's k-slot 8 (l / 16) + j holding
+// key 4 (l / 16) + j (j < 4) or 16 + 4 (l / 16) + j - 4 (j >= 4) of the
+// half: the lane's own scores, so P^T needs no exchange; the transposed V
 // reads put the same keys in the same k-slots.  Two LDS stages of K and V
 // tiles copied by DMA through buffer descriptors.
-template <int KVT, int D, bool PAGED>
-__global__ __launch_bounds__(512, 4) void prefill16_kernel(PrefillArgs a, int q_tiles) {
-  constexpr int W = 8;
+template <int KVT, int D, bool PAGED, int CB>
+__global__ __launch_bounds__(512 / CB, 4 / CB) void prefill16_kernel(PrefillArgs a, int q_tiles) {
+  constexpr int W = 8 / CB;
   constexpr bool F8 = KVT == kFP8;
+  static_assert(CB == 1 || CB == 2, "one or two column blocks per wave");
   static_assert(!F8 || (PAGED && D == 128), "fp8 caches: paged, head_dim 128");
   using T = Tile<D, W>;              // bf16 tiles the MFMAs read
   using TC = Tile<D, W, F8 ? 1 : 2>;  // tiles as copied from the cache
-  constexpr int BM = 16 * W;
+  constexpr int BM = 16 * CB * W;
   constexpr int KS = D / 32;  // MFMA k-steps over head_dim
   constexpr int DB = D / 16;  // 16-row blocks of O^T
   constexpr int GPW = T::groups_per_wave;
   constexpr int kDma = TC::dma_per_wave;
   constexpr int kWaitLgkm0 = 0xc07f;
-  static_assert(GPW == 1 && TC::groups_per_wave == 1, "one 8-key group per wave");
+  static_assert(BM == 128 && GPW == CB && TC::groups_per_wave == GPW, "8-key groups per wave");
   // copy targets (two stages); with fp8 caches, bf16 tiles dequantised from them
   __shared__ __attribute__((aligned(1024))) uint8_t k0b[TC::bytes], v0b[TC::bytes];
   __shared__ __attribute__((aligned(1024))) uint8_t k1b[TC::bytes], v1b[TC::bytes];
@@ -772,10 +783,16 @@ __global__ __launch_bounds__(512, 4) void prefill16_kernel(PrefillArgs a, int q_
   const int32_t* table = PAGED ? a.block_table + (int64_t)b * a.max_blocks_per_seq : nullptr;
   const int log2bs = PAGED ? __builtin_ctz(a.block_size) : 0;
 
-  // this lane's query column: row q0 + 16 * wave + col
-  const int qrow = q0 + wave * 16 + col;
-  const bool qvalid = qrow < lq;
-  const bool wave_rows = q0 + wave * 16 < lq;
+  // this lane's query column in column block cb: row q0 + 16 (CB wave + cb) + col
+  const int wrow0 = q0 + 16 * CB * wave;  // the wave's first row
+  int qrow[CB];
+  bool qvalid[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    qrow[cb] = wrow0 + 16 * cb + col;
+    qvalid[cb] = qrow[cb] < lq;
+  }
+  const bool wave_rows = wrow0 < lq;
   // The row max is taken over unscaled scores, which needs scale > 0: a
   // negative scale is applied as |scale| to -q (bf16 negation is exact), and
   // a zero scale as 1e-30 (every logit then rounds to exactly 0 in the
@@ -790,12 +807,13 @@ __global__ __launch_bounds__(512, 4) void prefill16_kernel(PrefillArgs a, int q_
   // read row 0); the sign and the zeroing of those rows are applied once the
   // first tile has landed, so that the q loads and the first copy are in
   // flight together
-  uint4 qf[KS];
-  {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         ((int64_t)(q_start + (qvalid ? qrow : 0)) * a.num_heads + h) * D + grp4 * 8;
+  uint4 qf[CB][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(qp + ks * 32);
+  for (int cb = 0; cb < CB; ++cb) {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((int64_t)(q_start + (qvalid[cb] ? qrow[cb] : 0)) * a.num_heads + h) * D + grp4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[cb][ks] = *reinterpret_cast<const uint4*>(qp + ks * 32);
   }
 
   // K A operand: row 16 kb + col, piece 4 ks + lane / 16
@@ -814,83 +832,129 @@ __global__ __launch_bounds__(512, 4) void prefill16_kernel(PrefillArgs a, int q_
     }
   }
 
-  f32x4_t o[DB];
+  f32x4_t o[CB][DB];
+  float m[CB], l[CB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x4_t{};
-  float m = kNegBig, l = 0.0f;
+  for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[cb][db] = f32x4_t{};
+    m[cb] = kNegBig;
+    l[cb] = 0.0f;
+  }
 
   auto compute = [&](const uint8_t* kb_lds, const uint8_t* vb_lds, int key0, uint64_t valid, bool blocks_ok)
                      __attribute__((always_inline)) {
-    const int lim = min(a.causal ? qrow + offset - key0 + 1 : kBN, lk - key0);
-    const int lim_first = min(a.causal ? q0 + wave * 16 + offset - key0 + 1 : kBN, lk - key0);
-    const int lim_last = min(a.causal ? q0 + wave * 16 + 16 + offset - key0 : kBN, lk - key0);
+    const int lim_first = min(a.causal ? wrow0 + offset - key0 + 1 : kBN, lk - key0);
+    const int lim_last = min(a.causal ? wrow0 + 16 * CB + offset - key0 : kBN, lk - key0);
     if (!wave_rows || lim_last <= 0) return;  // nothing of this tile reaches the wave's rows
-    f32x4_t s[4];
+    f32x4_t s[CB][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) s[kb] = f32x4_t{};
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+      for (int kb = 0; kb < 4; ++kb) s[cb][kb] = f32x4_t{};
+    // K fragments one k-step ahead: the four reads of step ks + 1 are in
+    // flight during the 4 CB MFMAs of step ks
+    uint4 kf[2][4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const uint4 kf = *reinterpret_cast<const uint4*>(kb_lds + kb * 16 * T::row_bytes + k_off[ks]);
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), s[kb], 0, 0, 0);
+    for (int kb = 0; kb < 4; ++kb)
+      kf[0][kb] = *reinterpret_cast<const uint4*>(kb_lds + kb * 16 * T::row_bytes + k_off[0]);
+#if PKV_PREFILL_QK_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the first step's reads
+#endif
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          kf[(ks + 1) & 1][kb] = *reinterpret_cast<const uint4*>(kb_lds + kb * 16 * T::row_bytes + k_off[ks + 1]);
       }
-    // mask (register i of block kb holds key 16 kb + 4 (lane / 16) + i)
-    if (lim_first < kBN) {
-      const int lim_g = lim - 4 * grp4;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[kb][i] = 16 * kb + i < lim_g ? s[kb][i] : -INFINITY;
+        for (int cb = 0; cb < CB; ++cb)
+          s[cb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[ks & 1][kb]), as_bf16x8(qf[cb][ks]),
+                                                              s[cb][kb], 0, 0, 0);
+#if PKV_PREFILL_QK_SCHED
+      if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the next step's reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * CB, 0);             // then this step's MFMAs
+#endif
+    }
+    // mask (register i of block kb holds key 16 kb + 4 (lane / 16) + i)
+    if (lim_first < kBN) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int lim = min(a.causal ? qrow[cb] + offset - key0 + 1 : kBN, lk - key0);
+        const int lim_g = lim - 4 * grp4;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[cb][kb][i] = 16 * kb + i < lim_g ? s[cb][kb][i] : -INFINITY;
+      }
     }
     if (!blocks_ok) {  // corrupt block table: skip the keys of invalid blocks
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const bool ok = ((valid >> (16 * kb + 4 * grp4)) & 0xfull) != 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[kb][i] = ok ? s[kb][i] : -INFINITY;
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[cb][kb][i] = ok ? s[cb][kb][i] : -INFINITY;
       }
     }
-    float mx = -INFINITY;
+    float mx[CB];
+    bool grow = false;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int cb = 0; cb < CB; ++cb) {
+      float x = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = max_quarters(mx) * scale;
-    // lazy running max: move it (and rescale) only when it grows by > 2^8
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleBits) != 0) {
-      const float mn = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - mn);
-      m = mn;
-      l *= alpha;
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        for (int i = 0; i < 4; ++i) x = fmaxf(x, s[cb][kb][i]);
+      mx[cb] = max_quarters(x) * scale;
+      grow = grow || mx[cb] > m[cb] + kRescaleBits;
     }
-    const float neg_m = -m;
-    float ps = 0.0f;
+    // lazy running max: move it (and rescale) only when it grows by > 2^8
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const float mn = fmaxf(m[cb], mx[cb]);
+        const float alpha = fast_exp2(m[cb] - mn);
+        m[cb] = mn;
+        l[cb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[cb][db] *= alpha;
+      }
+    }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      f32x8_t pv;
+      uint4 pb[CB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = fast_exp2(fmaf(s[2 * hf][i], scale, neg_m));
-        pv[4 + i] = fast_exp2(fmaf(s[2 * hf + 1][i], scale, neg_m));
+      for (int cb = 0; cb < CB; ++cb) {
+        const float neg_m = -m[cb];
+        f32x8_t pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = fast_exp2(fmaf(s[cb][2 * hf][i], scale, neg_m));
+          pv[4 + i] = fast_exp2(fmaf(s[cb][2 * hf + 1][i], scale, neg_m));
+        }
+        pb[cb] = __builtin_bit_cast(uint4, __builtin_convertvector(pv, bf16x8_t));
+        float ps = l[cb];
+        ps = dot2_bf16(pb[cb].x, 0x3f803f80u, ps);
+        ps = dot2_bf16(pb[cb].y, 0x3f803f80u, ps);
+        ps = dot2_bf16(pb[cb].z, 0x3f803f80u, ps);
+        l[cb] = dot2_bf16(pb[cb].w, 0x3f803f80u, ps);
       }
-      const uint4 pb = __builtin_bit_cast(uint4, __builtin_convertvector(pv, bf16x8_t));
-      ps = dot2_bf16(pb.x, 0x3f803f80u, ps);
-      ps = dot2_bf16(pb.y, 0x3f803f80u, ps);
-      ps = dot2_bf16(pb.z, 0x3f803f80u, ps);
-      ps = dot2_bf16(pb.w, 0x3f803f80u, ps);
       const uint8_t* vh = vb_lds + hf * 32 * T::row_bytes;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const uint2 lo = read_tr(vh + v_off[db]);
         const uint2 hi = read_tr(vh + 16 * T::row_bytes + v_off[db]);
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)),
-                                                        as_bf16x8(pb), o[db], 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          o[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)),
+                                                              as_bf16x8(pb[cb]), o[cb][db], 0, 0, 0);
       }
     }
-    l += ps;
   };
 
   // Two stages: the copy of tile t + 1 is in flight while tile t is computed.
@@ -919,22 +983,25 @@ __global__ __launch_bounds__(512, 4) void prefill16_kernel(PrefillArgs a, int q_
       __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * kDma));  // tile t (and the q rows) have landed
       __builtin_amdgcn_sched_barrier(0);  // the compiler does not see the copies: keep LDS accesses below
       if constexpr (F8) {
-        // this wave's 8 copied rows (one 16-code piece per lane) -> bf16
-        // tiles in the layouts the MFMA reads; V rows of keys that do not
-        // exist become zeros
-        const int r = wave * 8 + (lane >> 3), pc = lane & 7;
-        const uint4 k8 = *reinterpret_cast<const uint4*>(kc + r * TC::row_bytes + pc * 16);
-        const uint4 v8 = *reinterpret_cast<const uint4*>(vc + r * TC::row_bytes + pc * 16);
-        const bool ok = (mc.valid >> r) & 1ull;
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(kxb + r * T::row_bytes + (((2 * pc) ^ kswz16<D>(r)) << 4)) =
-            e4m3x8_to_bf16x8(k8.x, k8.y);
-        *reinterpret_cast<uint4*>(kxb + r * T::row_bytes + (((2 * pc + 1) ^ kswz16<D>(r)) << 4)) =
-            e4m3x8_to_bf16x8(k8.z, k8.w);
-        *reinterpret_cast<uint4*>(vxb + r * T::row_bytes + (((2 * pc) ^ vswz16<D>(r)) << 4)) =
-            ok ? e4m3x8_to_bf16x8(v8.x, v8.y) : z;
-        *reinterpret_cast<uint4*>(vxb + r * T::row_bytes + (((2 * pc + 1) ^ vswz16<D>(r)) << 4)) =
-            ok ? e4m3x8_to_bf16x8(v8.z, v8.w) : z;
+        // this wave's copied rows (8 per pass, one 16-code piece per lane)
+        // -> bf16 tiles in the layouts the MFMA reads; V rows of keys that
+        // do not exist become zeros
+#pragma unroll
+        for (int x = 0; x < GPW; ++x) {
+          const int r = (wave * GPW + x) * 8 + (lane >> 3), pc = lane & 7;
+          const uint4 k8 = *reinterpret_cast<const uint4*>(kc + r * TC::row_bytes + pc * 16);
+          const uint4 v8 = *reinterpret_cast<const uint4*>(vc + r * TC::row_bytes + pc * 16);
+          const bool ok = (mc.valid >> r) & 1ull;
+          const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+          *reinterpret_cast<uint4*>(kxb + r * T::row_bytes + (((2 * pc) ^ kswz16<D>(r)) << 4)) =
+              e4m3x8_to_bf16x8(k8.x, k8.y);
+          *reinterpret_cast<uint4*>(kxb + r * T::row_bytes + (((2 * pc + 1) ^ kswz16<D>(r)) << 4)) =
+              e4m3x8_to_bf16x8(k8.z, k8.w);
+          *reinterpret_cast<uint4*>(vxb + r * T::row_bytes + (((2 * pc) ^ vswz16<D>(r)) << 4)) =
+              ok ? e4m3x8_to_bf16x8(v8.x, v8.y) : z;
+          *reinterpret_cast<uint4*>(vxb + r * T::row_bytes + (((2 * pc + 1) ^ vswz16<D>(r)) << 4)) =
+              ok ? e4m3x8_to_bf16x8(v8.z, v8.w) : z;
+        }
       } else {
         zero_rows<D, W>(mc.valid, vc, wave, lane);
       }
@@ -942,9 +1009,12 @@ __global__ __launch_bounds__(512, 4) void prefill16_kernel(PrefillArgs a, int q_
       __builtin_amdgcn_s_barrier();
       if (q_fresh) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          qf[ks] = qvalid ? make_uint4(qf[ks].x ^ q_sign, qf[ks].y ^ q_sign, qf[ks].z ^ q_sign, qf[ks].w ^ q_sign)
-                          : make_uint4(0u, 0u, 0u, 0u);
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            qf[cb][ks] = qvalid[cb] ? make_uint4(qf[cb][ks].x ^ q_sign, qf[cb][ks].y ^ q_sign,
+                                                 qf[cb][ks].z ^ q_sign, qf[cb][ks].w ^ q_sign)
+                                    : make_uint4(0u, 0u, 0u, 0u);
         q_fresh = false;
       }
       if constexpr (F8) compute(kxb, vxb, t * kBN, mc.valid, mc.blocks_ok);
@@ -963,16 +1033,19 @@ __global__ __launch_bounds__(512, 4) void prefill16_kernel(PrefillArgs a, int q_
     __builtin_amdgcn_s_waitcnt(0x0f70);  // copies past the last tile land before LDS is released
   }
 
-  // normalise and store: lane holds O^T rows 16 db + 4 (lane / 16) + i of column col
-  l = sum_quarters(l);
-  if (!qvalid) return;
-  const float inv = l > 0.0f ? (F8 ? a.v_scale[g] : 1.0f) / l : 0.0f;
-  uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q_start + qrow) * a.num_heads + h) * D;
+  // normalise and store: lane holds O^T rows 16 db + 4 (lane / 16) + i of its column
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const uint32_t w0 = pack_bf16x2(o[db][0] * inv, o[db][1] * inv);
-    const uint32_t w1 = pack_bf16x2(o[db][2] * inv, o[db][3] * inv);
-    *reinterpret_cast<uint2*>(op + 16 * db + 4 * grp4) = make_uint2(w0, w1);
+  for (int cb = 0; cb < CB; ++cb) {
+    const float lt = sum_quarters(l[cb]);
+    if (!qvalid[cb]) continue;
+    const float inv = lt > 0.0f ? (F8 ? a.v_scale[g] : 1.0f) / lt : 0.0f;
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q_start + qrow[cb]) * a.num_heads + h) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint32_t w0 = pack_bf16x2(o[cb][db][0] * inv, o[cb][db][1] * inv);
+      const uint32_t w1 = pack_bf16x2(o[cb][db][2] * inv, o[cb][db][3] * inv);
+      *reinterpret_cast<uint2*>(op + 16 * db + 4 * grp4) = make_uint2(w0, w1);
+    }
   }
 }
 
@@ -981,14 +1054,14 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const int q_tiles = (a.max_seqlen_q + 127) / 128;
   const int64_t grid = work_grid(q_tiles, a.batch, a.num_heads, a.num_kv_heads);
   if (grid > 0x7fffffff / 2) return hipErrorInvalidValue;
+  constexpr int CB = PKV_PREFILL_CB;
+  const dim3 block(512 / CB);
   if constexpr (KVT == kFP8) {
-    hipLaunchKernelGGL((prefill16_kernel<kFP8, D, true>), dim3((unsigned)grid), dim3(512), 0, stream, a, q_tiles);
+    hipLaunchKernelGGL((prefill16_kernel<kFP8, D, true, CB>), dim3((unsigned)grid), block, 0, stream, a, q_tiles);
   } else if (a.block_table != nullptr) {
-    hipLaunchKernelGGL((prefill16_kernel<kBF16, D, true>), dim3((unsigned)grid), dim3(512), 0, stream, a,
-                       q_tiles);
+    hipLaunchKernelGGL((prefill16_kernel<kBF16, D, true, CB>), dim3((unsigned)grid), block, 0, stream, a, q_tiles);
   } else {
-    hipLaunchKernelGGL((prefill16_kernel<kBF16, D, false>), dim3((unsigned)grid), dim3(512), 0, stream, a,
-                       q_tiles);
+    hipLaunchKernelGGL((prefill16_kernel<kBF16, D, false, CB>), dim3((unsigned)grid), block, 0, stream, a, q_tiles);
   }
   return hipGetLastError();
 }
