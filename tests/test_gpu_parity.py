@@ -176,6 +176,36 @@ def test_decode_shapes(hq, hkv, d, bs, dtype):
     run_step_and_check(step)
 
 
+@pytest.mark.parametrize("prefix,hq,hkv,cache", [
+    ([40000], 4, 1, "bf16"),           # one unit shared by every wave of the grid
+    ([3000, 4, 4, 4], 32, 8, "bf16"),  # fewer chunks than waves: one-chunk parts, waves without chunks
+    ([3000, 0, 17, 0], 32, 8, "fp8"),  # the same with one-key sequences (then empty ones) between
+])
+def test_decode_units_split_over_many_waves(prefix, hq, hkv, cache):
+    """Units whose partial results come from many waves of the persistent
+    grid (up to every wave), and waves that own no chunk at all."""
+    step = workloads.build_step("split_extremes", 91, num_heads=hq, num_kv_heads=hkv, head_dim=128,
+                                block_size=16, q_dtype="bf16", cache_dtype=cache, prefix=prefix,
+                                new=[1] * len(prefix), kinds=["decode"] * len(prefix))
+    g = run_step_and_check(step)
+    a = g.decode().cpu()
+    b = g.decode().cpu()
+    assert torch.equal(a, b), "run-to-run results differ"
+    if min(prefix) == 0:
+        # the one-key sequences become empty: their rows are zeros, the rest unchanged
+        d = step.decode_inputs()
+        lens = d["cache_seqlens"].copy()
+        lens[np.array(prefix) == 0] = 0
+        say("split extremes, empty sequences")
+        g.dec_len = to_dev(lens, "i32")
+        out = out_f64(g.decode())
+        kc, vc = oracle_write(step)
+        want = paged.paged_decode(d["q"], step.q_dtype, kc, vc, step.cache_dtype, d["block_table"], lens,
+                                  step.scale, step.k_scale, step.v_scale)
+        assert np.all(out[lens == 0] == 0)
+        assert max_err(out, want) <= TOL[cache]
+
+
 def test_decode_zero_length_sequence_gives_zeros():
     step = workloads.config("tiny_decode")
     g = GpuStep(step)
