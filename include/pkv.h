@@ -1,9 +1,11 @@
 /*
  * pkv.h -- C ABI of libpkv.so: attention over a paged KV cache on AMD MI355X
- * (gfx950).  Three operations, each one or two hand-written HIP kernels:
+ * (gfx950).  Hand-written HIP kernels behind four calls:
  *
  *   pkv_kv_cache_write   scatter the step's new K/V rows into cache slots
  *   pkv_paged_decode     one query per sequence over its cached keys
+ *   pkv_paged_decode_append  the same decode storing the step's new K/V rows
+ *                        itself (one launch for write + decode)
  *   pkv_varlen_prefill   causal attention for a packed batch of query chunks
  *
  * Page citations (titles as the pages give them):
@@ -167,6 +169,53 @@ int pkv_paged_decode(void* out, const void* q, int q_dtype,
                      int32_t block_size, int32_t num_blocks, float softmax_scale,
                      int32_t split_keys, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * pkv_paged_decode_append -- the decode step with its own cache write.
+ * [paged-doc] section デコードパス ("キャッシュの動作"): the decode kernel reads
+ * the paged cache through the block table and updates it in place; in the
+ * section's worked example cache_seqlens lists the keys cached BEFORE the
+ * step ([30, 32, 70]) and each new token goes to the next position of its
+ * sequence (so sequence 1's token opens its second block).
+ *
+ * For every sequence b with 0 <= cache_seqlens[b] < max_blocks_per_seq *
+ * block_size, the new rows k_new[b], v_new[b] are stored at position
+ * p = cache_seqlens[b], i.e. at slot block_table[b][p / block_size] *
+ * block_size + p % block_size (exactly the bytes pkv_kv_cache_write would
+ * store there, fp8 encoding included), and out[b] is the decode of q[b] over
+ * the p + 1 keys that include the new one.  The result equals
+ * pkv_kv_cache_write followed by pkv_paged_decode with cache_seqlens + 1, in
+ * one launch on the matrix-core plan (bf16 and fp8 caches, automatic split);
+ * other plans launch a small append kernel before the decode kernels.
+ *
+ *   k_new, v_new  [batch, num_kv_heads, head_dim] of q_dtype (the cache's
+ *                 element type for F32/BF16 caches; BF16 for FP8 caches),
+ *                 heads and dims contiguous, sequences k_new_stride /
+ *                 v_new_stride ELEMENTS apart (>= num_kv_heads * head_dim),
+ *                 16-byte aligned.
+ *   k_cache, v_cache  modified in place (one row per sequence and head).
+ *   cache_seqlens [batch] keys cached before this call.  A sequence whose
+ *                 position p is negative or past the block table stores
+ *                 nothing; its result is unspecified (memory-safe).  The block
+ *                 holding p must be allocated in block_table, and no two
+ *                 sequences may append to the same slot.
+ *   Every other argument, the workspace size
+ *   (pkv_paged_decode_workspace_size with the same geometry) and the errors
+ *   are those of pkv_paged_decode; also PKV_ERR_INVALID for NULL k_new/v_new
+ *   or a bad stride.  Under PKV_VALIDATE=1 the call also rejects sequences
+ *   without room for the new token and two appends to one slot.
+ */
+int pkv_paged_decode_append(void* out, const void* q, int q_dtype,
+                            const void* k_new, int64_t k_new_stride,
+                            const void* v_new, int64_t v_new_stride,
+                            void* k_cache, void* v_cache, int cache_dtype,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* cache_seqlens, int32_t batch,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, float softmax_scale,
+                            int32_t split_keys, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * pkv_varlen_prefill -- causal attention for a packed batch of query chunks.

@@ -272,6 +272,30 @@ def paged_decode(q, q_dtype, k_cache, v_cache, cache_dtype, block_table, cache_s
     return out
 
 
+def paged_decode_append(q, q_dtype, k_new, v_new, k_cache, v_cache, cache_dtype, block_table,
+                        cache_seqlens, scale, k_scale=None, v_scale=None, pairs=None):
+    """The decode step that stores its own token first.
+
+    [paged-doc] "デコードパス", "キャッシュの動作": the decode kernel updates the
+    paged cache in place; in the section's worked example ``cache_seqlens``
+    counts the keys cached before the step and each sequence's new token goes
+    to the next position (sequence 1, with 32 keys in blocks of 32, opens its
+    second block).  So: token b's rows go to slot ``slot_of(row b, L_b)``
+    with ``L_b = cache_seqlens[b]``, then the plain decode runs over
+    ``L_b + 1`` keys.
+
+    Returns ``(out, k_cache', v_cache')``.
+    """
+    lens = np.asarray(cache_seqlens, dtype=np.int64)
+    bs = k_cache.shape[1]
+    slots = np.array([slot_of(block_table[b], int(lens[b]), bs) for b in range(lens.shape[0])],
+                     dtype=np.int64)
+    kc, vc = kv_cache_write(k_new, v_new, k_cache, v_cache, slots, q_dtype, cache_dtype, k_scale, v_scale)
+    out = paged_decode(q, q_dtype, kc, vc, cache_dtype, block_table, lens + 1, scale, k_scale, v_scale,
+                       pairs=pairs)
+    return out, kc, vc
+
+
 def varlen_prefill(q, q_dtype, k, v, kv_dtype, cu_seqlens_q, cu_seqlens_k, scale, causal,
                    block_table=None, k_scale=None, v_scale=None, rows=None):
     """Variable-length batch of query chunks, one sequence after another.

@@ -11,6 +11,8 @@ Calls (same names as the C entry points without the ``pkv_`` prefix):
 
 * :func:`kv_cache_write` -- scatter new K/V rows into cache slots;
 * :func:`paged_decode`   -- one query per sequence through the block table;
+* :func:`paged_decode_append` -- the same decode storing the step's new K/V
+  rows itself (write + decode in one call);
 * :func:`varlen_prefill` -- causal attention for a packed batch of chunks.
 """
 
@@ -54,6 +56,10 @@ def _load_library():
     lib.pkv_paged_decode.restype = ctypes.c_int
     lib.pkv_paged_decode.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, i32, vp,
                                      i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.pkv_paged_decode_append.restype = ctypes.c_int
+    lib.pkv_paged_decode_append.argtypes = [vp, vp, ctypes.c_int, vp, i64, vp, i64, vp, vp, ctypes.c_int,
+                                            vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                                            vp, sz, vp]
     lib.pkv_varlen_prefill.restype = ctypes.c_int
     lib.pkv_varlen_prefill.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp,
                                        i32, i32, i32, f32, i32, vp, i32, i32, i32, i32, i32, i32,
@@ -151,6 +157,37 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale,
         _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens),
         b, hq, hkv, d, bs, nb, float(softmax_scale), int(split_keys), _ptr(workspace), ws_bytes,
         _stream(stream)))
+    return out
+
+
+def paged_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, softmax_scale,
+                        k_scale=None, v_scale=None, out=None, split_keys=0, workspace=None, stream=None):
+    """Store ``k_new[b]``/``v_new[b]`` ([B, Hkv, D]) at position ``cache_seqlens[b]`` of
+    sequence b, then decode q [B, Hq, D] over the ``cache_seqlens[b] + 1`` keys."""
+    import torch
+    _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B, Hq, D]")
+    _require(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+    _require(block_table.dim() == 2 and block_table.is_contiguous() and
+             block_table.dtype == torch.int32, "block_table must be contiguous int32 [B, max_blocks]")
+    _require(cache_seqlens.dtype == torch.int32, "cache_seqlens must be int32")
+    b, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    _require(k_new.dim() == 3 and tuple(k_new.shape) == (b, hkv, d) and v_new.shape == k_new.shape,
+             "k_new and v_new must be [B, Hkv, D]")
+    _require(k_new.dtype == q.dtype and v_new.dtype == q.dtype, "k_new and v_new must have q's dtype")
+    _require(k_new.stride(2) == 1 and k_new.stride(1) == d, "k_new heads/dims must be contiguous")
+    _require(v_new.stride(2) == 1 and v_new.stride(1) == d, "v_new heads/dims must be contiguous")
+    if out is None:
+        out = torch.empty_like(q)
+    need = paged_decode_workspace_size(b, hq, hkv, d, bs, block_table.shape[1], split_keys)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pkv_paged_decode_append(
+        _ptr(out), _ptr(q), _dtype_code(q), _ptr(k_new), k_new.stride(0), _ptr(v_new), v_new.stride(0),
+        _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), b, hq, hkv, d, bs, nb,
+        float(softmax_scale), int(split_keys), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 

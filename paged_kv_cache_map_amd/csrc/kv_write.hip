@@ -31,30 +31,7 @@ constexpr int kUnroll = 4;       // source pieces in flight per lane per pass
 constexpr int kWord3 = 0x00020000;
 constexpr int kDropped = 0x7ffffff0;  // a buffer offset past any row: the store is dropped
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-// 16 source bytes -> the cache's bytes for them (16, 8 or 4), as 4 words.
-template <int SRC, int DST>
-__device__ __forceinline__ u32x4_t convert_piece(uint4 x, float sc) {
-  u32x4_t o = {x.x, x.y, x.z, x.w};
-  if constexpr (SRC == kBF16 && DST == kFP8) {
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-    uint32_t out[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
-      out[e >> 2] |= f32_to_e4m3(v / sc) << ((e & 3) * 8);
-    }
-    o.x = out[0];
-    o.y = out[1];
-  } else if constexpr (SRC == kF32 && DST == kFP8) {
-    o.x = f32_to_e4m3(__uint_as_float(x.x) / sc) | (f32_to_e4m3(__uint_as_float(x.y) / sc) << 8) |
-          (f32_to_e4m3(__uint_as_float(x.z) / sc) << 16) |
-          (f32_to_e4m3(__uint_as_float(x.w) / sc) << 24);
-  }
-  return o;
-}
 
 template <int SRC, int DST>
 __device__ __forceinline__ void store_piece(__amdgpu_buffer_rsrc_t r, int off, u32x4_t v) {

@@ -113,7 +113,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows8(const uint8_t* base, int
   return __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), 0, 8 * stride, kBufferWord3);
 }
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // A chunk's keys come as two 16-key sub-steps, each made of two 8-key row
@@ -403,9 +402,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int split_key
   __shared__ float red_l[kWaves][GW];
 
   const int log2bs = __builtin_ctz(a.block_size);
-  int lk = a.cache_seqlens[b];
   const int cap = a.max_blocks_per_seq * a.block_size;
-  lk = lk < 0 ? 0 : (lk > cap ? cap : lk);
+  const int lk = clamp_keys(a.cache_seqlens[b], a.len_bias, cap);
   const int start = split * split_keys;
   if (split > 0 && start >= lk) return;  // nothing to do for this split
   const int end = min(lk, start + split_keys);
@@ -548,9 +546,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int split_keys
   const int hq = a.num_heads;
   if (bh >= (int64_t)a.batch * hq) return;
   const int b = (int)(bh / hq);
-  int lk = a.cache_seqlens[b];
   const int cap = a.max_blocks_per_seq * a.block_size;
-  lk = lk < 0 ? 0 : (lk > cap ? cap : lk);
+  const int lk = clamp_keys(a.cache_seqlens[b], a.len_bias, cap);
   const int ns = (lk + split_keys - 1) / split_keys;
   if (ns <= 1) return;  // the decode kernel wrote this row already
   const float* ws_o = a.workspace + bh * num_splits * D;
@@ -593,8 +590,7 @@ __device__ __forceinline__ void build_prefix(int32_t* pre, int32_t* part, const 
   for (int i = 0; i < per; ++i) {
     const int b = b0 + i;
     if (b < B) {
-      int lk = a.cache_seqlens[b];
-      lk = lk < 0 ? 0 : (lk > cap ? cap : lk);
+      const int lk = clamp_keys(a.cache_seqlens[b], a.len_bias, cap);
       sum += ((lk + kChunk - 1) / kChunk) * units_per_seq;
     }
   }
@@ -612,8 +608,7 @@ __device__ __forceinline__ void build_prefix(int32_t* pre, int32_t* part, const 
     const int b = b0 + i;
     if (b < B) {
       pre[b] = run;
-      int lk = a.cache_seqlens[b];
-      lk = lk < 0 ? 0 : (lk > cap ? cap : lk);
+      const int lk = clamp_keys(a.cache_seqlens[b], a.len_bias, cap);
       run += ((lk + kChunk - 1) / kChunk) * units_per_seq;
     }
   }
@@ -671,12 +666,12 @@ struct StreamCtx {
   const int32_t* seqlens;
   int64_t block_bytes;
   int slot_stride, row_bytes, max_blocks, num_blocks, log2bs, bs, cap, heads_per_kv, head_groups;
+  int len_bias;  // added to cache_seqlens (1 when the call appends the step's token)
   uint32_t k_off, v_off;
 };
 
 __device__ __forceinline__ int seq_len(const StreamCtx& c, int b) {
-  const int lk = c.seqlens[b];
-  return lk < 0 ? 0 : (lk > c.cap ? c.cap : lk);
+  return clamp_keys(c.seqlens[b], c.len_bias, c.cap);
 }
 
 // Block ids of the four 8-key row groups of chunk p (lane j holds group j & 3).
@@ -814,6 +809,7 @@ __global__ __launch_bounds__(kStreamThreads) void decode_stream_kernel(DecodeArg
   c.v_cache = a.v_cache;
   c.block_table = a.block_table;
   c.seqlens = a.cache_seqlens;
+  c.len_bias = a.len_bias;
   c.row_bytes = C::row_bytes;
   c.slot_stride = a.num_kv_heads * C::row_bytes;
   c.block_bytes = (int64_t)a.block_size * c.slot_stride;
@@ -969,6 +965,79 @@ __global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs
   for (int e = 0; e < NV; ++e) store_out<QT>(a.out, bh * D + lane * NV + e, O[e] * inv);
 }
 
+// ---------------------------------------------------------------------------
+// Appending decode.  [paged-doc] section デコードパス (キャッシュの動作): the
+// decode kernel indexes the paged cache through the block table and updates
+// it in place; the worked example stores the new token of a sequence with
+// cache_seqlens[b] cached keys at position cache_seqlens[b].  The append call
+// takes the step's new K/V rows, stores each at that position (slot
+// block_table[b][pos / bs] * bs + pos % bs) and attends cache_seqlens[b] + 1
+// keys, so the write needs no launch of its own.
+// ---------------------------------------------------------------------------
+
+// Store the new K and V rows of KV head g of sequence b.  Lanes [0, P) move
+// the 16-byte source pieces of K, lanes [P, 2 P) those of V (P pieces per
+// head row, at most 32).  Nothing is stored when the position lies past the
+// block table or in an invalid block (bad metadata; memory-safe).
+template <int SRC, int DST, int D>
+__device__ __forceinline__ void append_head(const DecodeArgs& a, int b, int g, int lane) {
+  constexpr int src_row = D * Elt<SRC>::bytes;
+  constexpr int dst_row = D * Elt<DST>::bytes;
+  constexpr int P = src_row / 16;
+  constexpr int dst_piece = 16 * Elt<DST>::bytes / Elt<SRC>::bytes;  // cache bytes per source piece
+  static_assert(2 * P <= 64, "one wave moves a head's K and V rows");
+  const int pos = a.cache_seqlens[b];
+  const int cap = a.max_blocks_per_seq * a.block_size;
+  if (pos < 0 || pos >= cap) return;
+  const int blk = a.block_table[(int64_t)b * a.max_blocks_per_seq + (pos >> __builtin_ctz(a.block_size))];
+  if (blk < 0 || blk >= a.num_blocks || lane >= 2 * P) return;
+  const bool is_v = lane >= P;
+  const int pc = is_v ? lane - P : lane;
+  const uint8_t* src = (is_v ? a.v_new + (int64_t)b * a.v_new_stride : a.k_new + (int64_t)b * a.k_new_stride) +
+                       g * src_row + pc * 16;
+  const uint4 x = *reinterpret_cast<const uint4*>(src);
+  float sc = 1.0f;
+  if constexpr (DST == kFP8) sc = (is_v ? a.v_scale : a.k_scale)[g];
+  const u32x4_t v = convert_piece<SRC, DST>(x, sc);
+  const int64_t slot = (int64_t)blk * a.block_size + (pos & (a.block_size - 1));
+  // the caches are the caller's writable buffers (the decode kernels only read them)
+  uint8_t* dst = const_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) +
+                 slot * ((int64_t)a.num_kv_heads * dst_row) + g * dst_row + pc * dst_piece;
+  if constexpr (dst_piece == 16) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(v.x, v.y, v.z, v.w);
+  } else if constexpr (dst_piece == 8) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
+  } else {
+    *reinterpret_cast<uint32_t*>(dst) = v.x;
+  }
+}
+
+// The append on its own (plans other than the matrix-core stream-K kernel):
+// one wave per (sequence, KV head); the decode kernels run after it on the
+// same stream.
+template <int SRC, int DST, int D>
+__global__ __launch_bounds__(256) void append_kernel(DecodeArgs a) {
+  const int64_t w = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w >= (int64_t)a.batch * a.num_kv_heads) return;
+  append_head<SRC, DST, D>(a, (int)(w / a.num_kv_heads), (int)(w % a.num_kv_heads), threadIdx.x & 63);
+}
+
+template <int SRC, int DST>
+hipError_t launch_append_t(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t waves = (int64_t)a.batch * a.num_kv_heads;
+  const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
+  if (a.head_dim == 64) hipLaunchKernelGGL((append_kernel<SRC, DST, 64>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((append_kernel<SRC, DST, 128>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const DecodeArgs& a, hipStream_t stream) {
+  if (a.q_dtype == kF32 && a.cache_dtype == kF32) return launch_append_t<kF32, kF32>(a, stream);
+  if (a.q_dtype == kBF16 && a.cache_dtype == kBF16) return launch_append_t<kBF16, kBF16>(a, stream);
+  if (a.q_dtype == kBF16 && a.cache_dtype == kFP8) return launch_append_t<kBF16, kFP8>(a, stream);
+  return hipErrorInvalidValue;
+}
+
 // Workgroups of a persistent launch: every CU filled to the kernel's
 // occupancy, and never more waves than the workspace has slots for.
 template <typename K>
@@ -1081,8 +1150,7 @@ typedef const __attribute__((address_space(4))) int32_t* sptr_i32;
 typedef const __attribute__((address_space(4))) float* sptr_f32;
 
 __device__ __forceinline__ int seq_len_s(const StreamCtx& c, int b) {
-  const int lk = ((sptr_i32)c.seqlens)[b];
-  return lk < 0 ? 0 : (lk > c.cap ? c.cap : lk);
+  return clamp_keys(((sptr_i32)c.seqlens)[b], c.len_bias, c.cap);
 }
 
 // Block ids of the four 8-key groups of a chunk.
@@ -1341,7 +1409,30 @@ __device__ __forceinline__ void flush(MState<D>& st, const DecodeArgs& a, const 
 
 // N chunks in flight per wave, held in registers, OCC waves per SIMD (up to
 // 512 / OCC registers per lane).
-template <int CT, int D, int G, int N, int OCC>
+// The appending form (APPEND): before it issues any load, the wave that owns
+// the last chunk of a unit (the chunk that holds key cache_seqlens[b], the
+// new token) stores that unit's new K and V rows, then waits for the stores
+// and invalidates its CU's L1 (an acquire fence), so its own later load of
+// the chunk returns them.  No other wave reads the rows of that KV head at
+// that position.
+template <int CT, int D>
+__device__ __forceinline__ void append_range(const DecodeArgs& a, const int32_t* pre, int ug, int c0, int c1,
+                                             int lane) {
+  Pos p = locate(pre, a.batch, ug, c0);
+  int x = c0 - p.ch + p.nch - 1;  // last chunk of p's unit
+  bool stored = false;
+  while (x < c1) {
+    append_head<kBF16, CT, D>(a, p.b, p.gg, lane);
+    stored = true;
+    if (x + 1 >= c1) break;
+    p.ch = p.nch - 1;
+    p = advance(pre, ug, p);  // the next unit with chunks (one exists: x + 1 < c1 <= T)
+    x += p.nch;
+  }
+  if (stored) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+template <int CT, int D, int G, int N, int OCC, bool APPEND>
 __global__ __launch_bounds__(kStreamThreads, OCC) void decode_mfma_kernel(DecodeArgs a) {
   using Ge = Geo<CT, D>;
   __shared__ int32_t pre[kStreamMaxBatch + 1];
@@ -1362,12 +1453,14 @@ __global__ __launch_bounds__(kStreamThreads, OCC) void decode_mfma_kernel(Decode
   const int w = blockIdx.x * kWaves + wave;
   const int c0 = (int)(T * w / W), c1 = (int)(T * (w + 1) / W);
   if (c0 >= c1) return;
+  if constexpr (APPEND) append_range<CT, D>(a, pre, ug, c0, c1, lane);
 
   StreamCtx c;
   c.k_cache = a.k_cache;
   c.v_cache = a.v_cache;
   c.block_table = a.block_table;
   c.seqlens = a.cache_seqlens;
+  c.len_bias = a.len_bias;
   c.row_bytes = Ge::row_bytes;
   c.slot_stride = a.num_kv_heads * Ge::row_bytes;
   c.block_bytes = (int64_t)a.block_size * c.slot_stride;
@@ -1507,17 +1600,18 @@ constexpr int occupancy() {
   return CT == kFP8 ? PKV_DECODE_OCC_FP8 : PKV_DECODE_OCC;
 }
 
-template <int CT, int D, int G>
+template <int CT, int D, int G, bool APPEND>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   constexpr int N = depth<CT>();
   static int cached_grid = 0;  // per instantiation; the CU count of one process's GPUs is fixed
-  if (cached_grid == 0) cached_grid = persistent_grid(decode_mfma_kernel<CT, D, G, N, occupancy<CT>()>);
+  if (cached_grid == 0) cached_grid = persistent_grid(decode_mfma_kernel<CT, D, G, N, occupancy<CT>(), APPEND>);
   const int64_t max_chunks = (int64_t)a.batch * a.num_kv_heads *
                              (((int64_t)a.max_blocks_per_seq * a.block_size + kChunk - 1) / kChunk);
   int64_t grid = cached_grid;
   if (grid * kWaves > max_chunks) grid = (max_chunks + kWaves - 1) / kWaves;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((decode_mfma_kernel<CT, D, G, N, occupancy<CT>()>), dim3((unsigned)grid), dim3(kStreamThreads), 0, stream, a);
+  hipLaunchKernelGGL((decode_mfma_kernel<CT, D, G, N, occupancy<CT>(), APPEND>), dim3((unsigned)grid),
+                     dim3(kStreamThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)a.batch * a.num_heads;
@@ -1526,22 +1620,22 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int CT, int D>
+template <int CT, int D, bool APPEND>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   switch (a.num_heads / a.num_kv_heads) {
-    case 1: return launch_g<CT, D, 1>(a, stream);
-    case 2: return launch_g<CT, D, 2>(a, stream);
-    case 4: return launch_g<CT, D, 4>(a, stream);
-    case 8: return launch_g<CT, D, 8>(a, stream);
-    case 16: return launch_g<CT, D, 16>(a, stream);
+    case 1: return launch_g<CT, D, 1, APPEND>(a, stream);
+    case 2: return launch_g<CT, D, 2, APPEND>(a, stream);
+    case 4: return launch_g<CT, D, 4, APPEND>(a, stream);
+    case 8: return launch_g<CT, D, 8, APPEND>(a, stream);
+    case 16: return launch_g<CT, D, 16, APPEND>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int CT>
+template <int CT, bool APPEND>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
-  if (a.head_dim == 64) return launch_d<CT, 64>(a, stream);
-  if (a.head_dim == 128) return launch_d<CT, 128>(a, stream);
+  if (a.head_dim == 64) return launch_d<CT, 64, APPEND>(a, stream);
+  if (a.head_dim == 128) return launch_d<CT, 128, APPEND>(a, stream);
   return hipErrorInvalidValue;
 }
 
@@ -1614,10 +1708,15 @@ hipError_t launch_c(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream
 }  // namespace
 
 hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
+  const bool append = a.k_new != nullptr;
   if (p.stream && p.mfma) {
-    if (a.cache_dtype == kBF16) return mfd::launch<kBF16>(a, stream);
-    if (a.cache_dtype == kFP8) return mfd::launch<kFP8>(a, stream);
+    if (a.cache_dtype == kBF16) return append ? mfd::launch<kBF16, true>(a, stream) : mfd::launch<kBF16, false>(a, stream);
+    if (a.cache_dtype == kFP8) return append ? mfd::launch<kFP8, true>(a, stream) : mfd::launch<kFP8, false>(a, stream);
     return hipErrorInvalidValue;
+  }
+  if (append) {  // the other plans: the append kernel, then the decode as usual
+    const hipError_t e = launch_append(a, stream);
+    if (e != hipSuccess) return e;
   }
   if (a.cache_dtype == kF32) return launch_c<kF32>(a, p, stream);
   if (a.cache_dtype == kBF16) return launch_c<kBF16>(a, p, stream);

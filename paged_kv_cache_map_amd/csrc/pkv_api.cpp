@@ -87,6 +87,123 @@ int check_table_rows(const std::vector<int32_t>& table, const std::vector<int32_
 
 }  // namespace
 
+namespace {
+
+struct NewRows {  // the append call's new K/V rows (all NULL/0 for the plain decode)
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int64_t k_stride = 0;  // elements between sequences' rows
+  int64_t v_stride = 0;
+};
+
+int decode_common(const char* name, const NewRows& nr, void* out, const void* q, int q_dtype,
+                  const void* k_cache, const void* v_cache, int cache_dtype, const float* k_scale,
+                  const float* v_scale, const int32_t* block_table, int32_t max_blocks_per_seq,
+                  const int32_t* cache_seqlens, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t block_size, int32_t num_blocks, float softmax_scale,
+                  int32_t split_keys, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool append = nr.k != nullptr || nr.v != nullptr;
+  if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PKV_ERR_INVALID, "%s: sizes must be positive", name);
+  if (batch > 65535) return fail(PKV_ERR_INVALID, "%s: batch above 65535", name);
+  if (num_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "%s: num_heads %% num_kv_heads != 0", name);
+  if (!out || !q || !k_cache || !v_cache || !block_table || !cache_seqlens)
+    return fail(PKV_ERR_INVALID, "%s: NULL pointer", name);
+  if (append && (!nr.k || !nr.v)) return fail(PKV_ERR_INVALID, "%s: NULL k_new or v_new", name);
+  const bool pair_ok = (q_dtype == PKV_F32 && cache_dtype == PKV_F32) ||
+                       (q_dtype == PKV_BF16 && cache_dtype == PKV_BF16) ||
+                       (q_dtype == PKV_BF16 && cache_dtype == PKV_FP8_E4M3);
+  if (!pair_ok)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: unsupported q/cache dtypes %d/%d", name, q_dtype, cache_dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", name, head_dim);
+  if (!pow2_in(block_size, 8, 256))
+    return fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d not a power of two in [8, 256]", name, block_size);
+  if (!group_ok(num_heads / num_kv_heads))
+    return fail(PKV_ERR_UNSUPPORTED, "%s: group size %d not in {1,2,4,8,16}", name,
+                num_heads / num_kv_heads);
+  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID, "%s: fp8 cache needs k_scale and v_scale", name);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(PKV_ERR_INVALID, "%s: q, out and caches must be 16-byte aligned", name);
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  const int qb = elt_bytes(q_dtype);
+  if (append) {
+    if (nr.k_stride < row || nr.v_stride < row)
+      return fail(PKV_ERR_INVALID, "%s: new-row stride below the row width %lld", name, (long long)row);
+    if (!aligned16(nr.k) || !aligned16(nr.v) || (nr.k_stride * qb) % 16 != 0 || (nr.v_stride * qb) % 16 != 0)
+      return fail(PKV_ERR_INVALID, "%s: k_new, v_new and their strides must be 16-byte aligned", name);
+  }
+  pkv::DecodePlan plan;
+  const char* why = nullptr;
+  if (!pkv::plan_decode(batch, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        split_keys, cache_dtype != PKV_F32, &plan, &why))
+    return fail(PKV_ERR_INVALID, "%s: %s", name, why);
+  if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes > 0 && !workspace))
+    return fail(PKV_ERR_INVALID, "%s: workspace of %zu bytes needed, %zu given", name,
+                plan.workspace_bytes, workspace_bytes);
+  if (plan.workspace_bytes > 0 && !aligned16(workspace))
+    return fail(PKV_ERR_INVALID, "%s: workspace must be 16-byte aligned", name);
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_mode()) {
+    std::vector<int32_t> lens, table;
+    if (!fetch(lens, cache_seqlens, batch, s) ||
+        !fetch(table, block_table, (int64_t)batch * max_blocks_per_seq, s))
+      return fail(PKV_ERR_LAUNCH, "%s: could not read metadata", name);
+    if (append) {  // keys attended: the cached ones and the new one; new rows in distinct slots
+      std::unordered_set<int64_t> seen;
+      for (int32_t b = 0; b < batch; ++b) {
+        if (lens[b] < 0) return fail(PKV_ERR_INVALID, "%s: sequence %d has negative length", name, b);
+        if ((int64_t)lens[b] + 1 > (int64_t)max_blocks_per_seq * block_size)
+          return fail(PKV_ERR_INVALID, "%s: sequence %d has no room for its new token", name, b);
+        lens[b] += 1;
+      }
+      const int rc = check_table_rows(table, lens, max_blocks_per_seq, block_size, num_blocks, name);
+      if (rc != PKV_OK) return rc;
+      for (int32_t b = 0; b < batch; ++b) {
+        const int64_t pos = lens[b] - 1;
+        const int64_t slot = (int64_t)table[b * (size_t)max_blocks_per_seq + pos / block_size] * block_size +
+                             pos % block_size;
+        if (!seen.insert(slot).second)
+          return fail(PKV_ERR_INVALID, "%s: sequence %d appends to slot %lld twice", name, b, (long long)slot);
+      }
+    } else {
+      const int rc = check_table_rows(table, lens, max_blocks_per_seq, block_size, num_blocks, name);
+      if (rc != PKV_OK) return rc;
+    }
+  }
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = (const uint8_t*)k_cache;
+  a.v_cache = (const uint8_t*)v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.cache_seqlens = cache_seqlens;
+  a.workspace = (float*)workspace;
+  a.stream_slots = plan.stream_slots;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.batch = batch;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.softmax_scale = softmax_scale;
+  a.q_dtype = q_dtype;
+  a.cache_dtype = cache_dtype;
+  a.k_new = (const uint8_t*)nr.k;
+  a.v_new = (const uint8_t*)nr.v;
+  a.k_new_stride = nr.k_stride * qb;
+  a.v_new_stride = nr.v_stride * qb;
+  a.len_bias = append ? 1 : 0;
+  return launch_status(pkv::launch_paged_decode(a, plan, s), name);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* pkv_last_error(void) { return g_error.c_str(); }
@@ -179,73 +296,30 @@ int pkv_paged_decode(void* out, const void* q, int q_dtype, const void* k_cache,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                      float softmax_scale, int32_t split_keys, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
-    return fail(PKV_ERR_INVALID, "paged_decode: sizes must be positive");
-  if (batch > 65535) return fail(PKV_ERR_INVALID, "paged_decode: batch above 65535");
-  if (num_heads % num_kv_heads != 0)
-    return fail(PKV_ERR_INVALID, "paged_decode: num_heads %% num_kv_heads != 0");
-  if (!out || !q || !k_cache || !v_cache || !block_table || !cache_seqlens)
-    return fail(PKV_ERR_INVALID, "paged_decode: NULL pointer");
-  const bool pair_ok = (q_dtype == PKV_F32 && cache_dtype == PKV_F32) ||
-                       (q_dtype == PKV_BF16 && cache_dtype == PKV_BF16) ||
-                       (q_dtype == PKV_BF16 && cache_dtype == PKV_FP8_E4M3);
-  if (!pair_ok)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_decode: unsupported q/cache dtypes %d/%d", q_dtype,
-                cache_dtype);
-  if (head_dim != 64 && head_dim != 128)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_decode: head_dim %d not in {64, 128}", head_dim);
-  if (!pow2_in(block_size, 8, 256))
-    return fail(PKV_ERR_UNSUPPORTED, "paged_decode: block_size %d not a power of two in [8, 256]",
-                block_size);
-  if (!group_ok(num_heads / num_kv_heads))
-    return fail(PKV_ERR_UNSUPPORTED, "paged_decode: group size %d not in {1,2,4,8,16}",
-                num_heads / num_kv_heads);
-  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
-    return fail(PKV_ERR_INVALID, "paged_decode: fp8 cache needs k_scale and v_scale");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
-    return fail(PKV_ERR_INVALID, "paged_decode: q, out and caches must be 16-byte aligned");
-  pkv::DecodePlan plan;
-  const char* why = nullptr;
-  if (!pkv::plan_decode(batch, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                        split_keys, cache_dtype != PKV_F32, &plan, &why))
-    return fail(PKV_ERR_INVALID, "paged_decode: %s", why);
-  if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes > 0 && !workspace))
-    return fail(PKV_ERR_INVALID, "paged_decode: workspace of %zu bytes needed, %zu given",
-                plan.workspace_bytes, workspace_bytes);
-  if (plan.workspace_bytes > 0 && !aligned16(workspace))
-    return fail(PKV_ERR_INVALID, "paged_decode: workspace must be 16-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
-  if (validate_mode()) {
-    std::vector<int32_t> lens, table;
-    if (!fetch(lens, cache_seqlens, batch, s) ||
-        !fetch(table, block_table, (int64_t)batch * max_blocks_per_seq, s))
-      return fail(PKV_ERR_LAUNCH, "paged_decode: could not read metadata");
-    const int rc = check_table_rows(table, lens, max_blocks_per_seq, block_size, num_blocks,
-                                    "paged_decode");
-    if (rc != PKV_OK) return rc;
-  }
-  pkv::DecodeArgs a;
-  a.out = out;
-  a.q = q;
-  a.k_cache = (const uint8_t*)k_cache;
-  a.v_cache = (const uint8_t*)v_cache;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  a.block_table = block_table;
-  a.cache_seqlens = cache_seqlens;
-  a.workspace = (float*)workspace;
-  a.stream_slots = plan.stream_slots;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.batch = batch;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.block_size = block_size;
-  a.num_blocks = num_blocks;
-  a.softmax_scale = softmax_scale;
-  a.q_dtype = q_dtype;
-  a.cache_dtype = cache_dtype;
-  return launch_status(pkv::launch_paged_decode(a, plan, s), "paged_decode");
+  return decode_common("paged_decode", NewRows{}, out, q, q_dtype, k_cache, v_cache, cache_dtype, k_scale,
+                       v_scale, block_table, max_blocks_per_seq, cache_seqlens, batch, num_heads,
+                       num_kv_heads, head_dim, block_size, num_blocks, softmax_scale, split_keys, workspace,
+                       workspace_bytes, stream);
+}
+
+int pkv_paged_decode_append(void* out, const void* q, int q_dtype, const void* k_new, int64_t k_new_stride,
+                            const void* v_new, int64_t v_new_stride, void* k_cache, void* v_cache,
+                            int cache_dtype, const float* k_scale, const float* v_scale,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* cache_seqlens, int32_t batch, int32_t num_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            float softmax_scale, int32_t split_keys, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  NewRows nr;
+  nr.k = k_new;
+  nr.v = v_new;
+  nr.k_stride = k_new_stride;
+  nr.v_stride = v_new_stride;
+  if (!k_new || !v_new) return fail(PKV_ERR_INVALID, "paged_decode_append: NULL k_new or v_new");
+  return decode_common("paged_decode_append", nr, out, q, q_dtype, k_cache, v_cache, cache_dtype, k_scale,
+                       v_scale, block_table, max_blocks_per_seq, cache_seqlens, batch, num_heads,
+                       num_kv_heads, head_dim, block_size, num_blocks, softmax_scale, split_keys, workspace,
+                       workspace_bytes, stream);
 }
 
 int pkv_varlen_prefill(void* out, const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,

@@ -76,6 +76,42 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | ((r >> 20) - (120u << 3));
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 source bytes of a K or V row -> the cache's bytes for them (16, 8 or 4,
+// in the low words): a bit copy when the types match, else the fp8 encoding
+// e4m3(x / scale) with an IEEE fp32 division (the library is built with
+// correctly rounded division).  Every cache write of the library goes through
+// this one function, so the slot-map scatter and the appending decode store
+// identical bits.
+template <int SRC, int DST>
+__device__ __forceinline__ u32x4_t convert_piece(uint4 x, float sc) {
+  u32x4_t o = {x.x, x.y, x.z, x.w};
+  if constexpr (SRC == kBF16 && DST == kFP8) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+      out[e >> 2] |= f32_to_e4m3(v / sc) << ((e & 3) * 8);
+    }
+    o.x = out[0];
+    o.y = out[1];
+  } else if constexpr (SRC == kF32 && DST == kFP8) {
+    o.x = f32_to_e4m3(__uint_as_float(x.x) / sc) | (f32_to_e4m3(__uint_as_float(x.y) / sc) << 8) |
+          (f32_to_e4m3(__uint_as_float(x.z) / sc) << 16) |
+          (f32_to_e4m3(__uint_as_float(x.w) / sc) << 24);
+  }
+  return o;
+}
+
+// Keys a decode attends: cache_seqlens[b] (raw) plus bias (1 when the call
+// appends the step's token itself), clamped to [0, cap].
+__device__ __forceinline__ int clamp_keys(int raw, int bias, int cap) {
+  const int64_t x = (int64_t)raw + bias;
+  return x < 0 ? 0 : (x > cap ? cap : (int)x);
+}
+
 // ---------------------------------------------------------------------------
 // cross-lane helpers (wave64)
 // ---------------------------------------------------------------------------

@@ -77,6 +77,15 @@ struct DecodeArgs {
   float softmax_scale;
   int q_dtype;
   int cache_dtype;
+  // Append call (k_new != NULL): the step's new K/V rows, [batch, Hkv, D] of
+  // q_dtype, sequences k_new_stride / v_new_stride bytes apart.  The call
+  // stores them at position cache_seqlens[b] and attends cache_seqlens[b] + 1
+  // keys (len_bias = 1); otherwise len_bias = 0 and nothing is written.
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  int64_t k_new_stride;
+  int64_t v_new_stride;
+  int32_t len_bias;
 };
 
 hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);

@@ -63,6 +63,19 @@ class GpuStep:
                                 self.s.scale, self.k_scale, self.v_scale, split_keys=split_keys,
                                 workspace=workspace)
 
+    def append_decode(self, split_keys=0, workspace=None):
+        """The appending decode: stores the decode sequences' new rows and attends."""
+        d = self.s.decode_append_inputs()
+        return pkv.paged_decode_append(self.dec_q, to_dev(d["k_new"], self.s.q_dtype),
+                                       to_dev(d["v_new"], self.s.q_dtype), self.k_cache, self.v_cache,
+                                       self.dec_bt, to_dev(d["cache_seqlens"], "i32"), self.s.scale,
+                                       self.k_scale, self.v_scale, split_keys=split_keys,
+                                       workspace=workspace)
+
+    def write_prefill_only(self):
+        pkv.kv_cache_write(self.k_new, self.v_new, self.k_cache, self.v_cache,
+                           to_dev(self.s.prefill_slot_map(), "i32"), self.k_scale, self.v_scale)
+
     def prefill(self):
         p = self.pre
         return pkv.varlen_prefill(self.pre_q, self.k_cache, self.v_cache, self.pre_cu_q,
@@ -79,6 +92,18 @@ def oracle_decode(step, kc, vc, pairs=None):
     d = step.decode_inputs()
     return paged.paged_decode(d["q"], step.q_dtype, kc, vc, step.cache_dtype, d["block_table"],
                               d["cache_seqlens"], step.scale, step.k_scale, step.v_scale, pairs=pairs)
+
+
+def oracle_append_decode(step, pairs=None):
+    """The oracle's appending decode on the step's decode sequences, after the
+    oracle's write of the prefill sequences' tokens.  Returns (out, kc, vc)."""
+    kc, vc = paged.kv_cache_write(step.k_new, step.v_new, step.k_cache, step.v_cache,
+                                  step.prefill_slot_map(), step.q_dtype, step.cache_dtype,
+                                  step.k_scale, step.v_scale)
+    d = step.decode_append_inputs()
+    return paged.paged_decode_append(d["q"], step.q_dtype, d["k_new"], d["v_new"], kc, vc,
+                                     step.cache_dtype, d["block_table"], d["cache_seqlens"], step.scale,
+                                     step.k_scale, step.v_scale, pairs=pairs)
 
 
 def oracle_prefill(step, kc, vc, rows=None):

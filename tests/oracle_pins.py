@@ -278,3 +278,65 @@ def check_write_example(paged, seed=10):
     untouched[g["derived"]["new_token_slots"]] = False
     assert flat_k[untouched].tobytes() == flat_k_old[untouched].tobytes()
     assert flat_v[untouched].tobytes() == flat_v_old[untouched].tobytes()
+
+
+# ---------------------------------------------------------------------------
+# the decode that stores its own token ([paged-doc] "デコードパス", キャッシュの動作)
+# ---------------------------------------------------------------------------
+
+
+def check_append_example(paged, seed=12):
+    """The decode example as one appending step: lengths [30, 32, 70] before
+    the step; the three new rows land at slots 94, 32, 198 (nothing else in
+    the pool changes) and each output is SDPA over the sequence's keys in
+    order, the new one last, walked here through the printed table."""
+    g = load_golden("page2_decode_example.json")
+    p = g["printed"]
+    bs = p["block_size"]
+    table = np.array(p["block_table"], dtype=np.int32)
+    lens = p["cache_seqlens"]
+    rng = np.random.default_rng(seed)
+    hq, hkv, d = 8, 2, 64
+    kc = rng.standard_normal((8, bs, hkv, d)).astype(np.float32)
+    vc = rng.standard_normal((8, bs, hkv, d)).astype(np.float32)
+    kn = rng.standard_normal((3, hkv, d)).astype(np.float32)
+    vn = rng.standard_normal((3, hkv, d)).astype(np.float32)
+    q = rng.standard_normal((3, hq, d)).astype(np.float32)
+    out, k2, v2 = paged.paged_decode_append(q, "f32", kn, vn, kc, vc, "f32", table,
+                                            np.array(lens, np.int32), 0.125)
+    slots = g["derived"]["new_token_slots"]
+    fk_old, fk = kc.reshape(-1, hkv, d), k2.reshape(-1, hkv, d)
+    fv_old, fv = vc.reshape(-1, hkv, d), v2.reshape(-1, hkv, d)
+    changed = [s for s in range(8 * bs) if not np.array_equal(fk[s], fk_old[s])]
+    assert sorted(changed) == sorted(slots)
+    for b, s in enumerate(slots):
+        assert fk[s].tobytes() == kn[b].tobytes() and fv[s].tobytes() == vn[b].tobytes()
+    keep = np.ones(8 * bs, bool)
+    keep[slots] = False
+    assert fv[keep].tobytes() == fv_old[keep].tobytes()
+    for b, n in enumerate(lens):
+        walk = [table[b][j // bs] * bs + j % bs for j in range(n)]
+        kk = np.concatenate([fk_old[walk], kn[b][None]]).astype(np.float64)
+        vv = np.concatenate([fv_old[walk], vn[b][None]]).astype(np.float64)
+        want = _sdpa(q[b:b + 1].astype(np.float64), kk, vv, 0.125, causal=False)
+        np.testing.assert_allclose(out[b:b + 1], want, rtol=1e-12, atol=1e-12)
+
+
+def check_append_to_empty_sequence(paged, seed=13):
+    """A sequence with no cached key attends to its new token alone: every q
+    head returns the new V row of its KV head exactly (softmax of one logit)."""
+    rng = np.random.default_rng(seed)
+    hq, hkv, d, bs = 6, 2, 8, 4
+    kc = np.full((3, bs, hkv, d), np.nan, np.float32)
+    vc = np.full((3, bs, hkv, d), np.nan, np.float32)
+    table = np.array([[2, -1], [0, 1]], np.int32)
+    kc[0], vc[0] = rng.standard_normal((2, bs, hkv, d)).astype(np.float32)
+    kc[1, :1], vc[1, :1] = rng.standard_normal((2, 1, hkv, d)).astype(np.float32)
+    kn = rng.standard_normal((2, hkv, d)).astype(np.float32)
+    vn = rng.standard_normal((2, hkv, d)).astype(np.float32)
+    q = rng.standard_normal((2, hq, d)).astype(np.float32)
+    out, _, _ = paged.paged_decode_append(q, "f32", kn, vn, kc, vc, "f32", table,
+                                          np.array([0, 5], np.int32), 0.9)
+    for h in range(hq):
+        assert np.array_equal(out[0, h], vn[0, h // (hq // hkv)].astype(np.float64))
+    assert np.all(np.isfinite(out[1]))

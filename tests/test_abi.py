@@ -20,8 +20,9 @@ def declared_functions():
 
 def test_header_declares_the_three_calls():
     names = declared_functions()
-    for want in ("pkv_kv_cache_write", "pkv_paged_decode", "pkv_varlen_prefill",
-                 "pkv_paged_decode_workspace_size", "pkv_last_error", "pkv_version"):
+    for want in ("pkv_kv_cache_write", "pkv_paged_decode", "pkv_paged_decode_append",
+                 "pkv_varlen_prefill", "pkv_paged_decode_workspace_size", "pkv_last_error",
+                 "pkv_version"):
         assert want in names
 
 
@@ -99,6 +100,35 @@ def decode(**kw):
 ])
 def test_decode_rejects(kw, code):
     assert decode(**kw) == code
+
+
+def append(**kw):
+    a = dict(out=FAKE, q=FAKE, qdt=pkv.BF16, kn=FAKE, kns=256, vn=FAKE, vns=256, kc=FAKE, vc=FAKE,
+             cdt=pkv.BF16, ksc=NULL, vsc=NULL, bt=FAKE, maxblk=4, sl=FAKE, b=3, hq=8, hkv=2, d=128,
+             bs=16, nb=10, scale=0.1, split=0, ws=FAKE, wsb=1 << 30, stream=NULL)
+    a.update(kw)
+    return pkv.library().pkv_paged_decode_append(
+        a["out"], a["q"], a["qdt"], a["kn"], a["kns"], a["vn"], a["vns"], a["kc"], a["vc"], a["cdt"],
+        a["ksc"], a["vsc"], a["bt"], a["maxblk"], a["sl"], a["b"], a["hq"], a["hkv"], a["d"], a["bs"],
+        a["nb"], a["scale"], a["split"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=NULL), pkv.ERR_INVALID),
+    (dict(vn=NULL), pkv.ERR_INVALID),
+    (dict(kns=255), pkv.ERR_INVALID),                 # stride below the row width 2 x 128
+    (dict(vns=260), pkv.ERR_INVALID),                 # 520-byte stride is not 16-byte aligned
+    (dict(kn=ODD), pkv.ERR_INVALID),
+    (dict(b=0), pkv.ERR_INVALID),
+    (dict(d=80), pkv.ERR_UNSUPPORTED),
+    (dict(cdt=pkv.FP8_E4M3), pkv.ERR_INVALID),        # fp8 without scales
+    (dict(qdt=pkv.F32), pkv.ERR_UNSUPPORTED),         # fp32 q and new rows with a bf16 cache
+    (dict(split=100), pkv.ERR_INVALID),
+    (dict(split=128, maxblk=64, wsb=0, ws=NULL), pkv.ERR_INVALID),
+])
+def test_append_rejects(kw, code):
+    assert append(**kw) == code
+    assert b"paged_decode_append" in pkv.library().pkv_last_error()
 
 
 def prefill(**kw):

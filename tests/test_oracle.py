@@ -156,6 +156,14 @@ def test_decode_is_varlen_with_one_query():
     pins.check_decode_is_varlen_with_one_query(paged)
 
 
+def test_append_example():
+    pins.check_append_example(paged)
+
+
+def test_append_to_empty_sequence():
+    pins.check_append_to_empty_sequence(paged)
+
+
 def test_write_skip_and_errors():
     kc = np.zeros((2, 4, 1, 8), np.float32)
     vc = np.zeros((2, 4, 1, 8), np.float32)

@@ -21,7 +21,8 @@ PAGED_CHECKS = [
     pins.check_dense_causal_square, pins.check_dense_noncausal, pins.check_prefix_alignment,
     pins.check_varlen_example_outputs, pins.check_equal_keys_mean,
     pins.check_paged_decode_matches_dense, pins.check_paged_prefill_matches_contig,
-    pins.check_decode_is_varlen_with_one_query,
+    pins.check_decode_is_varlen_with_one_query, pins.check_append_example,
+    pins.check_append_to_empty_sequence,
 ]
 
 # (name, original text, planted text)
@@ -54,6 +55,10 @@ PAGED_MUTATIONS = [
     ("prefill_wrong_table_row", "k_rows = gather(k, block_table[b], lk)",
      "k_rows = gather(k, block_table[0], lk)"),
     ("decode_drops_last_key", "lk = int(cache_seqlens[b])", "lk = int(cache_seqlens[b]) - 1"),
+    ("append_after_last_key", "slots = np.array([slot_of(block_table[b], int(lens[b]), bs)",
+     "slots = np.array([slot_of(block_table[b], int(lens[b]) - 1, bs)"),
+    ("append_not_attended", "out = paged_decode(q, q_dtype, kc, vc, cache_dtype, block_table, lens + 1,",
+     "out = paged_decode(q, q_dtype, kc, vc, cache_dtype, block_table, lens,"),
     ("empty_row_not_zero", "out[:, h, :] = np.where(has_key[:, None], numer / np.where(has_key, denom, 1.0)[:, None], 0.0)",
      "out[:, h, :] = numer / np.where(has_key, denom, 1.0)[:, None] + np.where(has_key, 0.0, 1.0)[:, None]"),
 ]

@@ -168,6 +168,25 @@ class Step:
             seq_ids=ids,
         )
 
+    def decode_append_inputs(self) -> dict:
+        """Arguments of the appending decode call: the decode sequences' new
+        K/V rows and their lengths before the step (the call stores the rows)."""
+        d = self.decode_inputs()
+        rows = self.token_ranges()[d["seq_ids"]]
+        d["k_new"] = np.ascontiguousarray(self.k_new[rows])
+        d["v_new"] = np.ascontiguousarray(self.v_new[rows])
+        d["cache_seqlens"] = self.prefix[d["seq_ids"]].astype(np.int32)
+        return d
+
+    def prefill_slot_map(self) -> np.ndarray:
+        """The step's slot map with the decode sequences' tokens skipped (-1),
+        for a step whose decode tokens are stored by the appending decode."""
+        sm = self.slot_map.copy()
+        starts = self.token_ranges()
+        for i in self.ids("decode"):
+            sm[starts[i]:starts[i + 1]] = -1
+        return sm
+
     def prefill_inputs(self) -> dict:
         """Arguments of the varlen call (paged K/V) for the prefill sequences."""
         ids = self.ids("prefill")
