@@ -42,6 +42,8 @@ def parse():
                     help="decode split size in keys (0: the library's automatic plan)")
     ap.add_argument("--only", default=None,
                     help="diagnostic: time one named workload and print its kernel times only")
+    ap.add_argument("--append", action="store_true",
+                    help="diagnostic (--only): store the decode tokens with the appending decode")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 512 MiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -116,12 +118,13 @@ def decode_traffic():
 class Runner:
     """A workload step on the GPU with `copies` rotated replicas of its KV pool."""
 
-    def __init__(self, step, copies=1, split_keys=0):
+    def __init__(self, step, copies=1, split_keys=0, append=False):
         import torch
         from workloads.device import to_dev
         self.torch = torch
         self.s = step
         self.split_keys = split_keys
+        self.append = append
         self.copies = []
         for _ in range(copies):
             self.copies.append((to_dev(step.k_cache, step.cache_dtype),
@@ -144,6 +147,13 @@ class Runner:
                                                    step.num_kv_heads, step.head_dim, bs,
                                                    d["block_table"].shape[1], split_keys)
             self.dws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+            if append:  # the decode sequences' rows go through the appending decode
+                a = step.decode_append_inputs()
+                self.akn = to_dev(a["k_new"], step.q_dtype)
+                self.avn = to_dev(a["v_new"], step.q_dtype)
+                self.alen = to_dev(a["cache_seqlens"], "i32")
+                self.slot_map = to_dev(step.prefill_slot_map(), "i32")
+        self.write_tokens = int((step.prefill_slot_map() >= 0).sum()) if append else step.num_tokens
         p = step.prefill_inputs()
         self.has_prefill = len(p["seq_ids"]) > 0
         if self.has_prefill:
@@ -161,7 +171,8 @@ class Runner:
         s = self.s
         if ev is not None:
             ev[0].record()
-        pkv.kv_cache_write(self.k_new, self.v_new, kc, vc, self.slot_map, self.k_scale, self.v_scale)
+        if self.write_tokens:
+            pkv.kv_cache_write(self.k_new, self.v_new, kc, vc, self.slot_map, self.k_scale, self.v_scale)
         if ev is not None:
             ev[1].record()
         if self.has_prefill:
@@ -173,7 +184,11 @@ class Runner:
             ev[2].record()
         elif ev is not None:
             ev[2] = ev[1]
-        if self.has_decode:
+        if self.has_decode and self.append:
+            pkv.paged_decode_append(self.dq, self.akn, self.avn, kc, vc, self.dbt, self.alen, s.scale,
+                                    self.k_scale, self.v_scale, out=self.dout, split_keys=self.split_keys,
+                                    workspace=self.dws)
+        elif self.has_decode:
             pkv.paged_decode(self.dq, kc, vc, self.dbt, self.dlen, s.scale, self.k_scale,
                              self.v_scale, out=self.dout, split_keys=self.split_keys,
                              workspace=self.dws)
@@ -231,16 +246,21 @@ def copies_for(step):
     return max(1, math.ceil(ROTATE_BYTES / pool))
 
 
-def measure(name, steps, warmup, split_keys=0, **overrides):
+def measure(name, steps, warmup, split_keys=0, append=False, **overrides):
+    """Time one workload step.  append=True: the decode sequences' new rows
+    are stored by the appending decode call (one launch for their write and
+    their attention); the slot-map write then covers the prefill tokens only,
+    and the decode figures count the appended rows' write bytes as well."""
     import workloads
     step = workloads.config(name, **overrides)
-    r = Runner(step, copies_for(step), split_keys)
+    r = Runner(step, copies_for(step), split_keys, append)
     t = r.time(steps, warmup)
     res = dict(t)
-    res["write_bytes"] = write_bytes(step)
-    res["write_gbs"] = res["write_bytes"] / (t["write_ms"] * 1e6)
+    step_write = write_bytes(step)
+    res["write_bytes"] = step_write * r.write_tokens // max(step.num_tokens, 1)
+    res["write_gbs"] = res["write_bytes"] / (t["write_ms"] * 1e6) if r.write_tokens else 0.0
     if r.has_decode:
-        res["decode_bytes"] = decode_bytes(step)
+        res["decode_bytes"] = decode_bytes(step) + (step_write - res["write_bytes"])
         res["decode_gbs"] = res["decode_bytes"] / (t["decode_ms"] * 1e6)
         res["decode_frac_hbm"] = res["decode_gbs"] / HBM_PEAK_GBS
     if r.has_prefill:
@@ -293,7 +313,7 @@ def main():
 
     if args.only:
         print(f"[bench] {args.only} (diagnostic)", flush=True)
-        _, res = measure(args.only, args.steps, args.warmup, args.split_keys)
+        _, res = measure(args.only, args.steps, args.warmup, args.split_keys, args.append)
         print(json.dumps({"diagnostic": args.only,
                           **{k: (round(v, 5) if isinstance(v, float) else v) for k, v in res.items()}}),
               flush=True)

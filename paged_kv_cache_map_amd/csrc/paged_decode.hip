@@ -975,34 +975,57 @@ __global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs
 // keys, so the write needs no launch of its own.
 // ---------------------------------------------------------------------------
 
-// Store the new K and V rows of KV head g of sequence b.  Lanes [0, P) move
-// the 16-byte source pieces of K, lanes [P, 2 P) those of V (P pieces per
-// head row, at most 32).  Nothing is stored when the position lies past the
-// block table or in an invalid block (bad metadata; memory-safe).
+// One lane's share of the new K and V rows of KV head g of sequence b: lanes
+// [0, P) move the 16-byte source pieces of K, lanes [P, 2 P) those of V (P
+// pieces per head row, at most 32).  fetch_new issues the source load and
+// the length load without waiting for either; store_new finds the slot and
+// stores (nothing for idle lanes, or for a position past the block table or
+// in an invalid block: bad metadata, memory-safe).
+struct NewPiece {
+  uint4 x;  // the lane's source bytes
+  int b, g;
+  int pos;  // cache_seqlens[b]: the new token's position
+};
+
+typedef const __attribute__((address_space(4))) int32_t* cptr_i32;
+typedef const __attribute__((address_space(4))) float* cptr_f32;
+
+template <int SRC, int D>
+__device__ __forceinline__ NewPiece fetch_new(const DecodeArgs& a, int b, int g, int lane) {
+  constexpr int src_row = D * Elt<SRC>::bytes;
+  constexpr int P = src_row / 16;
+  static_assert(2 * P <= 64, "one wave moves a head's K and V rows");
+  const int l = lane < 2 * P ? lane : 2 * P - 1;
+  const bool is_v = l >= P;
+  const uint8_t* src = (is_v ? a.v_new + (int64_t)b * a.v_new_stride : a.k_new + (int64_t)b * a.k_new_stride) +
+                       g * src_row + (is_v ? l - P : l) * 16;
+  NewPiece n;
+  n.x = *reinterpret_cast<const uint4*>(src);
+  n.b = b;
+  n.g = g;
+  n.pos = ((cptr_i32)a.cache_seqlens)[b];  // metadata is not written while a kernel runs
+  return n;
+}
+
 template <int SRC, int DST, int D>
-__device__ __forceinline__ void append_head(const DecodeArgs& a, int b, int g, int lane) {
+__device__ __forceinline__ void store_new(const DecodeArgs& a, const NewPiece& n, int lane) {
   constexpr int src_row = D * Elt<SRC>::bytes;
   constexpr int dst_row = D * Elt<DST>::bytes;
   constexpr int P = src_row / 16;
   constexpr int dst_piece = 16 * Elt<DST>::bytes / Elt<SRC>::bytes;  // cache bytes per source piece
-  static_assert(2 * P <= 64, "one wave moves a head's K and V rows");
-  const int pos = a.cache_seqlens[b];
   const int cap = a.max_blocks_per_seq * a.block_size;
-  if (pos < 0 || pos >= cap) return;
-  const int blk = a.block_table[(int64_t)b * a.max_blocks_per_seq + (pos >> __builtin_ctz(a.block_size))];
+  if (n.pos < 0 || n.pos >= cap) return;
+  const int blk = ((cptr_i32)a.block_table)[(int64_t)n.b * a.max_blocks_per_seq +
+                                            (n.pos >> __builtin_ctz(a.block_size))];
   if (blk < 0 || blk >= a.num_blocks || lane >= 2 * P) return;
   const bool is_v = lane >= P;
-  const int pc = is_v ? lane - P : lane;
-  const uint8_t* src = (is_v ? a.v_new + (int64_t)b * a.v_new_stride : a.k_new + (int64_t)b * a.k_new_stride) +
-                       g * src_row + pc * 16;
-  const uint4 x = *reinterpret_cast<const uint4*>(src);
   float sc = 1.0f;
-  if constexpr (DST == kFP8) sc = (is_v ? a.v_scale : a.k_scale)[g];
-  const u32x4_t v = convert_piece<SRC, DST>(x, sc);
-  const int64_t slot = (int64_t)blk * a.block_size + (pos & (a.block_size - 1));
+  if constexpr (DST == kFP8) sc = ((cptr_f32)(is_v ? a.v_scale : a.k_scale))[n.g];
+  const int64_t slot = (int64_t)blk * a.block_size + (n.pos & (a.block_size - 1));
   // the caches are the caller's writable buffers (the decode kernels only read them)
-  uint8_t* dst = const_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) +
-                 slot * ((int64_t)a.num_kv_heads * dst_row) + g * dst_row + pc * dst_piece;
+  uint8_t* dst = const_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) + slot * ((int64_t)a.num_kv_heads * dst_row) +
+                 n.g * dst_row + (is_v ? lane - P : lane) * dst_piece;
+  const u32x4_t v = convert_piece<SRC, DST>(n.x, sc);
   if constexpr (dst_piece == 16) {
     *reinterpret_cast<uint4*>(dst) = make_uint4(v.x, v.y, v.z, v.w);
   } else if constexpr (dst_piece == 8) {
@@ -1010,6 +1033,12 @@ __device__ __forceinline__ void append_head(const DecodeArgs& a, int b, int g, i
   } else {
     *reinterpret_cast<uint32_t*>(dst) = v.x;
   }
+}
+
+// Store the new K and V rows of KV head g of sequence b.
+template <int SRC, int DST, int D>
+__device__ __forceinline__ void append_head(const DecodeArgs& a, int b, int g, int lane) {
+  store_new<SRC, DST, D>(a, fetch_new<SRC, D>(a, b, g, lane), lane);
 }
 
 // The append on its own (plans other than the matrix-core stream-K kernel):
@@ -1409,27 +1438,47 @@ __device__ __forceinline__ void flush(MState<D>& st, const DecodeArgs& a, const 
 
 // N chunks in flight per wave, held in registers, OCC waves per SIMD (up to
 // 512 / OCC registers per lane).
-// The appending form (APPEND): before it issues any load, the wave that owns
-// the last chunk of a unit (the chunk that holds key cache_seqlens[b], the
-// new token) stores that unit's new K and V rows, then waits for the stores
-// and invalidates its CU's L1 (an acquire fence), so its own later load of
-// the chunk returns them.  No other wave reads the rows of that KV head at
-// that position.
-template <int CT, int D>
-__device__ __forceinline__ void append_range(const DecodeArgs& a, const int32_t* pre, int ug, int c0, int c1,
-                                             int lane) {
-  Pos p = locate(pre, a.batch, ug, c0);
+// The appending form (APPEND): the wave that owns the last chunk of a unit
+// (the chunk holding key cache_seqlens[b], the new token) stores that unit's
+// new K and V rows before it issues the load of that chunk.  A wave's memory
+// operations reach the caches in issue order, so its own later load returns
+// the stored rows; no other wave reads the rows of that KV head at that
+// position.  The rows of the first unit that ends past the wave's first N
+// chunks are fetched before those chunks' loads and stored after them, so
+// waiting for them holds up nothing; units ending inside the first N chunks
+// (before their loads) and the further ones are stored directly.
+
+// First chunk >= lo that ends a unit, and that unit; -1 if none below hi.
+// p0: the position of chunk c0.
+__device__ __forceinline__ int first_unit_end(const int32_t* pre, int ug, const Pos& p0, int c0, int lo, int hi,
+                                              Pos& p) {
+  if (lo >= hi) return -1;
+  p = p0;
   int x = c0 - p.ch + p.nch - 1;  // last chunk of p's unit
-  bool stored = false;
-  while (x < c1) {
-    append_head<kBF16, CT, D>(a, p.b, p.gg, lane);
-    stored = true;
-    if (x + 1 >= c1) break;
+  while (x < lo) {
+    if (x + 1 >= hi) return -1;
     p.ch = p.nch - 1;
-    p = advance(pre, ug, p);  // the next unit with chunks (one exists: x + 1 < c1 <= T)
+    p = advance(pre, ug, p);  // the next unit with chunks (one exists: x + 1 < hi <= T)
     x += p.nch;
   }
-  if (stored) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return x < hi ? x : -1;
+}
+
+// Store the rows of every unit whose last chunk lies in [lo, hi).
+template <int CT, int D>
+__device__ __forceinline__ void append_range(const DecodeArgs& a, const int32_t* pre, int ug, const Pos& p0, int c0,
+                                             int lo, int hi, int lane) {
+  Pos p;
+  int x = first_unit_end(pre, ug, p0, c0, lo, hi, p);
+  if (x < 0) return;
+  for (;;) {
+    append_head<kBF16, CT, D>(a, p.b, p.gg, lane);
+    if (x + 1 >= hi) break;
+    p.ch = p.nch - 1;
+    p = advance(pre, ug, p);
+    x += p.nch;
+    if (x >= hi) break;
+  }
 }
 
 template <int CT, int D, int G, int N, int OCC, bool APPEND>
@@ -1453,7 +1502,16 @@ __global__ __launch_bounds__(kStreamThreads, OCC) void decode_mfma_kernel(Decode
   const int w = blockIdx.x * kWaves + wave;
   const int c0 = (int)(T * w / W), c1 = (int)(T * (w + 1) / W);
   if (c0 >= c1) return;
-  if constexpr (APPEND) append_range<CT, D>(a, pre, ug, c0, c1, lane);
+  const Pos p0 = locate(pre, a.batch, ug, c0);
+  NewPiece pend;  // APPEND: the rows of the first unit ending past the first N chunks
+  int pend_x = -1;
+  if constexpr (APPEND) {
+    Pos pe;
+    pend_x = first_unit_end(pre, ug, p0, c0, c0 + N, c1, pe);
+    if (pend_x >= 0) pend = fetch_new<kBF16, D>(a, pe.b, pe.gg, lane);
+    append_range<CT, D>(a, pre, ug, p0, c0, c0, min(c1, c0 + N), lane);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no load of the caches moves above these stores
+  }
 
   StreamCtx c;
   c.k_cache = a.k_cache;
@@ -1521,7 +1579,7 @@ __global__ __launch_bounds__(kStreamThreads, OCC) void decode_mfma_kernel(Decode
   };
   Chunk<CT, D> ring[N];
   uint4 qbuf[NQ][Ge::KS];
-  Pos cur = locate(pre, a.batch, ug, c0);
+  Pos cur = p0;
   cur.len = seq_len_s(c, cur.b);
   Pos ip = cur, lp = cur;  // next chunk to load, last chunk loaded
 #pragma unroll
@@ -1530,6 +1588,13 @@ __global__ __launch_bounds__(kStreamThreads, OCC) void decode_mfma_kernel(Decode
     issue(ring[j], ip, fetch_tbl(c, ip));
     lp = ip;
     ip = next_pos(ip, c0 + j);
+  }
+  if constexpr (APPEND) {
+    if (pend_x >= 0) {
+      store_new<kBF16, CT, D>(a, pend, lane);
+      append_range<CT, D>(a, pre, ug, p0, c0, pend_x + 1, c1, lane);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
   Tbl tb = fetch_tbl(c, ip);
   int x = c0;
