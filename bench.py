@@ -6,8 +6,10 @@ A step is one pass of the hot path over one batch: the KV write of the new
 tokens followed by the attention call(s) that read them (decode, prefill, or
 both for the mixed step).  The headline line measures the Llama-3.1-8B-shaped
 decode step (batch 64, 32/8 heads, head_dim 128, bf16, contexts U{512..4096},
-block size 16); `value` is that step's algorithmic HBM bytes (write + decode)
-per second.  Inputs are resident in HBM before timing starts; the KV pool is
+block size 16) done by the appending decode, which stores the 64 new tokens
+and attends in one call; `value` is that step's algorithmic HBM bytes (write
++ decode) per second.  The same step as two calls (slot-map write, then the
+plain decode) is reported beside it.  Inputs are resident in HBM before timing starts; the KV pool is
 replicated and rotated so that consecutive steps never find it in the 256 MB
 Infinity Cache.  Kernel durations come from HIP events recorded on the stream
 the kernels run on.  One JSON line is printed.
@@ -88,7 +90,7 @@ def prefill_flops(step):
 # measured in the same runs.  The figures belong to the decode sources with
 # the given digest: after any change to them the traffic is reported as null
 # until the counters are taken again.
-DECODE_TRAFFIC = {"digest": "1f3498aa5041adef", "read_bytes": 551602841, "write_bytes": 3628768}
+DECODE_TRAFFIC = {"digest": "26442499afddc454", "read_bytes": 551967996, "write_bytes": 3891149}
 DECODE_SOURCES = ("paged_kv_cache_map_amd/csrc/paged_decode.hip",
                   "paged_kv_cache_map_amd/csrc/pkv_device.hpp",
                   "paged_kv_cache_map_amd/csrc/pkv_plan.cpp",
@@ -203,9 +205,12 @@ class Runner:
         for i in range(warmup):
             self.run(i)
         torch.cuda.synchronize()
+        region = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         t0 = time.perf_counter()
+        region[0].record()
         for i in range(steps):
             self.run(warmup + i)
+        region[1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
@@ -216,6 +221,7 @@ class Runner:
         pre = [e[1].elapsed_time(e[2]) for e in evs] if self.has_prefill else [0.0]
         dec = [e[2].elapsed_time(e[3]) for e in evs] if self.has_decode else [0.0]
         return dict(ms_per_step=wall * 1e3 / steps,
+                    region_ms_per_step=region[0].elapsed_time(region[1]) / steps,
                     write_ms=float(np.mean(write)), write_ms_min=float(np.min(write)),
                     prefill_ms=float(np.mean(pre)), prefill_ms_min=float(np.min(pre)),
                     decode_ms=float(np.mean(dec)), decode_ms_min=float(np.min(dec)))
@@ -278,7 +284,7 @@ def measure(name, steps, warmup, split_keys=0, append=False, **overrides):
 # ---------------------------------------------------------------------------
 
 
-def cpu_baseline(step, algorithmic_bytes):
+def cpu_baseline(step, algorithmic_bytes, min_seconds=10.0):
     from oracle import paged
     try:
         from threadpoolctl import threadpool_info
@@ -286,17 +292,20 @@ def cpu_baseline(step, algorithmic_bytes):
     except Exception:  # noqa: BLE001 - reporting only
         blas_threads = 1
     cores = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    kc, vc = paged.kv_cache_write(step.k_new, step.v_new, step.k_cache, step.v_cache, step.slot_map,
-                                  step.q_dtype, step.cache_dtype, step.k_scale, step.v_scale)
-    d = step.decode_inputs()
-    paged.paged_decode(d["q"], step.q_dtype, kc, vc, step.cache_dtype, d["block_table"],
-                       d["cache_seqlens"], step.scale, step.k_scale, step.v_scale)
-    secs = time.perf_counter() - t0
-    return {"value": round(algorithmic_bytes / secs / 1e9, 4), "unit": "GB/s",
+    d = step.decode_append_inputs()
+    reps, t0 = 0, time.perf_counter()
+    while True:  # whole steps, repeated until about ten seconds of CPU work
+        paged.paged_decode_append(d["q"], step.q_dtype, d["k_new"], d["v_new"], step.k_cache, step.v_cache,
+                                  step.cache_dtype, d["block_table"], d["cache_seqlens"], step.scale,
+                                  step.k_scale, step.v_scale)
+        reps += 1
+        secs = time.perf_counter() - t0
+        if secs >= min_seconds:
+            break
+    return {"value": round(reps * algorithmic_bytes / secs / 1e9, 4), "unit": "GB/s",
             "cores": min(cores, blas_threads), "kind": "oracle",
-            "sample": (f"one whole step of the same workload (write of {step.num_tokens} tokens + "
-                       f"decode of {len(d['seq_ids'])} sequences), fp64 numpy, {secs:.2f} s; "
+            "sample": (f"{reps} whole steps of the same workload (append of {len(d['seq_ids'])} tokens + "
+                       f"decode of {len(d['seq_ids'])} sequences), fp64 numpy, {secs:.1f} s; "
                        f"BLAS threads {blas_threads}, host CPUs available {cores}")}
 
 
@@ -319,11 +328,16 @@ def main():
               flush=True)
         return
 
-    print("[bench] llama8b_decode", flush=True)
-    step, main_res = measure("llama8b_decode", args.steps, args.warmup, args.split_keys)
+    # The headline step stores its 64 new tokens with the appending decode
+    # (one call for write + attention, the decode path's in-place update);
+    # the same step with the slot-map write and the plain decode as two calls
+    # is measured next to it.
+    print("[bench] llama8b_decode (appending decode)", flush=True)
+    step, main_res = measure("llama8b_decode", args.steps, args.warmup, args.split_keys, append=True)
     step_bytes = main_res["write_bytes"] + main_res["decode_bytes"]
     value = step_bytes / (main_res["ms_per_step"] * 1e6)
     d = step.decode_inputs()
+    achieved = main_res["decode_bytes"] / (main_res["region_ms_per_step"] * 1e6)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -338,23 +352,32 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, random block permutation)",
         "config": {"workload": "llama8b_decode: Llama-3.1-8B-shaped single-layer decode step "
-                               "(kv write + paged decode)",
+                               "(kv write + paged decode, one appending-decode call)",
                    "batch": int(len(d["seq_ids"])), "num_heads": step.num_heads,
                    "num_kv_heads": step.num_kv_heads, "head_dim": step.head_dim,
                    "block_size": step.block_size,
                    "context": "cached lengths U{512..4096} (+1 new token)",
                    "keys_total": int(d["cache_seqlens"].sum()),
                    "step_bytes": int(step_bytes)},
-        "roofline": {"kernel": "paged_decode call (stream-K plan on the matrix cores: decode_mfma_kernel + stream_merge_kernel)",
-                     "bound": "hbm", "achieved": round(main_res["decode_gbs"], 2),
+        # the timed steps are nothing but back-to-back appending-decode calls:
+        # HIP events around the whole timed region give the call's average
+        "roofline": {"kernel": "paged_decode_append call (stream-K plan on the matrix cores: "
+                               "decode_mfma_kernel<append> + stream_merge_kernel); bytes = decode + appended rows",
+                     "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(main_res["decode_gbs"] / HBM_PEAK_GBS, 4),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": decode_traffic(),
                      "algorithmic_bytes_per_launch": int(main_res["decode_bytes"]),
-                     "avg_launch_ms": round(main_res["decode_ms"], 5)},
+                     "avg_launch_ms": round(main_res["region_ms_per_step"], 5),
+                     "avg_launch_ms_single_call_events": round(main_res["decode_ms"], 5)},
         "kernels": {"llama8b_decode": {k: (round(v, 5) if isinstance(v, float) else v)
                                        for k, v in main_res.items()}},
     }
+    print("[bench] llama8b_decode (slot-map write + plain decode)", flush=True)
+    _, sep = measure("llama8b_decode", args.steps, args.warmup, args.split_keys)
+    line["kernels"]["llama8b_decode_separate_calls"] = {
+        **{k: (round(v, 5) if isinstance(v, float) else v) for k, v in sep.items()},
+        "step_gbs": round(step_bytes / (sep["ms_per_step"] * 1e6), 2)}
     if args.configs == "all":
         for name, kw in (("varlen_prefill_prefix", {}), ("llama70b_long_decode", {}),
                          ("mixed_fp8", {})):
