@@ -247,6 +247,38 @@ def copy_probe(reps=5, nbytes=512 << 20):
             "gbs": 2 * nbytes / (float(np.mean(ms)) * 1e6)}
 
 
+def measure_copy_blocks(steps, warmup, pairs=4096, num_blocks=12288):
+    """The copy-on-write block copy on Llama-3.1-8B-shaped blocks (16 tokens x
+    8 KV heads x 128, bf16: 32 KiB per block and cache): ``pairs`` random
+    (src, dst) pairs over a pool of ``num_blocks`` blocks (targets distinct,
+    never a source).  Algorithmic bytes: every copied byte read once and
+    written once."""
+    import torch
+    import paged_kv_cache_map_amd as pkv
+    rng = np.random.default_rng(5)
+    shape = (num_blocks, 16, 8, 128)
+    k = torch.empty(shape, dtype=torch.bfloat16, device="cuda").normal_()
+    v = torch.empty_like(k).normal_()
+    perm = rng.permutation(num_blocks)
+    pr = np.stack([rng.choice(perm[pairs:], size=pairs), perm[:pairs]], 1).astype(np.int32)
+    pt = torch.from_numpy(pr).cuda()
+    for _ in range(warmup):
+        pkv.copy_blocks(k, v, pt)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
+        pkv.copy_blocks(k, v, pt)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    nbytes = 2 * 2 * pairs * 16 * 8 * 128 * 2
+    del k, v
+    torch.cuda.empty_cache()
+    return {"pairs": pairs, "block_bytes_per_cache": 32768, "bytes": nbytes, "ms": round(ms, 5),
+            "gbs": round(nbytes / (ms * 1e6), 2), "frac_hbm": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4)}
+
+
 def copies_for(step):
     pool = step.k_cache.nbytes + step.v_cache.nbytes
     return max(1, math.ceil(ROTATE_BYTES / pool))
@@ -394,6 +426,8 @@ def main():
             "mixed_fp8_decode_gbs": line["kernels"]["mixed_fp8"]["decode_gbs"],
             "mixed_fp8_prefill_tflops": line["kernels"]["mixed_fp8"]["prefill_tflops"],
         }
+    print("[bench] copy_blocks", flush=True)
+    line["kernels"]["copy_blocks"] = measure_copy_blocks(max(5, args.steps), 2)
     if args.copy_probe:
         print("[bench] copy probe", flush=True)
         line["kernels"]["copy_probe"] = copy_probe()

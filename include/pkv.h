@@ -1,12 +1,15 @@
 /*
  * pkv.h -- C ABI of libpkv.so: attention over a paged KV cache on AMD MI355X
- * (gfx950).  Hand-written HIP kernels behind four calls:
+ * (gfx950).  Hand-written HIP kernels behind five calls:
  *
  *   pkv_kv_cache_write   scatter the step's new K/V rows into cache slots
  *   pkv_paged_decode     one query per sequence over its cached keys
  *   pkv_paged_decode_append  the same decode storing the step's new K/V rows
  *                        itself (one launch for write + decode)
  *   pkv_varlen_prefill   causal attention for a packed batch of query chunks
+ *   pkv_copy_blocks      copy-on-write of whole cache blocks
+ * and a host-side block manager (pkv_block_manager_*: allocation, sharing,
+ * copy-on-write decisions, prefix hashes).
  *
  * Page citations (titles as the pages give them):
  *   [KV-mgmt]   itan.pw, "効率的な KV キャッシュ管理と Attention 計算"
@@ -252,6 +255,89 @@ int pkv_varlen_prefill(void* out, const void* q, int q_dtype,
                        int32_t block_size, int32_t num_blocks,
                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t total_q, int32_t total_k, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Block management.  [ch15] section "PagedAttention：メモリを「ページ」で貸し出
+ * す": the cache is handed out block by block as sequences grow, blocks need
+ * not be contiguous, and answers generated from one prompt share the prompt's
+ * blocks, a shared block being copied only when one of them must write into
+ * it (copy-on-write).  Section "プレフィックスキャッシュとchunked prefill":
+ * requests whose prompts begin alike reuse the cache of that prefix, found by
+ * a hash of each block's tokens.
+ * ---------------------------------------------------------------------------
+ */
+
+/*
+ * pkv_copy_blocks -- the copy-on-write data move: for each pair i, block
+ * block_pairs[2 i] of k_cache and of v_cache is copied to block
+ * block_pairs[2 i + 1] (the caches as above, num_blocks blocks of
+ * block_size * num_kv_heads * head_dim elements of cache_dtype).
+ *   block_pairs  [num_pairs, 2] int32 (src, dst), device.  Targets must be
+ *                distinct and no target may be a source of another pair
+ *                (the pairs run concurrently); a pair naming a block outside
+ *                [0, num_blocks) moves nothing.  Under PKV_VALIDATE=1 such
+ *                pairs are rejected.
+ * Errors: PKV_ERR_INVALID (NULL pointers, non-positive sizes, misaligned
+ * caches); PKV_ERR_UNSUPPORTED (unknown dtype, a block size in bytes that is
+ * not a multiple of 16 or not below 2 GiB).  num_pairs == 0 is a no-op.
+ */
+int pkv_copy_blocks(void* k_cache, void* v_cache, int cache_dtype, int32_t num_blocks,
+                    int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                    const int32_t* block_pairs, int32_t num_pairs, void* stream);
+
+/*
+ * pkv_block_manager -- host-side allocator of the physical blocks of one
+ * cache pool (plain host memory and host calls; no device access; not
+ * thread-safe).  Every block has a count of holders (sequences whose block
+ * table names it).  A block nobody holds is free; if it carries a registered
+ * prefix hash it stays findable by pkv_block_manager_lookup until it is
+ * handed out again (free blocks without a hash go first; among hashed ones
+ * the one released longest ago).  Calls return PKV_OK, or PKV_ERR_INVALID
+ * with nothing changed (NULL arguments, blocks outside the pool, releasing a
+ * block more often than it is held, no free block left); they do not set
+ * pkv_last_error.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* A manager of num_blocks blocks of block_size tokens, all free; NULL on bad sizes. */
+pkv_block_manager* pkv_block_manager_create(int32_t num_blocks, int32_t block_size);
+void pkv_block_manager_destroy(pkv_block_manager* m);
+/* Blocks that pkv_block_manager_allocate can hand out now (-1 for NULL). */
+int32_t pkv_block_manager_num_free(const pkv_block_manager* m);
+/* Holders of a block (-1 outside the pool). */
+int32_t pkv_block_manager_refcount(const pkv_block_manager* m, int32_t block);
+/* n free blocks into out_blocks (host array), each now held once. */
+int pkv_block_manager_allocate(pkv_block_manager* m, int32_t n, int32_t* out_blocks);
+/* One more holder for each listed block (all must be held already). */
+int pkv_block_manager_share(pkv_block_manager* m, const int32_t* blocks, int32_t n);
+/* One holder less for each listed block; a block no longer held becomes free. */
+int pkv_block_manager_release(pkv_block_manager* m, const int32_t* blocks, int32_t n);
+/* A child sequence sharing the parent's blocks: child_row (host, max_blocks_per_seq
+ * entries) = the parent's first ceil(num_tokens / block_size) entries, the
+ * rest -1; each shared block gains a holder. */
+int pkv_block_manager_fork(pkv_block_manager* m, const int32_t* parent_row, int32_t num_tokens,
+                           int32_t* child_row, int32_t max_blocks_per_seq);
+/* Room for a sequence's next token at position num_tokens (its block-table
+ * row, host, is updated in place): a fresh block when the position opens a
+ * logical block; when the block holding it is shared or carries a registered
+ * prefix, a fresh block replaces it in this row and out_copy = {old, new}
+ * names the copy to make with pkv_copy_blocks before the token is written
+ * (else out_copy = {-1, -1}).  *out_slot = the token's cache slot, the
+ * slot_map entry of pkv_kv_cache_write. */
+int pkv_block_manager_append_slot(pkv_block_manager* m, int32_t* table_row, int32_t max_blocks_per_seq,
+                                  int32_t num_tokens, int32_t* out_slot, int32_t* out_copy);
+/* Hash of a full block of token ids chained to the hash of the blocks before
+ * it (0 for the first block): 64-bit FNV-1a over the parent hash and the
+ * ids, little-endian. */
+uint64_t pkv_block_hash(uint64_t parent_hash, const int32_t* tokens, int32_t num_tokens);
+/* The block registered for a prefix hash, now held once more (a free one is
+ * taken back from the free blocks), or -1. */
+int32_t pkv_block_manager_lookup(pkv_block_manager* m, uint64_t hash);
+/* Register a held, full block under a prefix hash.  Returns PKV_OK, 1 when
+ * another block already carries that hash (nothing changed), or
+ * PKV_ERR_INVALID. */
+int pkv_block_manager_register(pkv_block_manager* m, int32_t block, uint64_t hash);
 
 #ifdef __cplusplus
 }

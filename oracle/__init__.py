@@ -38,6 +38,14 @@ Parity status per function (pins live in ``tests/test_oracle*.py``):
   ``scaled_dot_product_attention`` in float64, by the exact special cases
   (single visible key, equal keys, empty rows) and by paging invariants.
 * ``kvsize.*``: pinned by the figures [ch15] prints.
+* ``paged.paged_decode_append``: pinned by the decode worked example (the
+  new rows land at the derived slots and nowhere else; outputs equal float64
+  SDPA over the keys walked through the printed table) and by the empty
+  history case (the output is the new V row).
+* ``blocks.BlockModel`` / ``blocks.copy_blocks``: pinned by the copy-on-write
+  behaviour [ch15] describes (a fork shares every block; the first write to a
+  shared block copies exactly that block and leaves the other holder's
+  bytes as they were) on hand-made scenarios checked by other code.
 """
 
-from . import e4m3, kvsize, paged  # noqa: F401
+from . import blocks, e4m3, kvsize, paged  # noqa: F401

@@ -13,7 +13,9 @@ Calls (same names as the C entry points without the ``pkv_`` prefix):
 * :func:`paged_decode`   -- one query per sequence through the block table;
 * :func:`paged_decode_append` -- the same decode storing the step's new K/V
   rows itself (write + decode in one call);
-* :func:`varlen_prefill` -- causal attention for a packed batch of chunks.
+* :func:`varlen_prefill` -- causal attention for a packed batch of chunks;
+* :func:`copy_blocks`    -- copy-on-write of whole cache blocks;
+* :class:`BlockManager`  -- the host-side block allocator (``pkv_block_manager_*``).
 """
 
 import ctypes
@@ -64,6 +66,33 @@ def _load_library():
     lib.pkv_varlen_prefill.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp,
                                        i32, i32, i32, f32, i32, vp, i32, i32, i32, i32, i32, i32,
                                        i32, i32, vp]
+    lib.pkv_copy_blocks.restype = ctypes.c_int
+    lib.pkv_copy_blocks.argtypes = [vp, vp, ctypes.c_int, i32, i32, i32, i32, vp, i32, vp]
+    u64, ip = ctypes.c_uint64, ctypes.POINTER(ctypes.c_int32)
+    lib.pkv_block_manager_create.restype = vp
+    lib.pkv_block_manager_create.argtypes = [i32, i32]
+    lib.pkv_block_manager_destroy.restype = None
+    lib.pkv_block_manager_destroy.argtypes = [vp]
+    lib.pkv_block_manager_num_free.restype = i32
+    lib.pkv_block_manager_num_free.argtypes = [vp]
+    lib.pkv_block_manager_refcount.restype = i32
+    lib.pkv_block_manager_refcount.argtypes = [vp, i32]
+    lib.pkv_block_manager_allocate.restype = ctypes.c_int
+    lib.pkv_block_manager_allocate.argtypes = [vp, i32, ip]
+    lib.pkv_block_manager_share.restype = ctypes.c_int
+    lib.pkv_block_manager_share.argtypes = [vp, ip, i32]
+    lib.pkv_block_manager_release.restype = ctypes.c_int
+    lib.pkv_block_manager_release.argtypes = [vp, ip, i32]
+    lib.pkv_block_manager_fork.restype = ctypes.c_int
+    lib.pkv_block_manager_fork.argtypes = [vp, ip, i32, ip, i32]
+    lib.pkv_block_manager_append_slot.restype = ctypes.c_int
+    lib.pkv_block_manager_append_slot.argtypes = [vp, ip, i32, i32, ip, ip]
+    lib.pkv_block_hash.restype = u64
+    lib.pkv_block_hash.argtypes = [u64, ip, i32]
+    lib.pkv_block_manager_lookup.restype = i32
+    lib.pkv_block_manager_lookup.argtypes = [vp, u64]
+    lib.pkv_block_manager_register.restype = ctypes.c_int
+    lib.pkv_block_manager_register.argtypes = [vp, i32, u64]
     return lib
 
 
@@ -221,6 +250,106 @@ def varlen_prefill(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
         int(max_seqlen_k), float(softmax_scale), int(bool(causal)), _ptr(block_table), maxblk, bs, nb,
         hq, hkv, d, total_q, total_k, _stream(stream)))
     return out
+
+
+def copy_blocks(k_cache, v_cache, block_pairs, stream=None):
+    """Copy block ``src`` to block ``dst`` of both caches for every row
+    ``(src, dst)`` of ``block_pairs`` ([n, 2] int32, device)."""
+    import torch
+    _require(k_cache.is_contiguous() and v_cache.is_contiguous() and k_cache.dim() == 4 and
+             v_cache.shape == k_cache.shape, "caches must be contiguous [num_blocks, block_size, Hkv, D]")
+    _require(block_pairs.dtype == torch.int32 and block_pairs.is_contiguous() and
+             (block_pairs.numel() == 0 or (block_pairs.dim() == 2 and block_pairs.shape[1] == 2)),
+             "block_pairs must be contiguous int32 [n, 2]")
+    nb, bs, hkv, d = k_cache.shape
+    n = block_pairs.shape[0] if block_pairs.numel() else 0
+    _check(library().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), nb, bs, hkv, d,
+                                     _ptr(block_pairs), n, _stream(stream)))
+
+
+def _i32_array(values):
+    values = list(values)
+    return (ctypes.c_int32 * max(1, len(values)))(*values), len(values)
+
+
+class BlockManager:
+    """Host-side allocator of a pool's physical blocks (``pkv_block_manager_*``):
+    reference counts, forks that share blocks, copy-on-write decisions and
+    prefix hashes.  Block-table rows are plain Python lists of ints here."""
+
+    def __init__(self, num_blocks, block_size):
+        self._lib = library()
+        self._h = self._lib.pkv_block_manager_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise ValueError("num_blocks and block_size must be positive")
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def close(self):
+        if self._h:
+            self._lib.pkv_block_manager_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+    def _ok(self, code, what):
+        if code != OK:
+            raise PkvError(code, f"block manager: {what} refused")
+
+    @property
+    def num_free(self):
+        return int(self._lib.pkv_block_manager_num_free(self._h))
+
+    def refcount(self, block):
+        return int(self._lib.pkv_block_manager_refcount(self._h, int(block)))
+
+    def allocate(self, n):
+        arr, _ = _i32_array([0] * n)
+        self._ok(self._lib.pkv_block_manager_allocate(self._h, int(n), arr), f"allocate({n})")
+        return list(arr)[:n]
+
+    def share(self, blocks):
+        arr, n = _i32_array(blocks)
+        self._ok(self._lib.pkv_block_manager_share(self._h, arr, n), "share")
+
+    def release(self, blocks):
+        arr, n = _i32_array(blocks)
+        self._ok(self._lib.pkv_block_manager_release(self._h, arr, n), "release")
+
+    def fork(self, parent_row, num_tokens):
+        parent, width = _i32_array(parent_row)
+        child, _ = _i32_array([-1] * width)
+        self._ok(self._lib.pkv_block_manager_fork(self._h, parent, int(num_tokens), child, width), "fork")
+        return list(child)[:width]
+
+    def append_slot(self, row, num_tokens):
+        """Slot of the token at position ``num_tokens``; ``row`` (a list) is
+        updated in place.  Returns (slot, copy) with copy = (src, dst) or None."""
+        arr, width = _i32_array(row)
+        slot = ctypes.c_int32(0)
+        copy = (ctypes.c_int32 * 2)()
+        self._ok(self._lib.pkv_block_manager_append_slot(self._h, arr, width, int(num_tokens),
+                                                         ctypes.byref(slot), copy), "append_slot")
+        row[:] = list(arr)[:width]
+        return int(slot.value), (None if copy[0] < 0 else (int(copy[0]), int(copy[1])))
+
+    def lookup(self, block_hash):
+        return int(self._lib.pkv_block_manager_lookup(self._h, int(block_hash)))
+
+    def register(self, block, block_hash):
+        code = self._lib.pkv_block_manager_register(self._h, int(block), int(block_hash))
+        if code not in (OK, 1):
+            self._ok(code, "register")
+        return code == OK
+
+
+def block_hash(parent_hash, tokens):
+    """Chained hash of one full block of token ids (``pkv_block_hash``)."""
+    arr, n = _i32_array(tokens)
+    return int(library().pkv_block_hash(int(parent_hash), arr, n))
 
 
 def version():

@@ -20,8 +20,8 @@ OUT = PKG / "libpkv.so"
 BUILD = ROOT / "_build"
 ROCM = pathlib.Path(os.environ.get("ROCM_PATH", "/opt/rocm"))
 
-HIP_SOURCES = ["kv_write.hip", "paged_decode.hip", "varlen_prefill.hip"]
-HOST_SOURCES = ["pkv_api.cpp", "pkv_plan.cpp"]
+HIP_SOURCES = ["kv_write.hip", "paged_decode.hip", "varlen_prefill.hip", "block_copy.hip"]
+HOST_SOURCES = ["pkv_api.cpp", "pkv_plan.cpp", "pkv_blocks.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

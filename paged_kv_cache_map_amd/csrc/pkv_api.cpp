@@ -414,4 +414,47 @@ int pkv_varlen_prefill(void* out, const void* q, int q_dtype, const void* k, con
   return launch_status(pkv::launch_varlen_prefill(a, s), "varlen_prefill");
 }
 
+int pkv_copy_blocks(void* k_cache, void* v_cache, int cache_dtype, int32_t num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim, const int32_t* block_pairs, int32_t num_pairs,
+                    void* stream) {
+  if (num_pairs < 0) return fail(PKV_ERR_INVALID, "copy_blocks: num_pairs < 0");
+  if (num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_ERR_INVALID, "copy_blocks: sizes must be positive");
+  const int eb = elt_bytes(cache_dtype);
+  if (eb == 0) return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: unknown cache dtype %d", cache_dtype);
+  const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * eb;
+  if (block_bytes % 16 != 0 || block_bytes >= ((int64_t)1 << 31))
+    return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: block of %lld bytes (must be a multiple of 16 below 2 GiB)",
+                (long long)block_bytes);
+  if (!k_cache || !v_cache || (!block_pairs && num_pairs > 0))
+    return fail(PKV_ERR_INVALID, "copy_blocks: NULL pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID, "copy_blocks: caches must be 16-byte aligned");
+  if (num_pairs == 0) return ok();
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_mode()) {
+    std::vector<int32_t> pairs;
+    if (!fetch(pairs, block_pairs, 2 * (int64_t)num_pairs, s))
+      return fail(PKV_ERR_LAUNCH, "copy_blocks: could not read the pairs");
+    std::unordered_set<int32_t> dsts, srcs;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+      const int32_t a = pairs[2 * i], b = pairs[2 * i + 1];
+      if (a < 0 || a >= num_blocks || b < 0 || b >= num_blocks)
+        return fail(PKV_ERR_INVALID, "copy_blocks: pair %d (%d, %d) outside the pool of %d", i, a, b, num_blocks);
+      if (!dsts.insert(b).second) return fail(PKV_ERR_INVALID, "copy_blocks: block %d written twice", b);
+      srcs.insert(a);
+    }
+    for (int32_t b : dsts)
+      if (srcs.count(b)) return fail(PKV_ERR_INVALID, "copy_blocks: block %d is both a source and a target", b);
+  }
+  pkv::CopyBlocksArgs a;
+  a.k_cache = (uint8_t*)k_cache;
+  a.v_cache = (uint8_t*)v_cache;
+  a.pairs = block_pairs;
+  a.block_bytes = block_bytes;
+  a.num_pairs = num_pairs;
+  a.num_blocks = num_blocks;
+  return launch_status(pkv::launch_copy_blocks(a, s), "copy_blocks");
+}
+
 }  // extern "C"

@@ -119,4 +119,15 @@ struct PrefillArgs {
 
 hipError_t launch_varlen_prefill(const PrefillArgs& a, hipStream_t stream);
 
+struct CopyBlocksArgs {
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  const int32_t* pairs;  // [num_pairs, 2] (src, dst) block ids, device
+  int64_t block_bytes;   // bytes of one block of one cache (a multiple of 16, < 2^31)
+  int32_t num_pairs;
+  int32_t num_blocks;
+};
+
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
+
 }  // namespace pkv

@@ -18,11 +18,12 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
 
 
-def test_header_declares_the_three_calls():
+def test_header_declares_the_calls():
     names = declared_functions()
     for want in ("pkv_kv_cache_write", "pkv_paged_decode", "pkv_paged_decode_append",
                  "pkv_varlen_prefill", "pkv_paged_decode_workspace_size", "pkv_last_error",
-                 "pkv_version"):
+                 "pkv_version", "pkv_copy_blocks", "pkv_block_manager_create",
+                 "pkv_block_manager_append_slot", "pkv_block_hash"):
         assert want in names
 
 
@@ -129,6 +130,31 @@ def append(**kw):
 def test_append_rejects(kw, code):
     assert append(**kw) == code
     assert b"paged_decode_append" in pkv.library().pkv_last_error()
+
+
+def copy_blocks(**kw):
+    a = dict(kc=FAKE, vc=FAKE, cdt=pkv.BF16, nb=10, bs=16, hkv=8, d=128, pairs=FAKE, n=3, stream=NULL)
+    a.update(kw)
+    return pkv.library().pkv_copy_blocks(a["kc"], a["vc"], a["cdt"], a["nb"], a["bs"], a["hkv"], a["d"],
+                                         a["pairs"], a["n"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), pkv.ERR_INVALID),
+    (dict(nb=0), pkv.ERR_INVALID),
+    (dict(kc=NULL), pkv.ERR_INVALID),
+    (dict(pairs=NULL), pkv.ERR_INVALID),
+    (dict(vc=ODD), pkv.ERR_INVALID),
+    (dict(cdt=7), pkv.ERR_UNSUPPORTED),
+    (dict(cdt=pkv.FP8_E4M3, bs=1, hkv=1, d=8), pkv.ERR_UNSUPPORTED),   # an 8-byte block
+])
+def test_copy_blocks_rejects(kw, code):
+    assert copy_blocks(**kw) == code
+    assert b"copy_blocks" in pkv.library().pkv_last_error()
+
+
+def test_copy_blocks_no_pairs_is_a_no_op():
+    assert copy_blocks(n=0, pairs=NULL) == pkv.OK
 
 
 def prefill(**kw):
