@@ -27,7 +27,10 @@ namespace pkv {
 namespace {
 
 constexpr int kTokensPerWg = 4;  // one token per wave
-constexpr int kUnroll = 4;       // source pieces in flight per lane per pass
+#ifndef PKV_WRITE_UNROLL
+#define PKV_WRITE_UNROLL 4
+#endif
+constexpr int kUnroll = PKV_WRITE_UNROLL;  // source pieces in flight per lane per pass
 constexpr int kWord3 = 0x00020000;
 constexpr int kDropped = 0x7ffffff0;  // a buffer offset past any row: the store is dropped
 
