@@ -42,11 +42,17 @@
  *   block_table[b][j / block_size] * block_size + j % block_size.
  *
  * Element types: PKV_F32 (IEEE fp32), PKV_BF16 (bfloat16) and, for caches
- * only, PKV_FP8_E4M3 (OCP E4M3 "FN": bias 7, max 448, S.1111.111 = NaN) with
- * one fp32 scale per KV head for K and one for V: stored code = e4m3(x /
- * scale), value = code * scale.  (The pages only say an FP8 cache halves the
- * memory, [ch15] "KVキャッシュはどれくらいメモリを食う？"; the format is the
- * gfx950-native one.)
+ * only, two one-byte types with one fp32 scale per KV head for K and one for
+ * V ([ch15] "KVキャッシュはどれくらいメモリを食う？": an FP8 or INT8 cache takes
+ * exactly half the memory of a 16-bit one):
+ *   PKV_FP8_E4M3 (OCP E4M3 "FN": bias 7, max 448, S.1111.111 = NaN): stored
+ *     code = e4m3(x / scale), round to nearest even, saturating to +-448,
+ *     NaN -> 0x7F; value = code * scale.  (The format is the gfx950-native one.)
+ *   PKV_INT8 (two's complement): stored code = round-to-nearest-even of
+ *     x / scale saturated to [-127, 127] (symmetric; -128 is never stored),
+ *     NaN -> 0; value = code * scale.
+ * In both, x / scale is an IEEE fp32 division of the fp32 value of x by the
+ * head's fp32 scale.  FP8 and INT8 caches are read with BF16 queries.
  *
  * Supported shapes: head_dim in {64, 128}; block_size a power of two in
  * [8, 256]; num_heads a multiple of num_kv_heads with group size
@@ -82,6 +88,7 @@ extern "C" {
 #define PKV_F32 0
 #define PKV_BF16 1
 #define PKV_FP8_E4M3 2
+#define PKV_INT8 3
 
 /* Message of the last failing call on this thread ("" if none).  The string
  * is owned by the library and valid until the next call on this thread. */
@@ -103,13 +110,12 @@ const char* pkv_version(void);
  *                   row width num_kv_heads * head_dim).
  *   k_cache,v_cache caches of cache_dtype, layout above, num_slots =
  *                   num_blocks * block_size rows; modified in place.
- *   k_scale,v_scale [num_kv_heads] fp32, required iff cache_dtype is FP8,
- *                   else ignored (may be NULL).
+ *   k_scale,v_scale [num_kv_heads] fp32, required iff cache_dtype is FP8 or
+ *                   INT8, else ignored (may be NULL).
  *   slot_map        [num_tokens]; -1 = skip the token.  Slots must be
  *                   distinct (two tokens writing one slot race).
- * Supported pairs: F32->F32, BF16->BF16 (bit copies), F32->FP8 and BF16->FP8
- * (code = e4m3 round-to-nearest-even of the IEEE fp32 quotient x / scale,
- * saturating to +-448, NaN -> 0x7F).
+ * Supported pairs: F32->F32, BF16->BF16 (bit copies), F32 or BF16 -> FP8 or
+ * INT8 (the encodings above).
  * Pointers and byte strides must be 16-byte aligned.
  * Errors: PKV_ERR_INVALID for NULL pointers, num_tokens < 0, stride below the
  * row width, misalignment, non-positive sizes; PKV_ERR_UNSUPPORTED for other
@@ -140,8 +146,9 @@ size_t pkv_paged_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t
  *
  *   out   [batch, num_heads, head_dim] of q_dtype, written.
  *   q     [batch, num_heads, head_dim] of q_dtype (F32 or BF16), contiguous.
- *   k_cache, v_cache of cache_dtype (F32 with F32 q; BF16 or FP8 with BF16 q).
- *   k_scale, v_scale [num_kv_heads] fp32, required iff FP8.
+ *   k_cache, v_cache of cache_dtype (F32 with F32 q; BF16, FP8 or INT8 with
+ *               BF16 q).
+ *   k_scale, v_scale [num_kv_heads] fp32, required iff FP8 or INT8.
  *   block_table [batch, max_blocks_per_seq], row-major; entries past the
  *               sequence's last block are never read (may be -1).  An entry
  *               inside the sequence that is negative or >= num_blocks is read
@@ -192,7 +199,8 @@ int pkv_paged_decode(void* out, const void* q, int q_dtype,
  * other plans launch a small append kernel before the decode kernels.
  *
  *   k_new, v_new  [batch, num_kv_heads, head_dim] of q_dtype (the cache's
- *                 element type for F32/BF16 caches; BF16 for FP8 caches),
+ *                 element type for F32/BF16 caches; BF16 for FP8 and INT8
+ *                 caches),
  *                 heads and dims contiguous, sequences k_new_stride /
  *                 v_new_stride ELEMENTS apart (>= num_kv_heads * head_dim),
  *                 16-byte aligned.
@@ -237,8 +245,8 @@ int pkv_paged_decode_append(void* out, const void* q, int q_dtype,
  *         blocks of block_size); request b has Lk = cu_seqlens_k[b+1] -
  *         cu_seqlens_k[b] keys read through block_table row b
  *         ([batch, max_blocks_per_seq]).
- *   kv_dtype  BF16 with BF16 q (contiguous or paged), FP8 with BF16 q (paged
- *             only, k_scale/v_scale required), F32 with F32 q.
+ *   kv_dtype  BF16 with BF16 q (contiguous or paged), FP8 or INT8 with BF16
+ *             q (paged only, k_scale/v_scale required), F32 with F32 q.
  *   causal  1: query row i of a request with Lq queries and Lk keys sees keys
  *           j <= i + Lk - Lq (aligned to the end, so a chunk after a cached
  *           prefix sees the whole prefix); 0: sees all Lk keys.

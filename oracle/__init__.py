@@ -38,6 +38,10 @@ Parity status per function (pins live in ``tests/test_oracle*.py``):
   ``scaled_dot_product_attention`` in float64, by the exact special cases
   (single visible key, equal keys, empty rows) and by paging invariants.
 * ``kvsize.*``: pinned by the figures [ch15] prints.
+* ``int8.encode`` / ``int8.decode``: pinned by the definition's spot values
+  (ties to even, saturation at +-127, NaN -> 0) and by torch's
+  round-half-to-even on the same fp32 quotients; the encoding itself is a
+  reading (the pages only say an INT8 cache halves the memory).
 * ``paged.paged_decode_append``: pinned by the decode worked example (the
   new rows land at the derived slots and nowhere else; outputs equal float64
   SDPA over the keys walked through the printed table) and by the empty
@@ -48,4 +52,4 @@ Parity status per function (pins live in ``tests/test_oracle*.py``):
   bytes as they were) on hand-made scenarios checked by other code.
 """
 
-from . import blocks, e4m3, kvsize, paged  # noqa: F401
+from . import blocks, e4m3, int8, kvsize, paged  # noqa: F401

@@ -6,7 +6,8 @@ Storage conventions (host numpy arrays, the same bits the GPU receives):
 
 * ``"f32"``  -> ``np.float32`` values;
 * ``"bf16"`` -> ``np.uint16`` bit patterns (the upper half of an IEEE fp32);
-* ``"fp8"``  -> ``np.uint8`` OCP E4M3 codes, one fp32 scale per KV head.
+* ``"fp8"``  -> ``np.uint8`` OCP E4M3 codes, one fp32 scale per KV head;
+* ``"int8"`` -> ``np.int8`` codes, one fp32 scale per KV head.
 
 Cache layout: one K and one V tensor per layer, each ``[num_blocks,
 block_size, num_kv_heads, head_dim]`` and contiguous, so that cache slot
@@ -20,7 +21,7 @@ stride to equal that width; [paged-doc] "ページド・アテンション", sec
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, int8
 
 # ---------------------------------------------------------------------------
 # storage <-> float64
@@ -43,11 +44,12 @@ def to_f64(arr: np.ndarray, dtype: str, scale=None) -> np.ndarray:
         return np.asarray(arr, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
         return bf16_bits_to_f64(arr)
-    if dtype == "fp8":
+    if dtype in ("fp8", "int8"):
         if scale is None:
-            raise ValueError("fp8 storage needs a per-head scale")
+            raise ValueError(f"{dtype} storage needs a per-head scale")
         per_head = np.asarray(scale, dtype=np.float32).astype(np.float64)
-        return e4m3.decode(arr) * per_head[:, None]
+        codes = e4m3.decode(arr) if dtype == "fp8" else int8.decode(arr)
+        return codes * per_head[:, None]
     raise ValueError(f"unknown storage dtype {dtype!r}")
 
 
@@ -148,11 +150,11 @@ def kv_cache_write(k, v, k_cache, v_cache, slot_map, src_dtype: str, cache_dtype
 def _store_row(row, src_dtype, cache_dtype, scale):
     if cache_dtype == src_dtype and cache_dtype in ("f32", "bf16"):
         return row
-    if cache_dtype == "fp8":
+    if cache_dtype in ("fp8", "int8"):
         x = _to_f32_values(row, src_dtype)                       # [hkv, d] float32
         s = np.asarray(scale, dtype=np.float32)[:, None]
         quotient = (x / s).astype(np.float32)                     # IEEE fp32 division
-        return e4m3.encode_fast(quotient)
+        return e4m3.encode_fast(quotient) if cache_dtype == "fp8" else int8.encode(quotient)
     raise ValueError(f"unsupported write {src_dtype} -> {cache_dtype}")
 
 
@@ -338,8 +340,8 @@ def varlen_prefill(q, q_dtype, k, v, kv_dtype, cu_seqlens_q, cu_seqlens_k, scale
 
 
 def _rows_to_f64(rows, dtype, scale, head=None):
-    if dtype == "fp8":
+    if dtype in ("fp8", "int8"):
         s = np.asarray(scale, dtype=np.float32)
         s = s if head is None else s[head:head + 1]
-        return to_f64(rows, "fp8", s)
+        return to_f64(rows, dtype, s)
     return to_f64(rows, dtype)

@@ -27,7 +27,7 @@ import pathlib
 LIB_PATH = pathlib.Path(os.environ.get("PKV_LIBRARY") or
                         pathlib.Path(__file__).resolve().with_name("libpkv.so"))
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, INT8 = 0, 1, 2, 3
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_LAUNCH = 0, -1, -2, -3
 
 
@@ -120,6 +120,8 @@ def _dtype_code(t):
         return BF16
     if t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return FP8_E4M3
+    if t.dtype == torch.int8:
+        return INT8
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -141,8 +143,9 @@ def _require(cond, msg):
 def kv_cache_write(k, v, k_cache, v_cache, slot_map, k_scale=None, v_scale=None, stream=None):
     """Store ``k[t]`` and ``v[t]`` ([T, Hkv, D]) at cache slot ``slot_map[t]`` (-1 skips).
 
-    Caches are ``[num_blocks, block_size, Hkv, D]`` (fp32, bf16, or uint8 /
-    float8_e4m3fn codes with per-head fp32 ``k_scale``/``v_scale``).
+    Caches are ``[num_blocks, block_size, Hkv, D]`` (fp32, bf16, uint8 /
+    float8_e4m3fn E4M3 codes or int8 codes, the one-byte ones with per-head
+    fp32 ``k_scale``/``v_scale``).
     """
     _require(k.dim() == 3 and v.shape == k.shape, "k and v must be [T, Hkv, D]")
     _require(k.stride(2) == 1 and k.stride(1) == k.shape[2], "k heads/dims must be contiguous")

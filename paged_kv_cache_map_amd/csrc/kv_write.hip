@@ -18,7 +18,9 @@
 //
 // For an fp8 cache each source element x becomes e4m3(x / scale[head]) with an
 // IEEE fp32 division (the library is built with correctly rounded division)
-// and round-to-nearest-even, saturating at +-448.
+// and round-to-nearest-even, saturating at +-448; for an int8 cache the
+// quotient is rounded to the nearest integer (ties to even) and saturated to
+// [-127, 127].
 
 #include "pkv_device.hpp"
 #include "pkv_internal.h"
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(WriteArgs a) {
       const bool is_k = q < pieces;
       const bool is_v = !is_k && q < 2 * pieces;
       float sc = 1.0f;
-      if constexpr (DST == kFP8) {
+      if constexpr (scaled8(DST)) {
         const int qq = min(q, 2 * pieces - 1);
         const int e = (is_k ? qq : qq - pieces) * elems_per_piece;
         sc = (is_k ? a.k_scale : a.v_scale)[e / a.head_dim];
@@ -112,6 +114,10 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((kv_write_kernel<kBF16, kFP8>), grid, block, 0, stream, a);
   } else if (a.src_dtype == kF32 && a.cache_dtype == kFP8) {
     hipLaunchKernelGGL((kv_write_kernel<kF32, kFP8>), grid, block, 0, stream, a);
+  } else if (a.src_dtype == kBF16 && a.cache_dtype == kI8) {
+    hipLaunchKernelGGL((kv_write_kernel<kBF16, kI8>), grid, block, 0, stream, a);
+  } else if (a.src_dtype == kF32 && a.cache_dtype == kI8) {
+    hipLaunchKernelGGL((kv_write_kernel<kF32, kI8>), grid, block, 0, stream, a);
   } else {
     return hipErrorInvalidValue;
   }

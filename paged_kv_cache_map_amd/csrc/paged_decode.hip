@@ -218,14 +218,14 @@ __device__ __forceinline__ float qk_partial(const uint4 (&k)[Cfg<CT, D, GW>::qk_
       const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc = dot2_bf16(qw[j], kw[j], acc);
-    } else if constexpr (CT == kFP8) {
+    } else if constexpr (scaled8(CT)) {
       const uint4 q0 = *reinterpret_cast<const uint4*>(q_h + (i * 64 + quarter * 16) * 2);
       const uint4 q1 = *reinterpret_cast<const uint4*>(q_h + (i * 64 + quarter * 16) * 2 + 16);
       const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc = dot2_bf16(qw[2 * j], e4m3x2_to_bf16x2<false>(kw[j]), acc);
-        acc = dot2_bf16(qw[2 * j + 1], e4m3x2_to_bf16x2<true>(kw[j]), acc);
+        acc = dot2_bf16(qw[2 * j], code8x2_to_bf16x2<CT, false>(kw[j]), acc);
+        acc = dot2_bf16(qw[2 * j + 1], code8x2_to_bf16x2<CT, true>(kw[j]), acc);
       }
     } else {
       const uint4 qv = *reinterpret_cast<const uint4*>(q_h + i * 64 + quarter * 16);
@@ -247,11 +247,11 @@ __device__ __forceinline__ void v_values(const uint32_t* w, float* out) {
       out[2 * j] = bf16_lo(w[j]);
       out[2 * j + 1] = bf16_hi(w[j]);
     }
-  } else if constexpr (CT == kFP8) {
+  } else if constexpr (scaled8(CT)) {
 #pragma unroll
     for (int j = 0; j < C::pv_vec / 4; ++j) {
-      const float2_t a = e4m3x2_to_f32x2<false>(w[j]);
-      const float2_t b = e4m3x2_to_f32x2<true>(w[j]);
+      const float2_t a = code8x2_to_f32x2<CT, false>(w[j]);
+      const float2_t b = code8x2_to_f32x2<CT, true>(w[j]);
       out[4 * j] = a.x;
       out[4 * j + 1] = a.y;
       out[4 * j + 2] = b.x;
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int split_key
   }
   float logit_scale = a.softmax_scale * kLog2e;
   float out_scale = 1.0f;
-  if constexpr (CT == kFP8) {
+  if constexpr (scaled8(CT)) {
     logit_scale *= a.k_scale[g];
     out_scale = a.v_scale[g];
   }
@@ -850,7 +850,7 @@ __global__ __launch_bounds__(kStreamThreads) void decode_stream_kernel(DecodeArg
     load_chunk_stream<CT, D, GW, SMALL>(A, c, cur, tbl_cur, lane);
     float logit_scale = base_scale, out_scale = 1.0f;
     const int g_cur = cur.gg / head_groups;
-    if constexpr (CT == kFP8) {
+    if constexpr (scaled8(CT)) {
       logit_scale *= a.k_scale[g_cur];
       out_scale = a.v_scale[g_cur];
     }
@@ -870,7 +870,7 @@ __global__ __launch_bounds__(kStreamThreads) void decode_stream_kernel(DecodeArg
       if (last) return false;
       if (nxt.b != cur.b || nxt.gg != cur.gg) {
         load_q<CT, D, GW>(q_w, a, c, nxt, lane);
-        if constexpr (CT == kFP8) {
+        if constexpr (scaled8(CT)) {
           const int g = nxt.gg / head_groups;
           logit_scale = base_scale * a.k_scale[g];
           out_scale = a.v_scale[g];
@@ -1020,7 +1020,7 @@ __device__ __forceinline__ void store_new(const DecodeArgs& a, const NewPiece& n
   if (blk < 0 || blk >= a.num_blocks || lane >= 2 * P) return;
   const bool is_v = lane >= P;
   float sc = 1.0f;
-  if constexpr (DST == kFP8) sc = ((cptr_f32)(is_v ? a.v_scale : a.k_scale))[n.g];
+  if constexpr (scaled8(DST)) sc = ((cptr_f32)(is_v ? a.v_scale : a.k_scale))[n.g];
   const int64_t slot = (int64_t)blk * a.block_size + (n.pos & (a.block_size - 1));
   // the caches are the caller's writable buffers (the decode kernels only read them)
   uint8_t* dst = const_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) + slot * ((int64_t)a.num_kv_heads * dst_row) +
@@ -1064,6 +1064,7 @@ hipError_t launch_append(const DecodeArgs& a, hipStream_t stream) {
   if (a.q_dtype == kF32 && a.cache_dtype == kF32) return launch_append_t<kF32, kF32>(a, stream);
   if (a.q_dtype == kBF16 && a.cache_dtype == kBF16) return launch_append_t<kBF16, kBF16>(a, stream);
   if (a.q_dtype == kBF16 && a.cache_dtype == kFP8) return launch_append_t<kBF16, kFP8>(a, stream);
+  if (a.q_dtype == kBF16 && a.cache_dtype == kI8) return launch_append_t<kBF16, kI8>(a, stream);
   return hipErrorInvalidValue;
 }
 
@@ -1162,12 +1163,14 @@ __device__ __forceinline__ float sum_quarters(float x) {
   return sum_halves(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
-// Sixteen E4M3 codes -> sixteen bf16 (exact), as two 8-element operands.
-__device__ __forceinline__ void e4m3x16_to_bf16(const uint4& x, uint4& lo, uint4& hi) {
-  lo = make_uint4(e4m3x2_to_bf16x2<false>(x.x), e4m3x2_to_bf16x2<true>(x.x), e4m3x2_to_bf16x2<false>(x.y),
-                  e4m3x2_to_bf16x2<true>(x.y));
-  hi = make_uint4(e4m3x2_to_bf16x2<false>(x.z), e4m3x2_to_bf16x2<true>(x.z), e4m3x2_to_bf16x2<false>(x.w),
-                  e4m3x2_to_bf16x2<true>(x.w));
+// Sixteen one-byte codes (E4M3 or int8) -> sixteen bf16 (exact), as two
+// 8-element operands.
+template <int CT>
+__device__ __forceinline__ void code8x16_to_bf16(const uint4& x, uint4& lo, uint4& hi) {
+  lo = make_uint4(code8x2_to_bf16x2<CT, false>(x.x), code8x2_to_bf16x2<CT, true>(x.x),
+                  code8x2_to_bf16x2<CT, false>(x.y), code8x2_to_bf16x2<CT, true>(x.y));
+  hi = make_uint4(code8x2_to_bf16x2<CT, false>(x.z), code8x2_to_bf16x2<CT, true>(x.z),
+                  code8x2_to_bf16x2<CT, false>(x.w), code8x2_to_bf16x2<CT, true>(x.w));
 }
 
 // Values every lane of a wave needs (lengths, block-table entries, scales)
@@ -1281,7 +1284,7 @@ __device__ __forceinline__ void unit_scales(Chunk<CT, D>& r, const DecodeArgs& a
   // masked keys stay at -inf instead of -inf * 0).
   float sc = a.softmax_scale;
   r.vs = 1.0f;
-  if constexpr (CT == kFP8) {
+  if constexpr (scaled8(CT)) {
     sc *= ((sptr_f32)a.k_scale)[p.gg];
     r.vs = ((sptr_f32)a.v_scale)[p.gg];
   }
@@ -1297,9 +1300,9 @@ template <int CT, int D, int SW>
 __device__ __forceinline__ void store_rows(const uint4& x, uint8_t* w, int row, int piece) {
   using G = Geo<CT, D>;
   const int sw = SW == 0 ? kswz<D>(row) : vswz<D>(row);
-  if constexpr (CT == kFP8) {
+  if constexpr (scaled8(CT)) {
     uint4 lo, hi;
-    e4m3x16_to_bf16(x, lo, hi);
+    code8x16_to_bf16<CT>(x, lo, hi);
     *reinterpret_cast<uint4*>(w + row * G::lds_row + (((2 * piece) ^ sw) << 4)) = lo;
     *reinterpret_cast<uint4*>(w + row * G::lds_row + (((2 * piece + 1) ^ sw) << 4)) = hi;
   } else {
@@ -1656,13 +1659,13 @@ __global__ __launch_bounds__(kStreamThreads, OCC) void decode_mfma_kernel(Decode
 // per SIMD; fp8 chunks take half that, and two of them fit two waves.
 template <int CT>
 constexpr int depth() {
-  return CT == kFP8 ? PKV_DECODE_DEPTH_FP8 : PKV_DECODE_DEPTH;
+  return scaled8(CT) ? PKV_DECODE_DEPTH_FP8 : PKV_DECODE_DEPTH;
 }
 
 // Waves per SIMD the kernel is compiled for.
 template <int CT>
 constexpr int occupancy() {
-  return CT == kFP8 ? PKV_DECODE_OCC_FP8 : PKV_DECODE_OCC;
+  return scaled8(CT) ? PKV_DECODE_OCC_FP8 : PKV_DECODE_OCC;
 }
 
 template <int CT, int D, int G, bool APPEND>
@@ -1777,6 +1780,7 @@ hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p, hipStre
   if (p.stream && p.mfma) {
     if (a.cache_dtype == kBF16) return append ? mfd::launch<kBF16, true>(a, stream) : mfd::launch<kBF16, false>(a, stream);
     if (a.cache_dtype == kFP8) return append ? mfd::launch<kFP8, true>(a, stream) : mfd::launch<kFP8, false>(a, stream);
+    if (a.cache_dtype == kI8) return append ? mfd::launch<kI8, true>(a, stream) : mfd::launch<kI8, false>(a, stream);
     return hipErrorInvalidValue;
   }
   if (append) {  // the other plans: the append kernel, then the decode as usual
@@ -1786,6 +1790,7 @@ hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p, hipStre
   if (a.cache_dtype == kF32) return launch_c<kF32>(a, p, stream);
   if (a.cache_dtype == kBF16) return launch_c<kBF16>(a, p, stream);
   if (a.cache_dtype == kFP8) return launch_c<kFP8>(a, p, stream);
+  if (a.cache_dtype == kI8) return launch_c<kI8>(a, p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -44,6 +44,7 @@ int elt_bytes(int dtype) {
     case PKV_F32: return 4;
     case PKV_BF16: return 2;
     case PKV_FP8_E4M3: return 1;
+    case PKV_INT8: return 1;
     default: return 0;
   }
 }
@@ -51,6 +52,9 @@ int elt_bytes(int dtype) {
 bool pow2_in(int32_t x, int32_t lo, int32_t hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 
 bool group_ok(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+// One-byte caches decoded as code x per-head scale.
+bool scaled_cache(int dtype) { return dtype == PKV_FP8_E4M3 || dtype == PKV_INT8; }
 
 // Synchronous copy of n int32 from the device (validation mode only).
 bool fetch(std::vector<int32_t>& dst, const int32_t* src, int64_t n, hipStream_t stream) {
@@ -113,7 +117,7 @@ int decode_common(const char* name, const NewRows& nr, void* out, const void* q,
   if (append && (!nr.k || !nr.v)) return fail(PKV_ERR_INVALID, "%s: NULL k_new or v_new", name);
   const bool pair_ok = (q_dtype == PKV_F32 && cache_dtype == PKV_F32) ||
                        (q_dtype == PKV_BF16 && cache_dtype == PKV_BF16) ||
-                       (q_dtype == PKV_BF16 && cache_dtype == PKV_FP8_E4M3);
+                       (q_dtype == PKV_BF16 && scaled_cache(cache_dtype));
   if (!pair_ok)
     return fail(PKV_ERR_UNSUPPORTED, "%s: unsupported q/cache dtypes %d/%d", name, q_dtype, cache_dtype);
   if (head_dim != 64 && head_dim != 128)
@@ -123,8 +127,8 @@ int decode_common(const char* name, const NewRows& nr, void* out, const void* q,
   if (!group_ok(num_heads / num_kv_heads))
     return fail(PKV_ERR_UNSUPPORTED, "%s: group size %d not in {1,2,4,8,16}", name,
                 num_heads / num_kv_heads);
-  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
-    return fail(PKV_ERR_INVALID, "%s: fp8 cache needs k_scale and v_scale", name);
+  if (scaled_cache(cache_dtype) && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID, "%s: fp8 and int8 caches need k_scale and v_scale", name);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(PKV_ERR_INVALID, "%s: q, out and caches must be 16-byte aligned", name);
   const int64_t row = (int64_t)num_kv_heads * head_dim;
@@ -219,8 +223,7 @@ int pkv_kv_cache_write(const void* k, int64_t k_token_stride, const void* v, int
     return fail(PKV_ERR_INVALID, "kv_cache_write: num_kv_heads, head_dim and num_slots must be positive");
   const bool pair_ok = (src_dtype == PKV_F32 && cache_dtype == PKV_F32) ||
                        (src_dtype == PKV_BF16 && cache_dtype == PKV_BF16) ||
-                       (src_dtype == PKV_BF16 && cache_dtype == PKV_FP8_E4M3) ||
-                       (src_dtype == PKV_F32 && cache_dtype == PKV_FP8_E4M3);
+                       ((src_dtype == PKV_BF16 || src_dtype == PKV_F32) && scaled_cache(cache_dtype));
   if (!pair_ok)
     return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write: unsupported dtype pair %d -> %d", src_dtype,
                 cache_dtype);
@@ -231,8 +234,8 @@ int pkv_kv_cache_write(const void* k, int64_t k_token_stride, const void* v, int
     return fail(PKV_ERR_INVALID, "kv_cache_write: token stride below the row width %lld", (long long)row);
   if (!k || !v || !k_cache || !v_cache || (!slot_map && num_tokens > 0))
     return fail(PKV_ERR_INVALID, "kv_cache_write: NULL pointer");
-  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
-    return fail(PKV_ERR_INVALID, "kv_cache_write: fp8 cache needs k_scale and v_scale");
+  if (scaled_cache(cache_dtype) && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID, "kv_cache_write: fp8 and int8 caches need k_scale and v_scale");
   const int sb = elt_bytes(src_dtype);
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
       (k_token_stride * sb) % 16 != 0 || (v_token_stride * sb) % 16 != 0)
@@ -337,11 +340,11 @@ int pkv_varlen_prefill(void* out, const void* q, int q_dtype, const void* k, con
   if (causal != 0 && causal != 1) return fail(PKV_ERR_INVALID, "varlen_prefill: causal must be 0 or 1");
   const bool paged = block_table != nullptr;
   const bool pair_ok = (q_dtype == PKV_BF16 && kv_dtype == PKV_BF16) ||
-                       (q_dtype == PKV_BF16 && kv_dtype == PKV_FP8_E4M3 && paged) ||
+                       (q_dtype == PKV_BF16 && scaled_cache(kv_dtype) && paged) ||
                        (q_dtype == PKV_F32 && kv_dtype == PKV_F32);
   if (!pair_ok)
     return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: unsupported q/kv dtypes %d/%d%s", q_dtype, kv_dtype,
-                paged ? "" : " (fp8 needs the paged cache)");
+                paged ? "" : " (fp8 and int8 need the paged cache)");
   if (head_dim != 64 && head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: head_dim %d not in {64, 128}", head_dim);
   if (!group_ok(num_heads / num_kv_heads))
@@ -354,8 +357,8 @@ int pkv_varlen_prefill(void* out, const void* q, int q_dtype, const void* k, con
     if (max_blocks_per_seq <= 0 || num_blocks <= 0)
       return fail(PKV_ERR_INVALID, "varlen_prefill: max_blocks_per_seq and num_blocks must be positive");
   }
-  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale))
-    return fail(PKV_ERR_INVALID, "varlen_prefill: fp8 cache needs k_scale and v_scale");
+  if (scaled_cache(kv_dtype) && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID, "varlen_prefill: fp8 and int8 caches need k_scale and v_scale");
   if (batch == 0 || max_seqlen_q == 0 || total_q == 0) return ok();
   if (!out || !q || !k || !v || !cu_seqlens_q || !cu_seqlens_k)
     return fail(PKV_ERR_INVALID, "varlen_prefill: NULL pointer");

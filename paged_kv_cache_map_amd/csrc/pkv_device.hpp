@@ -14,7 +14,10 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-enum : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+enum : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kI8 = 3 };
+
+// Caches of one byte per element, decoded as code x per-head scale.
+constexpr bool scaled8(int ct) { return ct == kFP8 || ct == kI8; }
 
 template <int T>
 struct Elt;
@@ -24,6 +27,8 @@ template <>
 struct Elt<kBF16> { static constexpr int bytes = 2; };
 template <>
 struct Elt<kFP8> { static constexpr int bytes = 1; };
+template <>
+struct Elt<kI8> { static constexpr int bytes = 1; };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -58,6 +63,44 @@ __device__ __forceinline__ float2_t e4m3x2_to_f32x2(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(w, HIGH);
 }
 
+// Two int8 codes (bytes 0,1 or 2,3 of w) -> two bf16 in one word.  Exact:
+// an integer of magnitude <= 128 has at most 8 significant bits, so its fp32
+// value has zero low halves and the bf16 is its upper half.
+template <bool HIGH>
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w) {
+  constexpr int sh = HIGH ? 16 : 0;
+  const uint32_t lo = __float_as_uint((float)((int32_t)(w << (24 - sh)) >> 24));
+  const uint32_t hi = __float_as_uint((float)((int32_t)(w << (16 - sh)) >> 24));
+  return (lo >> 16) | (hi & 0xffff0000u);
+}
+
+template <bool HIGH>
+__device__ __forceinline__ float2_t i8x2_to_f32x2(uint32_t w) {
+  constexpr int sh = HIGH ? 16 : 0;
+  return float2_t{(float)((int32_t)(w << (24 - sh)) >> 24), (float)((int32_t)(w << (16 - sh)) >> 24)};
+}
+
+// The one-byte cache codes of type CT (fp8 E4M3 or int8) -> bf16 / fp32, exactly.
+template <int CT, bool HIGH>
+__device__ __forceinline__ uint32_t code8x2_to_bf16x2(uint32_t w) {
+  if constexpr (CT == kI8) return i8x2_to_bf16x2<HIGH>(w);
+  else return e4m3x2_to_bf16x2<HIGH>(w);
+}
+
+template <int CT, bool HIGH>
+__device__ __forceinline__ float2_t code8x2_to_f32x2(uint32_t w) {
+  if constexpr (CT == kI8) return i8x2_to_f32x2<HIGH>(w);
+  else return e4m3x2_to_f32x2<HIGH>(w);
+}
+
+// fp32 -> int8 code: round to nearest, ties to even; saturated to [-127, 127]
+// (symmetric: -128 is never produced); NaN -> 0.
+__device__ __forceinline__ uint32_t f32_to_i8(float x) {
+  if (x != x) return 0u;
+  const float r = __builtin_rintf(fminf(fmaxf(x, -127.0f), 127.0f));
+  return (uint32_t)(int32_t)r & 0xffu;
+}
+
 // fp32 -> E4M3 code: round to nearest, ties to even mantissa; |x| >= 448 and
 // +-inf saturate to +-448; NaN -> 0x7F.  Integer formulation on the fp32 bits.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
@@ -78,29 +121,35 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+template <int DST>
+__device__ __forceinline__ uint32_t encode8(float x) {
+  if constexpr (DST == kI8) return f32_to_i8(x);
+  else return f32_to_e4m3(x);
+}
+
 // 16 source bytes of a K or V row -> the cache's bytes for them (16, 8 or 4,
-// in the low words): a bit copy when the types match, else the fp8 encoding
-// e4m3(x / scale) with an IEEE fp32 division (the library is built with
-// correctly rounded division).  Every cache write of the library goes through
+// in the low words): a bit copy when the types match, else the one-byte
+// encoding (fp8 E4M3 or int8) of x / scale with an IEEE fp32 division (the
+// library is built with correctly rounded division).  Every cache write of the library goes through
 // this one function, so the slot-map scatter and the appending decode store
 // identical bits.
 template <int SRC, int DST>
 __device__ __forceinline__ u32x4_t convert_piece(uint4 x, float sc) {
   u32x4_t o = {x.x, x.y, x.z, x.w};
-  if constexpr (SRC == kBF16 && DST == kFP8) {
+  if constexpr (SRC == kBF16 && scaled8(DST)) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
     uint32_t out[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float v = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
-      out[e >> 2] |= f32_to_e4m3(v / sc) << ((e & 3) * 8);
+      out[e >> 2] |= encode8<DST>(v / sc) << ((e & 3) * 8);
     }
     o.x = out[0];
     o.y = out[1];
-  } else if constexpr (SRC == kF32 && DST == kFP8) {
-    o.x = f32_to_e4m3(__uint_as_float(x.x) / sc) | (f32_to_e4m3(__uint_as_float(x.y) / sc) << 8) |
-          (f32_to_e4m3(__uint_as_float(x.z) / sc) << 16) |
-          (f32_to_e4m3(__uint_as_float(x.w) / sc) << 24);
+  } else if constexpr (SRC == kF32 && scaled8(DST)) {
+    o.x = encode8<DST>(__uint_as_float(x.x) / sc) | (encode8<DST>(__uint_as_float(x.y) / sc) << 8) |
+          (encode8<DST>(__uint_as_float(x.z) / sc) << 16) |
+          (encode8<DST>(__uint_as_float(x.w) / sc) << 24);
   }
   return o;
 }

@@ -76,10 +76,12 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Eight E4M3 codes (two words) -> eight bf16 (four words), exact.
-__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-  return make_uint4(e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
-                    e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1));
+// Eight one-byte cache codes (E4M3 or int8; two words) -> eight bf16 (four
+// words), exact.
+template <int KVT>
+__device__ __forceinline__ uint4 code8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return make_uint4(code8x2_to_bf16x2<KVT, false>(w0), code8x2_to_bf16x2<KVT, true>(w0),
+                    code8x2_to_bf16x2<KVT, false>(w1), code8x2_to_bf16x2<KVT, true>(w1));
 }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& x, int i) {
@@ -230,8 +232,8 @@ struct Loader {
       if constexpr (KVT == kBF16) {
         *reinterpret_cast<uint4*>(dst) = x;
       } else {
-        *reinterpret_cast<uint4*>(dst) = e4m3x8_to_bf16x8(x.x, x.y);
-        *reinterpret_cast<uint4*>(dst + 8) = e4m3x8_to_bf16x8(x.z, x.w);
+        *reinterpret_cast<uint4*>(dst) = code8x8_to_bf16x8<KVT>(x.x, x.y);
+        *reinterpret_cast<uint4*>(dst + 8) = code8x8_to_bf16x8<KVT>(x.z, x.w);
       }
     }
     uint4 rows[kr];
@@ -241,7 +243,7 @@ struct Loader {
       if constexpr (KVT == kBF16) {
         rows[r] = x;
       } else {
-        rows[r] = e4m3x8_to_bf16x8(x.x, x.y);
+        rows[r] = code8x8_to_bf16x8<KVT>(x.x, x.y);
       }
     }
     uint16_t* vt = buf + L::k_elems + v_group(tid) * 8 * L::vt_row + v_key0(tid);
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int q_
   }
   float scale = a.softmax_scale * kLog2e;
   float out_scale = 1.0f;
-  if constexpr (KVT == kFP8) {
+  if constexpr (scaled8(KVT)) {
     scale *= a.k_scale[g];
     out_scale = a.v_scale[g];
   }
@@ -729,10 +731,14 @@ __device__ __forceinline__ float sum_quarters(float x) {
 // tiles copied by DMA through buffer descriptors.
 template <int KVT, int D, bool PAGED, int CB>
 __global__ __launch_bounds__(512 / CB, 4 / CB) void prefill16_kernel(PrefillArgs a, int q_tiles) {
+  // The body is device code only: the host pass of the compiler, which
+  // needs no more than the kernel's signature, rejects some of its template
+  // instantiations when both one-byte cache types are built in one file.
+#if defined(__HIP_DEVICE_COMPILE__)
   constexpr int W = 8 / CB;
-  constexpr bool F8 = KVT == kFP8;
+  constexpr bool F8 = KVT == kFP8 || KVT == kI8;  // one-byte cache, dequantised in LDS
   static_assert(CB == 1 || CB == 2, "one or two column blocks per wave");
-  static_assert(!F8 || (PAGED && D == 128), "fp8 caches: paged, head_dim 128");
+  static_assert(!F8 || (PAGED && D == 128), "one-byte caches: paged, head_dim 128");
   using T = Tile<D, W>;              // bf16 tiles the MFMAs read
   using TC = Tile<D, W, F8 ? 1 : 2>;  // tiles as copied from the cache
   constexpr int BM = 16 * CB * W;
@@ -994,13 +1000,13 @@ __global__ __launch_bounds__(512 / CB, 4 / CB) void prefill16_kernel(PrefillArgs
           const bool ok = (mc.valid >> r) & 1ull;
           const uint4 z = make_uint4(0u, 0u, 0u, 0u);
           *reinterpret_cast<uint4*>(kxb + r * T::row_bytes + (((2 * pc) ^ kswz16<D>(r)) << 4)) =
-              e4m3x8_to_bf16x8(k8.x, k8.y);
+              code8x8_to_bf16x8<KVT>(k8.x, k8.y);
           *reinterpret_cast<uint4*>(kxb + r * T::row_bytes + (((2 * pc + 1) ^ kswz16<D>(r)) << 4)) =
-              e4m3x8_to_bf16x8(k8.z, k8.w);
+              code8x8_to_bf16x8<KVT>(k8.z, k8.w);
           *reinterpret_cast<uint4*>(vxb + r * T::row_bytes + (((2 * pc) ^ vswz16<D>(r)) << 4)) =
-              ok ? e4m3x8_to_bf16x8(v8.x, v8.y) : z;
+              ok ? code8x8_to_bf16x8<KVT>(v8.x, v8.y) : z;
           *reinterpret_cast<uint4*>(vxb + r * T::row_bytes + (((2 * pc + 1) ^ vswz16<D>(r)) << 4)) =
-              ok ? e4m3x8_to_bf16x8(v8.z, v8.w) : z;
+              ok ? code8x8_to_bf16x8<KVT>(v8.z, v8.w) : z;
         }
       } else {
         zero_rows<D, W>(mc.valid, vc, wave, lane);
@@ -1047,6 +1053,7 @@ __global__ __launch_bounds__(512 / CB, 4 / CB) void prefill16_kernel(PrefillArgs
       *reinterpret_cast<uint2*>(op + 16 * db + 4 * grp4) = make_uint2(w0, w1);
     }
   }
+#endif
 }
 
 template <int KVT, int D>
@@ -1056,8 +1063,8 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   if (grid > 0x7fffffff / 2) return hipErrorInvalidValue;
   constexpr int CB = PKV_PREFILL_CB;
   const dim3 block(512 / CB);
-  if constexpr (KVT == kFP8) {
-    hipLaunchKernelGGL((prefill16_kernel<kFP8, D, true, CB>), dim3((unsigned)grid), block, 0, stream, a, q_tiles);
+  if constexpr (scaled8(KVT)) {
+    hipLaunchKernelGGL((prefill16_kernel<KVT, D, true, CB>), dim3((unsigned)grid), block, 0, stream, a, q_tiles);
   } else if (a.block_table != nullptr) {
     hipLaunchKernelGGL((prefill16_kernel<kBF16, D, true, CB>), dim3((unsigned)grid), block, 0, stream, a, q_tiles);
   } else {
@@ -1095,7 +1102,11 @@ hipError_t launch_varlen_prefill(const PrefillArgs& a, hipStream_t stream) {
     if (a.head_dim == 64) return dma::launch<kBF16, 64>(a, stream);
     return dma::launch<kBF16, 128>(a, stream);
   }
-  // fp8 caches are paged (the entry point requires a block table)
+  // one-byte caches are paged (the entry point requires a block table)
+  if (a.kv_dtype == kI8) {
+    if (a.head_dim == 64) return launch_mfma<kI8, 64>(a, stream);
+    return dma::launch<kI8, 128>(a, stream);
+  }
   if (a.head_dim == 64) return launch_mfma<kFP8, 64>(a, stream);
   return dma::launch<kFP8, 128>(a, stream);
 }

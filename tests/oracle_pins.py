@@ -340,3 +340,33 @@ def check_append_to_empty_sequence(paged, seed=13):
     for h in range(hq):
         assert np.array_equal(out[0, h], vn[0, h // (hq // hkv)].astype(np.float64))
     assert np.all(np.isfinite(out[1]))
+
+
+# ---------------------------------------------------------------------------
+# the int8 codec (a reading: symmetric, round half to even, saturate at 127)
+# ---------------------------------------------------------------------------
+
+
+def int8_checks(mod):
+    """Pins of ``oracle.int8`` (or a planted copy): the definition's spot
+    values, then torch's round-half-to-even and clamp on the same quotients."""
+    import torch
+
+    def spot():
+        x = np.array([0.0, -0.0, 0.5, 1.5, 2.5, -2.5, -0.5, 0.49999997, 126.5, 127.4, 127.6, 200.0, -127.5,
+                      -200.0, np.inf, -np.inf, np.nan], np.float32)
+        want = [0, 0, 0, 2, 2, -2, 0, 0, 126, 127, 127, 127, -127, -127, 127, -127, 0]
+        assert mod.encode(x).tolist() == want
+        assert mod.encode(x).dtype == np.int8
+        codes = np.arange(-127, 128).astype(np.int8)
+        assert np.array_equal(mod.decode(codes), np.arange(-127, 128, dtype=np.float64))
+        assert np.array_equal(mod.encode(mod.decode(codes).astype(np.float32)), codes)
+
+    def library():
+        rng = np.random.default_rng(3)
+        x = np.concatenate([rng.standard_normal(4000) * s for s in (0.7, 30.0, 400.0)]).astype(np.float32)
+        x = np.concatenate([x, np.arange(-130, 131, dtype=np.float32) + np.float32(0.5)])
+        ref = torch.clamp(torch.round(torch.from_numpy(x)), -127, 127).to(torch.int8).numpy()
+        assert np.array_equal(mod.encode(x), ref)
+
+    return [lambda _m: spot(), lambda _m: library()]

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle_pins as pins
-from oracle import e4m3, kvsize, paged
+from oracle import e4m3, int8, kvsize, paged
 
 # ---------------------------------------------------------------------------
 # fp8 E4M3 codec
@@ -250,3 +250,24 @@ def test_row_subset_equals_full_computation():
     part = paged.varlen_prefill(q, "f32", k, v, "f32", cu_q, cu_k, 0.4, True, rows=rows)
     np.testing.assert_array_equal(part[rows], full[rows])
     assert np.all(np.delete(part, rows, axis=0) == 0)
+
+
+def test_int8_codec_pins():
+    for check in pins.int8_checks(int8):
+        check(int8)
+
+
+def test_int8_write_and_decode_use_the_head_scale():
+    """An int8 cache stores RNE(x / scale[h]) saturated to 127; decoding gives
+    code x scale[h]."""
+    k = np.array([[[1.0, -2.0, 3.06, 1000.0]], [[0.5, 0.25, -0.75, 0.0]]], np.float32)  # [2, 1, 4]
+    v = -k
+    kc = np.zeros((1, 2, 1, 4), np.int8)
+    scale = np.array([0.02], np.float32)
+    k2, v2 = paged.kv_cache_write(k, v, kc, kc.copy(), np.array([1, 0]), "f32", "int8", scale, scale)
+    assert k2[0, 1, 0].tolist() == [50, -100, 127, 127]       # 3.06 / 0.02 = 153 -> 127
+    assert k2[0, 0, 0].tolist() == [25, 12, -38, 0]           # 0.25 / 0.02 = 12.5 -> 12 (even)
+    assert v2[0, 1, 0].tolist() == [-50, 100, -127, -127]
+    vals = paged.to_f64(k2[0], "int8", scale)
+    assert vals[1, 0].tolist() == [50 * np.float64(np.float32(0.02)), -100 * np.float64(np.float32(0.02)),
+                                   127 * np.float64(np.float32(0.02)), 127 * np.float64(np.float32(0.02))]

@@ -142,3 +142,28 @@ def test_real_codec_passes():
 def test_planted_codec_mistake_is_caught(name, original, planted):
     mod = _load_mutant("e4m3.py", original, planted)
     assert _some_check_fails(mod, _e4m3_checks(mod)), f"mutation {name} survived every pin"
+
+
+INT8_MUTATIONS = [
+    ("round_half_away", "codes[finite] = np.clip(np.rint(q[finite]), -127, 127).astype(np.int64)",
+     "codes[finite] = np.clip(np.sign(q[finite]) * np.floor(np.abs(q[finite]) + 0.5), -127, 127).astype(np.int64)"),
+    ("asymmetric_range", "codes[finite] = np.clip(np.rint(q[finite]), -127, 127).astype(np.int64)",
+     "codes[finite] = np.clip(np.rint(q[finite]), -128, 127).astype(np.int64)"),
+    ("truncate", "codes[finite] = np.clip(np.rint(q[finite]), -127, 127).astype(np.int64)",
+     "codes[finite] = np.clip(np.trunc(q[finite]), -127, 127).astype(np.int64)"),
+    ("no_saturation", "codes[finite] = np.clip(np.rint(q[finite]), -127, 127).astype(np.int64)",
+     "codes[finite] = np.rint(q[finite]).astype(np.int64)"),
+    ("decode_unsigned", "return np.asarray(codes, dtype=np.int8).astype(np.float64)",
+     "return np.asarray(codes, dtype=np.int8).view(np.uint8).astype(np.float64)"),
+]
+
+
+def test_real_int8_codec_passes():
+    from oracle import int8
+    assert not _some_check_fails(int8, pins.int8_checks(int8))
+
+
+@pytest.mark.parametrize("name,original,planted", INT8_MUTATIONS, ids=[m[0] for m in INT8_MUTATIONS])
+def test_planted_int8_mistake_is_caught(name, original, planted):
+    mod = _load_mutant("int8.py", original, planted)
+    assert _some_check_fails(mod, pins.int8_checks(mod)), f"mutation {name} survived every pin"

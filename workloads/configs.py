@@ -94,6 +94,23 @@ def _fp8_codes(seed: int, stage: int, shape) -> np.ndarray:
     return out.reshape(shape)
 
 
+def _int8_codes(seed: int, stage: int, shape) -> np.ndarray:
+    """Codes drawn uniformly from [-127, 127] (the symmetric int8 range)."""
+    n = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(n, dtype=np.int8)
+    chunks = [(c, min(_CHUNK, n - c * _CHUNK)) for c in range(max(1, math.ceil(n / _CHUNK)))]
+
+    def fill(chunk):
+        c, size = chunk
+        if size <= 0:
+            return
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stage, c])))
+        out[c * _CHUNK:c * _CHUNK + size] = rng.integers(-127, 128, size=size, dtype=np.int32).astype(np.int8)
+
+    _run_chunks(fill, chunks)
+    return out.reshape(shape)
+
+
 def _run_chunks(fill, chunks):
     workers = min(len(chunks), max(1, min(16, os.cpu_count() or 1)))
     if workers == 1:
@@ -117,7 +134,7 @@ class Step:
     head_dim: int
     block_size: int
     q_dtype: str            # "f32" | "bf16"   (also the new K/V dtype)
-    cache_dtype: str        # "f32" | "bf16" | "fp8"
+    cache_dtype: str        # "f32" | "bf16" | "fp8" | "int8"
     kinds: list             # per sequence: "prefill" | "decode"
     prefix: np.ndarray      # int32 [N] tokens cached before the step
     new: np.ndarray         # int32 [N] tokens added this step
@@ -259,6 +276,9 @@ def build_step(name: str, seed: int, *, num_heads: int, num_kv_heads: int, head_
     if cache_dtype == "fp8":
         k_cache = _fp8_codes(seed, 4, shape)
         v_cache = _fp8_codes(seed, 5, shape)
+    elif cache_dtype == "int8":
+        k_cache = _int8_codes(seed, 4, shape)
+        v_cache = _int8_codes(seed, 5, shape)
     else:
         k_cache = _normal(seed, 4, shape, cache_dtype)
         v_cache = _normal(seed, 5, shape, cache_dtype)
@@ -267,7 +287,8 @@ def build_step(name: str, seed: int, *, num_heads: int, num_kv_heads: int, head_
         for i in range(n):
             p = np.arange(int(prefix[i]))
             history[block_table[i, p // bs].astype(np.int64) * bs + p % bs] = True
-        nan = {"f32": np.float32(np.nan), "bf16": BF16_NAN, "fp8": FP8_NAN}[cache_dtype]
+        # int8 has no NaN: -128, a code the encoder never stores, marks the slots
+        nan = {"f32": np.float32(np.nan), "bf16": BF16_NAN, "fp8": FP8_NAN, "int8": np.int8(-128)}[cache_dtype]
         k_cache.reshape(num_blocks * bs, hkv * d)[~history] = nan
         v_cache.reshape(num_blocks * bs, hkv * d)[~history] = nan
     # 5. new K/V in the query dtype
@@ -275,9 +296,10 @@ def build_step(name: str, seed: int, *, num_heads: int, num_kv_heads: int, head_
     v_new = _normal(seed, 7, (tokens, hkv, d), q_dtype)
     # 6. fp8 scales: per-head amax / 448
     k_scale = v_scale = None
-    if cache_dtype == "fp8":
-        k_scale = _amax_scale(k_new, q_dtype)
-        v_scale = _amax_scale(v_new, q_dtype)
+    if cache_dtype in ("fp8", "int8"):
+        top = 448.0 if cache_dtype == "fp8" else 127.0  # the code range's largest magnitude
+        k_scale = _amax_scale(k_new, q_dtype, top)
+        v_scale = _amax_scale(v_new, q_dtype, top)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     return Step(name=name, num_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
@@ -287,14 +309,14 @@ def build_step(name: str, seed: int, *, num_heads: int, num_kv_heads: int, head_
                 k_scale=k_scale, v_scale=v_scale, seed=seed)
 
 
-def _amax_scale(x: np.ndarray, dtype: str) -> np.ndarray:
+def _amax_scale(x: np.ndarray, dtype: str, top: float = 448.0) -> np.ndarray:
     if dtype == "bf16":
         vals = (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
     else:
         vals = x.astype(np.float32)
     amax = np.abs(vals).max(axis=(0, 2)) if vals.shape[0] else np.ones(vals.shape[1], np.float32)
     amax = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
-    return (amax / np.float32(448.0)).astype(np.float32)
+    return (amax / np.float32(top)).astype(np.float32)
 
 
 def _rng(seed: int) -> np.random.Generator:
@@ -325,6 +347,8 @@ def config(name: str, **overrides) -> Step:
     * ``mixed_fp8``: 4 prefill chunks of 512 tokens (prefix U{0..8192}) then 256
       decode sequences (cached U{1024..16384}); 32/8 heads, head_dim 128;
       fp8 E4M3 cache with per-head scales, bf16 queries.
+    * ``mixed_int8``: the same step (same lengths) with an int8 cache
+      (per-head scales amax / 127).
 
     ``overrides`` can shrink a workload (``batch``, ``len_lo``, ``len_hi`` ...)
     for the oracle-sized parity cases; the seed stays the config's.
@@ -365,7 +389,7 @@ def config(name: str, **overrides) -> Step:
         return build_step(name, seed, num_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
                           q_dtype="bf16", cache_dtype="bf16", prefix=np.full(b, length, np.int32),
                           new=np.ones(b, np.int32), kinds=["decode"] * b)
-    if name == "mixed_fp8":
+    if name in ("mixed_fp8", "mixed_int8"):
         seed = 1005
         n_pre = overrides.get("prefill_chunks", 4)
         chunk = overrides.get("chunk", 512)
@@ -377,8 +401,8 @@ def config(name: str, **overrides) -> Step:
         prefix = np.concatenate([pre_p, dec_l]).astype(np.int32)
         new = np.concatenate([np.full(n_pre, chunk), np.ones(n_dec)]).astype(np.int32)
         return build_step(name, seed, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
-                          q_dtype="bf16", cache_dtype="fp8", prefix=prefix, new=new,
-                          kinds=["prefill"] * n_pre + ["decode"] * n_dec)
+                          q_dtype="bf16", cache_dtype="fp8" if name == "mixed_fp8" else "int8",
+                          prefix=prefix, new=new, kinds=["prefill"] * n_pre + ["decode"] * n_dec)
     raise KeyError(name)
 
 

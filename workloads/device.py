@@ -13,6 +13,8 @@ def to_dev(arr, dtype, device="cuda"):
         t = torch.from_numpy(arr.astype(np.float32, copy=False))
     elif dtype == "fp8":
         t = torch.from_numpy(arr.astype(np.uint8, copy=False))
+    elif dtype == "int8":
+        t = torch.from_numpy(arr.astype(np.int8, copy=False))
     elif dtype == "i32":
         t = torch.from_numpy(arr.astype(np.int32, copy=False))
     else:
@@ -30,4 +32,6 @@ def to_host(t, dtype):
         return t.numpy()
     if dtype == "fp8":
         return t.view(torch.uint8).numpy()
+    if dtype == "int8":
+        return t.view(torch.int8).numpy()
     raise ValueError(dtype)
