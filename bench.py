@@ -55,7 +55,7 @@ def parse():
 # algorithmic work (what the method must move / compute)
 # ---------------------------------------------------------------------------
 
-ELT = {"f32": 4, "bf16": 2, "fp8": 1}
+ELT = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}
 
 
 def write_bytes(step):
@@ -429,7 +429,7 @@ def main():
         "step_gbs": round(step_bytes / (sep["ms_per_step"] * 1e6), 2)}
     if args.configs == "all":
         for name, kw in (("varlen_prefill_prefix", {}), ("llama70b_long_decode", {}),
-                         ("mixed_fp8", {})):
+                         ("mixed_fp8", {}), ("mixed_int8", {})):
             print(f"[bench] {name}", flush=True)
             _, res = measure(name, max(3, args.steps // 4), 2, args.split_keys, **kw)
             line["kernels"][name] = {k: (round(v, 5) if isinstance(v, float) else v)
@@ -442,6 +442,8 @@ def main():
             "long_decode_gbs": line["kernels"]["llama70b_long_decode"]["decode_gbs"],
             "mixed_fp8_decode_gbs": line["kernels"]["mixed_fp8"]["decode_gbs"],
             "mixed_fp8_prefill_tflops": line["kernels"]["mixed_fp8"]["prefill_tflops"],
+            "mixed_int8_decode_gbs": line["kernels"]["mixed_int8"]["decode_gbs"],
+            "mixed_int8_prefill_tflops": line["kernels"]["mixed_int8"]["prefill_tflops"],
         }
     print("[bench] copy_blocks", flush=True)
     line["kernels"]["copy_blocks"] = measure_copy_blocks(max(5, args.steps), 2)
