@@ -1,12 +1,13 @@
 /*
  * pkv.h -- C ABI of libpkv.so: attention over a paged KV cache on AMD MI355X
- * (gfx950).  Hand-written HIP kernels behind five calls:
+ * (gfx950).  Hand-written HIP kernels behind six calls:
  *
  *   pkv_kv_cache_write   scatter the step's new K/V rows into cache slots
  *   pkv_paged_decode     one query per sequence over its cached keys
  *   pkv_paged_decode_append  the same decode storing the step's new K/V rows
  *                        itself (one launch for write + decode)
  *   pkv_varlen_prefill   causal attention for a packed batch of query chunks
+ *   pkv_mixed_attention  a chunked-prefill step's prefill and decode in one launch
  *   pkv_copy_blocks      copy-on-write of whole cache blocks
  * and a host-side block manager (pkv_block_manager_*: allocation, sharing,
  * copy-on-write decisions, prefix hashes).
@@ -263,6 +264,48 @@ int pkv_varlen_prefill(void* out, const void* q, int q_dtype,
                        int32_t block_size, int32_t num_blocks,
                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t total_q, int32_t total_k, void* stream);
+
+/*
+ * pkv_mixed_attention -- the attention of a mixed chunked-prefill step: the
+ * prefill chunks (causal, over the paged cache) and the decode sequences in
+ * one call.  [ch15] section "プレフィックスキャッシュとchunked prefill": long
+ * prefills are cut into chunks that join other requests' decodes in one
+ * batch, so that the compute-heavy prefill and the memory-heavy decode
+ * complement each other; [paged-doc] sections "Varlen パス" and デコードパス:
+ * the varlen kernel takes mixed batches, the decode kernel does not.
+ *
+ * The results are those of pkv_varlen_prefill(causal = 1, paged) on the
+ * prefill arguments and of pkv_paged_decode (split_keys = 0) on the decode
+ * arguments (the decode's split points may differ, so its bits may differ
+ * within rounding).  Shared arguments: the caches, their dtype and scales,
+ * num_blocks, block_size, the head counts, head_dim, softmax_scale and
+ * q_dtype.  For one-byte caches (FP8, INT8) at head_dim 128, with a decode
+ * batch that the automatic plan serves with its matrix-core stream-K kernel
+ * (batch <= 2048), both kinds of work run in ONE kernel launch (each CU runs
+ * a decode worker and prefill tiles side by side; then the decode's merge
+ * kernel); otherwise the prefill kernel and the decode kernels are launched
+ * one after the other.  prefill_batch or decode_batch may be 0 (that part is
+ * skipped).
+ *   prefill_*    as pkv_varlen_prefill's out, q, cu_seqlens_q, cu_seqlens_k,
+ *                batch, max_seqlen_q, max_seqlen_k, block_table,
+ *                max_blocks_per_seq, total_q (the block table is required).
+ *   decode_*, cache_seqlens, workspace  as pkv_paged_decode's out, q,
+ *                block_table, max_blocks_per_seq, cache_seqlens, batch and
+ *                workspace (pkv_paged_decode_workspace_size with split 0).
+ * Errors: those of the two calls (the message names the failing part).
+ */
+int pkv_mixed_attention(const void* k_cache, const void* v_cache, int cache_dtype,
+                        const float* k_scale, const float* v_scale, int32_t num_blocks,
+                        int32_t block_size, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, float softmax_scale, int q_dtype,
+                        void* prefill_out, const void* prefill_q, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int32_t prefill_batch, int32_t max_seqlen_q,
+                        int32_t max_seqlen_k, const int32_t* prefill_block_table,
+                        int32_t prefill_max_blocks, int32_t total_q, void* decode_out,
+                        const void* decode_q, const int32_t* decode_block_table,
+                        int32_t decode_max_blocks, const int32_t* cache_seqlens,
+                        int32_t decode_batch, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * ---------------------------------------------------------------------------

@@ -14,6 +14,7 @@ Calls (same names as the C entry points without the ``pkv_`` prefix):
 * :func:`paged_decode_append` -- the same decode storing the step's new K/V
   rows itself (write + decode in one call);
 * :func:`varlen_prefill` -- causal attention for a packed batch of chunks;
+* :func:`mixed_attention` -- a chunked-prefill step's prefill and decode in one call;
 * :func:`copy_blocks`    -- copy-on-write of whole cache blocks;
 * :class:`BlockManager`  -- the host-side block allocator (``pkv_block_manager_*``).
 """
@@ -66,6 +67,10 @@ def _load_library():
     lib.pkv_varlen_prefill.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp,
                                        i32, i32, i32, f32, i32, vp, i32, i32, i32, i32, i32, i32,
                                        i32, i32, vp]
+    lib.pkv_mixed_attention.restype = ctypes.c_int
+    lib.pkv_mixed_attention.argtypes = [vp, vp, ctypes.c_int, vp, vp, i32, i32, i32, i32, i32, f32, ctypes.c_int,
+                                        vp, vp, vp, vp, i32, i32, i32, vp, i32, i32,
+                                        vp, vp, vp, i32, vp, i32, vp, sz, vp]
     lib.pkv_copy_blocks.restype = ctypes.c_int
     lib.pkv_copy_blocks.argtypes = [vp, vp, ctypes.c_int, i32, i32, i32, i32, vp, i32, vp]
     u64, ip = ctypes.c_uint64, ctypes.POINTER(ctypes.c_int32)
@@ -253,6 +258,65 @@ def varlen_prefill(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
         int(max_seqlen_k), float(softmax_scale), int(bool(causal)), _ptr(block_table), maxblk, bs, nb,
         hq, hkv, d, total_q, total_k, _stream(stream)))
     return out
+
+
+def mixed_attention(k_cache, v_cache, softmax_scale, prefill=None, decode=None, k_scale=None, v_scale=None,
+                    workspace=None, stream=None):
+    """A chunked-prefill step's attention in one call.
+
+    ``prefill``: dict(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+    block_table[, out]) as for :func:`varlen_prefill` (causal, paged);
+    ``decode``: dict(q, block_table, cache_seqlens[, out]) as for
+    :func:`paged_decode`.  Returns (prefill_out, decode_out) (None for a
+    missing part)."""
+    import torch
+    _require(k_cache.is_contiguous() and v_cache.is_contiguous() and k_cache.dim() == 4,
+             "caches must be contiguous [num_blocks, block_size, Hkv, D]")
+    nb, bs, hkv, d = k_cache.shape
+    p_out = d_out = None
+    pq = pcq = pck = pbt = None
+    pb = mq = mk = pmax = tq = 0
+    hq = None
+    q_dtype = None
+    if prefill is not None:
+        pq = prefill["q"]
+        _require(pq.dim() == 3 and pq.is_contiguous(), "prefill q must be contiguous [sum Lq, Hq, D]")
+        pbt = prefill["block_table"]
+        _require(pbt.dim() == 2 and pbt.is_contiguous() and pbt.dtype == torch.int32,
+                 "prefill block_table must be contiguous int32")
+        pcq, pck = prefill["cu_seqlens_q"], prefill["cu_seqlens_k"]
+        _require(pcq.dtype == torch.int32 and pck.dtype == torch.int32, "cu_seqlens must be int32")
+        p_out = prefill.get("out")
+        p_out = torch.empty_like(pq) if p_out is None else p_out
+        pb, mq, mk, pmax, tq = pcq.numel() - 1, int(prefill["max_seqlen_q"]), int(prefill["max_seqlen_k"]), \
+            pbt.shape[1], pq.shape[0]
+        hq, q_dtype = pq.shape[1], pq.dtype
+    dq = dbt = dlen = None
+    db = dmax = 0
+    if decode is not None:
+        dq = decode["q"]
+        _require(dq.dim() == 3 and dq.is_contiguous(), "decode q must be contiguous [B, Hq, D]")
+        dbt, dlen = decode["block_table"], decode["cache_seqlens"]
+        _require(dbt.dim() == 2 and dbt.is_contiguous() and dbt.dtype == torch.int32,
+                 "decode block_table must be contiguous int32")
+        _require(dlen.dtype == torch.int32, "cache_seqlens must be int32")
+        d_out = decode.get("out")
+        d_out = torch.empty_like(dq) if d_out is None else d_out
+        db, dmax = dq.shape[0], dbt.shape[1]
+        _require(hq is None or hq == dq.shape[1], "prefill and decode q must have the same heads")
+        hq, q_dtype = dq.shape[1], dq.dtype
+        need = paged_decode_workspace_size(db, hq, hkv, d, bs, dmax, 0)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dq.device)
+    if hq is None:
+        return None, None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    qcode = F32 if q_dtype == torch.float32 else BF16
+    _check(library().pkv_mixed_attention(
+        _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), nb, bs, hq, hkv, d,
+        float(softmax_scale), qcode, _ptr(p_out), _ptr(pq), _ptr(pcq), _ptr(pck), pb, mq, mk, _ptr(pbt), pmax, tq,
+        _ptr(d_out), _ptr(dq), _ptr(dbt), dmax, _ptr(dlen), db, _ptr(workspace), ws_bytes, _stream(stream)))
+    return p_out, d_out
 
 
 def copy_blocks(k_cache, v_cache, block_pairs, stream=None):

@@ -20,7 +20,9 @@ OUT = PKG / "libpkv.so"
 BUILD = ROOT / "_build"
 ROCM = pathlib.Path(os.environ.get("ROCM_PATH", "/opt/rocm"))
 
-HIP_SOURCES = ["kv_write.hip", "paged_decode.hip", "varlen_prefill.hip", "block_copy.hip"]
+# attention.hip includes paged_decode.hip and varlen_prefill.hip (one unit: the
+# mixed-step kernel runs the bodies of both)
+HIP_SOURCES = ["kv_write.hip", "attention.hip", "block_copy.hip"]
 HOST_SOURCES = ["pkv_api.cpp", "pkv_plan.cpp", "pkv_blocks.cpp"]
 
 HIPCC_FLAGS = [

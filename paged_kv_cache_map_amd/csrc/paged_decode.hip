@@ -55,8 +55,6 @@ namespace {
 
 constexpr int kWaves = kDecodeWaves;
 constexpr int kChunk = kDecodeChunk;  // keys per wave iteration (2 sub-steps of 16)
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -1.0e30f;   // running-max start: finite, so exp2 never sees inf - inf
 
 template <int CT, int D, int GW>
 struct Cfg {
@@ -1484,25 +1482,24 @@ __device__ __forceinline__ void append_range(const DecodeArgs& a, const int32_t*
   }
 }
 
-template <int CT, int D, int G, int N, int OCC, bool APPEND>
-__global__ __launch_bounds__(kStreamThreads, OCC) void decode_mfma_kernel(DecodeArgs a) {
+// The workgroup body of the stream-K decode: workgroup wg of num_wgs, with
+// its LDS passed in (the chunk prefix, the scan scratch and each wave's K and
+// V chunk), so that a launch that serves other work too can run it.
+template <int CT, int D, int G, int N, bool APPEND>
+__device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int wg, int num_wgs, int32_t* pre,
+                                                 int32_t* part, uint8_t* k_lds, uint8_t* v_lds) {
   using Ge = Geo<CT, D>;
-  __shared__ int32_t pre[kStreamMaxBatch + 1];
-  __shared__ int32_t part[kStreamThreads];
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kWaves][Ge::vbytes];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kWaves][Ge::vbytes];
-
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int ug = a.num_kv_heads;  // units per sequence: one per KV head
   build_prefix(pre, part, a, ug);
-  if (blockIdx.x == 0) {  // the merge kernel reads the prefix instead of rebuilding it
+  if (wg == 0) {  // the merge kernel reads the prefix instead of rebuilding it
     int32_t* pre_g = stream_prefix(a, G, D);
     for (int i = threadIdx.x; i <= a.batch; i += kStreamThreads) pre_g[i] = pre[i];
   }
   const int64_t T = pre[a.batch];
-  const int W = gridDim.x * kWaves;
-  const int w = blockIdx.x * kWaves + wave;
+  const int W = num_wgs * kWaves;
+  const int w = wg * kWaves + wave;
   const int c0 = (int)(T * w / W), c1 = (int)(T * (w + 1) / W);
   if (c0 >= c1) return;
   const Pos p0 = locate(pre, a.batch, ug, c0);
@@ -1537,8 +1534,8 @@ __global__ __launch_bounds__(kStreamThreads, OCC) void decode_mfma_kernel(Decode
                            : 0x7ffffff0u;  // idle lanes read nothing
   o.q = (lane & 15) < G ? (uint32_t)((lane & 15) * Ge::qrow + (lane >> 4) * 16) : 0x7ffffff0u;
 
-  uint8_t* k_w = k_lds[wave];
-  uint8_t* v_w = v_lds[wave];
+  uint8_t* k_w = k_lds + wave * Ge::vbytes;
+  uint8_t* v_w = v_lds + wave * Ge::vbytes;
   uint32_t k_off[Ge::KS];
 #pragma unroll
   for (int ks = 0; ks < Ge::KS; ++ks)
@@ -1652,6 +1649,24 @@ __global__ __launch_bounds__(kStreamThreads, OCC) void decode_mfma_kernel(Decode
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // loads past the last chunk land before the wave ends
+}
+
+template <int CT, int D>
+struct DecodeLds {  // LDS of decode_mfma_body, in bytes
+  static constexpr int pre = ((kStreamMaxBatch + 1) * 4 + 15) / 16 * 16;
+  static constexpr int part = kStreamThreads * 4;
+  static constexpr int chunk = kWaves * Geo<CT, D>::vbytes;  // K (or V) chunks of all waves
+  static constexpr int bytes = pre + part + 2 * chunk;
+};
+
+template <int CT, int D, int G, int N, int OCC, bool APPEND>
+__global__ __launch_bounds__(kStreamThreads, OCC) void decode_mfma_kernel(DecodeArgs a) {
+  using Ge = Geo<CT, D>;
+  __shared__ int32_t pre[kStreamMaxBatch + 1];
+  __shared__ int32_t part[kStreamThreads];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kWaves * Ge::vbytes];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kWaves * Ge::vbytes];
+  decode_mfma_body<CT, D, G, N, APPEND>(a, blockIdx.x, gridDim.x, pre, part, k_lds, v_lds);
 }
 
 // Chunks in flight per wave and waves per SIMD: bf16 chunks (16 KiB of K and

@@ -105,7 +105,8 @@ int decode_common(const char* name, const NewRows& nr, void* out, const void* q,
                   const float* v_scale, const int32_t* block_table, int32_t max_blocks_per_seq,
                   const int32_t* cache_seqlens, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
                   int32_t head_dim, int32_t block_size, int32_t num_blocks, float softmax_scale,
-                  int32_t split_keys, void* workspace, size_t workspace_bytes, void* stream) {
+                  int32_t split_keys, void* workspace, size_t workspace_bytes, void* stream,
+                  pkv::DecodeArgs* prepared = nullptr, pkv::DecodePlan* prepared_plan = nullptr) {
   const bool append = nr.k != nullptr || nr.v != nullptr;
   if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
     return fail(PKV_ERR_INVALID, "%s: sizes must be positive", name);
@@ -203,7 +204,115 @@ int decode_common(const char* name, const NewRows& nr, void* out, const void* q,
   a.k_new_stride = nr.k_stride * qb;
   a.v_new_stride = nr.v_stride * qb;
   a.len_bias = append ? 1 : 0;
+  if (prepared) {  // checked and planned; the caller launches
+    *prepared = a;
+    *prepared_plan = plan;
+    return ok();
+  }
   return launch_status(pkv::launch_paged_decode(a, plan, s), name);
+}
+
+// Checks and, unless `prepared` is given, launches a varlen prefill.  With
+// `prepared`, *empty is set when there is nothing to compute.
+int prefill_common(void* out, const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                       const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
+                       const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
+                       int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                       const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size,
+                       int32_t num_blocks, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t total_q, int32_t total_k, void* stream, pkv::PrefillArgs* prepared = nullptr,
+                       bool* empty = nullptr) {
+  if (empty) *empty = false;
+  if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+    return fail(PKV_ERR_INVALID, "varlen_prefill: negative size");
+  if (batch > 65535) return fail(PKV_ERR_INVALID, "varlen_prefill: batch above 65535");
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "varlen_prefill: num_heads must be a positive multiple of num_kv_heads");
+  if (causal != 0 && causal != 1) return fail(PKV_ERR_INVALID, "varlen_prefill: causal must be 0 or 1");
+  const bool paged = block_table != nullptr;
+  const bool pair_ok = (q_dtype == PKV_BF16 && kv_dtype == PKV_BF16) ||
+                       (q_dtype == PKV_BF16 && scaled_cache(kv_dtype) && paged) ||
+                       (q_dtype == PKV_F32 && kv_dtype == PKV_F32);
+  if (!pair_ok)
+    return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: unsupported q/kv dtypes %d/%d%s", q_dtype, kv_dtype,
+                paged ? "" : " (fp8 and int8 need the paged cache)");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: head_dim %d not in {64, 128}", head_dim);
+  if (!group_ok(num_heads / num_kv_heads))
+    return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: group size %d not in {1,2,4,8,16}",
+                num_heads / num_kv_heads);
+  if (paged) {
+    if (!pow2_in(block_size, 8, 256))
+      return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: block_size %d not a power of two in [8, 256]",
+                  block_size);
+    if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+      return fail(PKV_ERR_INVALID, "varlen_prefill: max_blocks_per_seq and num_blocks must be positive");
+  }
+  if (scaled_cache(kv_dtype) && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID, "varlen_prefill: fp8 and int8 caches need k_scale and v_scale");
+  if (batch == 0 || max_seqlen_q == 0 || total_q == 0) {
+    if (empty) *empty = true;
+    return ok();
+  }
+  if (!out || !q || !k || !v || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(PKV_ERR_INVALID, "varlen_prefill: NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(PKV_ERR_INVALID, "varlen_prefill: q, k, v and out must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_mode()) {
+    std::vector<int32_t> cq, ck, table;
+    if (!fetch(cq, cu_seqlens_q, batch + 1, s) || !fetch(ck, cu_seqlens_k, batch + 1, s))
+      return fail(PKV_ERR_LAUNCH, "varlen_prefill: could not read cu_seqlens");
+    if (cq[0] != 0 || ck[0] != 0) return fail(PKV_ERR_INVALID, "varlen_prefill: cu_seqlens must start at 0");
+    std::vector<int32_t> klens((size_t)batch);
+    for (int32_t b = 0; b < batch; ++b) {
+      const int32_t lq = cq[b + 1] - cq[b], lk = ck[b + 1] - ck[b];
+      if (lq < 0 || lk < 0) return fail(PKV_ERR_INVALID, "varlen_prefill: cu_seqlens not monotone at %d", b);
+      if (lq > max_seqlen_q || lk > max_seqlen_k)
+        return fail(PKV_ERR_INVALID, "varlen_prefill: request %d exceeds the max_seqlen hints", b);
+      klens[b] = lk;
+    }
+    if (cq[batch] > total_q) return fail(PKV_ERR_INVALID, "varlen_prefill: cu_seqlens_q exceeds total_q");
+    if (paged) {
+      if (!fetch(table, block_table, (int64_t)batch * max_blocks_per_seq, s))
+        return fail(PKV_ERR_LAUNCH, "varlen_prefill: could not read block_table");
+      const int rc = check_table_rows(table, klens, max_blocks_per_seq, block_size, num_blocks,
+                                      "varlen_prefill");
+      if (rc != PKV_OK) return rc;
+    } else if (ck[batch] > total_k) {
+      return fail(PKV_ERR_INVALID, "varlen_prefill: cu_seqlens_k exceeds total_k");
+    }
+  }
+  pkv::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k = (const uint8_t*)k;
+  a.v = (const uint8_t*)v;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.block_table = block_table;
+  a.batch = batch;
+  a.max_seqlen_q = max_seqlen_q;
+  a.max_seqlen_k = max_seqlen_k;
+  a.softmax_scale = softmax_scale;
+  a.causal = causal;
+  a.max_blocks_per_seq = paged ? max_blocks_per_seq : 0;
+  a.block_size = paged ? block_size : 0;
+  a.num_blocks = paged ? num_blocks : 0;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.q_dtype = q_dtype;
+  a.kv_dtype = kv_dtype;
+  if (prepared) {
+    *prepared = a;
+    return ok();
+  }
+  return launch_status(pkv::launch_varlen_prefill(a, s), "varlen_prefill");
 }
 
 }  // namespace
@@ -325,6 +434,7 @@ int pkv_paged_decode_append(void* out, const void* q, int q_dtype, const void* k
                        workspace_bytes, stream);
 }
 
+
 int pkv_varlen_prefill(void* out, const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
                        const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
                        const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
@@ -332,89 +442,55 @@ int pkv_varlen_prefill(void* out, const void* q, int q_dtype, const void* k, con
                        const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size,
                        int32_t num_blocks, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t total_q, int32_t total_k, void* stream) {
-  if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
-    return fail(PKV_ERR_INVALID, "varlen_prefill: negative size");
-  if (batch > 65535) return fail(PKV_ERR_INVALID, "varlen_prefill: batch above 65535");
-  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
-    return fail(PKV_ERR_INVALID, "varlen_prefill: num_heads must be a positive multiple of num_kv_heads");
-  if (causal != 0 && causal != 1) return fail(PKV_ERR_INVALID, "varlen_prefill: causal must be 0 or 1");
-  const bool paged = block_table != nullptr;
-  const bool pair_ok = (q_dtype == PKV_BF16 && kv_dtype == PKV_BF16) ||
-                       (q_dtype == PKV_BF16 && scaled_cache(kv_dtype) && paged) ||
-                       (q_dtype == PKV_F32 && kv_dtype == PKV_F32);
-  if (!pair_ok)
-    return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: unsupported q/kv dtypes %d/%d%s", q_dtype, kv_dtype,
-                paged ? "" : " (fp8 and int8 need the paged cache)");
-  if (head_dim != 64 && head_dim != 128)
-    return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: head_dim %d not in {64, 128}", head_dim);
-  if (!group_ok(num_heads / num_kv_heads))
-    return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: group size %d not in {1,2,4,8,16}",
-                num_heads / num_kv_heads);
-  if (paged) {
-    if (!pow2_in(block_size, 8, 256))
-      return fail(PKV_ERR_UNSUPPORTED, "varlen_prefill: block_size %d not a power of two in [8, 256]",
-                  block_size);
-    if (max_blocks_per_seq <= 0 || num_blocks <= 0)
-      return fail(PKV_ERR_INVALID, "varlen_prefill: max_blocks_per_seq and num_blocks must be positive");
+  return prefill_common(out, q, q_dtype, k, v, kv_dtype, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, batch,
+                        max_seqlen_q, max_seqlen_k, softmax_scale, causal, block_table, max_blocks_per_seq,
+                        block_size, num_blocks, num_heads, num_kv_heads, head_dim, total_q, total_k, stream);
+}
+
+int pkv_mixed_attention(const void* k_cache, const void* v_cache, int cache_dtype, const float* k_scale,
+                        const float* v_scale, int32_t num_blocks, int32_t block_size, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int q_dtype,
+                        void* prefill_out, const void* prefill_q, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int32_t prefill_batch, int32_t max_seqlen_q,
+                        int32_t max_seqlen_k, const int32_t* prefill_block_table, int32_t prefill_max_blocks,
+                        int32_t total_q, void* decode_out, const void* decode_q,
+                        const int32_t* decode_block_table, int32_t decode_max_blocks,
+                        const int32_t* cache_seqlens, int32_t decode_batch, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (prefill_batch < 0 || decode_batch < 0)
+    return fail(PKV_ERR_INVALID, "mixed_attention: negative batch");
+  pkv::PrefillArgs pa;
+  bool p_empty = true;
+  if (prefill_batch > 0) {
+    if (!prefill_block_table) return fail(PKV_ERR_INVALID, "mixed_attention: the prefill reads the paged cache");
+    const int rc = prefill_common(prefill_out, prefill_q, q_dtype, k_cache, v_cache, cache_dtype, k_scale, v_scale,
+                                  cu_seqlens_q, cu_seqlens_k, prefill_batch, max_seqlen_q, max_seqlen_k,
+                                  softmax_scale, 1, prefill_block_table, prefill_max_blocks, block_size,
+                                  num_blocks, num_heads, num_kv_heads, head_dim, total_q, 0, stream, &pa, &p_empty);
+    if (rc != PKV_OK) return rc;
   }
-  if (scaled_cache(kv_dtype) && (!k_scale || !v_scale))
-    return fail(PKV_ERR_INVALID, "varlen_prefill: fp8 and int8 caches need k_scale and v_scale");
-  if (batch == 0 || max_seqlen_q == 0 || total_q == 0) return ok();
-  if (!out || !q || !k || !v || !cu_seqlens_q || !cu_seqlens_k)
-    return fail(PKV_ERR_INVALID, "varlen_prefill: NULL pointer");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return fail(PKV_ERR_INVALID, "varlen_prefill: q, k, v and out must be 16-byte aligned");
+  pkv::DecodeArgs da;
+  pkv::DecodePlan plan;
+  const bool has_decode = decode_batch > 0;
+  if (has_decode) {
+    const int rc = decode_common("mixed_attention", NewRows{}, decode_out, decode_q, q_dtype, k_cache, v_cache,
+                                 cache_dtype, k_scale, v_scale, decode_block_table, decode_max_blocks,
+                                 cache_seqlens, decode_batch, num_heads, num_kv_heads, head_dim, block_size,
+                                 num_blocks, softmax_scale, 0, workspace, workspace_bytes, stream, &da, &plan);
+    if (rc != PKV_OK) return rc;
+  }
   hipStream_t s = (hipStream_t)stream;
-  if (validate_mode()) {
-    std::vector<int32_t> cq, ck, table;
-    if (!fetch(cq, cu_seqlens_q, batch + 1, s) || !fetch(ck, cu_seqlens_k, batch + 1, s))
-      return fail(PKV_ERR_LAUNCH, "varlen_prefill: could not read cu_seqlens");
-    if (cq[0] != 0 || ck[0] != 0) return fail(PKV_ERR_INVALID, "varlen_prefill: cu_seqlens must start at 0");
-    std::vector<int32_t> klens((size_t)batch);
-    for (int32_t b = 0; b < batch; ++b) {
-      const int32_t lq = cq[b + 1] - cq[b], lk = ck[b + 1] - ck[b];
-      if (lq < 0 || lk < 0) return fail(PKV_ERR_INVALID, "varlen_prefill: cu_seqlens not monotone at %d", b);
-      if (lq > max_seqlen_q || lk > max_seqlen_k)
-        return fail(PKV_ERR_INVALID, "varlen_prefill: request %d exceeds the max_seqlen hints", b);
-      klens[b] = lk;
-    }
-    if (cq[batch] > total_q) return fail(PKV_ERR_INVALID, "varlen_prefill: cu_seqlens_q exceeds total_q");
-    if (paged) {
-      if (!fetch(table, block_table, (int64_t)batch * max_blocks_per_seq, s))
-        return fail(PKV_ERR_LAUNCH, "varlen_prefill: could not read block_table");
-      const int rc = check_table_rows(table, klens, max_blocks_per_seq, block_size, num_blocks,
-                                      "varlen_prefill");
-      if (rc != PKV_OK) return rc;
-    } else if (ck[batch] > total_k) {
-      return fail(PKV_ERR_INVALID, "varlen_prefill: cu_seqlens_k exceeds total_k");
-    }
+  // one launch for both kinds of work where the shared kernel is built: one-byte
+  // caches at head_dim 128 on the matrix-core decode plan
+  const bool fused = has_decode && !p_empty && scaled_cache(cache_dtype) && head_dim == 128 && plan.stream &&
+                     plan.mfma;
+  if (fused) return launch_status(pkv::launch_mixed(da, pa, s), "mixed_attention");
+  if (!p_empty) {
+    const int rc = launch_status(pkv::launch_varlen_prefill(pa, s), "mixed_attention");
+    if (rc != PKV_OK) return rc;
   }
-  pkv::PrefillArgs a;
-  a.out = out;
-  a.q = q;
-  a.k = (const uint8_t*)k;
-  a.v = (const uint8_t*)v;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  a.cu_seqlens_q = cu_seqlens_q;
-  a.cu_seqlens_k = cu_seqlens_k;
-  a.block_table = block_table;
-  a.batch = batch;
-  a.max_seqlen_q = max_seqlen_q;
-  a.max_seqlen_k = max_seqlen_k;
-  a.softmax_scale = softmax_scale;
-  a.causal = causal;
-  a.max_blocks_per_seq = paged ? max_blocks_per_seq : 0;
-  a.block_size = paged ? block_size : 0;
-  a.num_blocks = paged ? num_blocks : 0;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.total_q = total_q;
-  a.total_k = total_k;
-  a.q_dtype = q_dtype;
-  a.kv_dtype = kv_dtype;
-  return launch_status(pkv::launch_varlen_prefill(a, s), "varlen_prefill");
+  if (has_decode) return launch_status(pkv::launch_paged_decode(da, plan, s), "mixed_attention");
+  return ok();
 }
 
 int pkv_copy_blocks(void* k_cache, void* v_cache, int cache_dtype, int32_t num_blocks, int32_t block_size,

@@ -16,6 +16,9 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 enum : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kI8 = 3 };
 
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp2 never sees inf - inf
+
 // Caches of one byte per element, decoded as code x per-head scale.
 constexpr bool scaled8(int ct) { return ct == kFP8 || ct == kI8; }
 

@@ -119,6 +119,10 @@ struct PrefillArgs {
 
 hipError_t launch_varlen_prefill(const PrefillArgs& a, hipStream_t stream);
 
+// Prefill work items and the stream-K decode in one launch (one-byte caches,
+// head_dim 128, decode on the matrix-core plan), then the decode's merge.
+hipError_t launch_mixed(const DecodeArgs& da, const PrefillArgs& pa, hipStream_t stream);
+
 struct CopyBlocksArgs {
   uint8_t* k_cache;
   uint8_t* v_cache;

@@ -59,8 +59,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
 constexpr int kThreads = 256;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -1.0e30f;
 constexpr int kWaitVmcnt0 = 0x0f70;  // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)
 
 template <int D>
@@ -729,12 +727,14 @@ __device__ __forceinline__ float sum_quarters(float x) {
 // half: the lane's own scores, so P^T needs no exchange; the transposed V
 // reads put the same keys in the same k-slots.  Two LDS stages of K and V
 // tiles copied by DMA through buffer descriptors.
+// The workgroup body: work item hw (see work_item), with its LDS passed in
+// (two stages of K and V tiles as copied, and for one-byte caches the bf16
+// tiles dequantised from them), so that a launch that serves other work too
+// can run it.  Buffers are 1 KiB-aligned.
 template <int KVT, int D, bool PAGED, int CB>
-__global__ __launch_bounds__(512 / CB, 4 / CB) void prefill16_kernel(PrefillArgs a, int q_tiles) {
-  // The body is device code only: the host pass of the compiler, which
-  // needs no more than the kernel's signature, rejects some of its template
-  // instantiations when both one-byte cache types are built in one file.
-#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ void prefill16_body(const PrefillArgs& a, int q_tiles, int hw, uint8_t* k0b,
+                                               uint8_t* v0b, uint8_t* k1b, uint8_t* v1b, uint8_t* kxb,
+                                               uint8_t* vxb) {
   constexpr int W = 8 / CB;
   constexpr bool F8 = KVT == kFP8 || KVT == kI8;  // one-byte cache, dequantised in LDS
   static_assert(CB == 1 || CB == 2, "one or two column blocks per wave");
@@ -748,17 +748,13 @@ __global__ __launch_bounds__(512 / CB, 4 / CB) void prefill16_kernel(PrefillArgs
   constexpr int kDma = TC::dma_per_wave;
   constexpr int kWaitLgkm0 = 0xc07f;
   static_assert(BM == 128 && GPW == CB && TC::groups_per_wave == GPW, "8-key groups per wave");
-  // copy targets (two stages); with fp8 caches, bf16 tiles dequantised from them
-  __shared__ __attribute__((aligned(1024))) uint8_t k0b[TC::bytes], v0b[TC::bytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t k1b[TC::bytes], v1b[TC::bytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t kxb[F8 ? T::bytes : 16], vxb[F8 ? T::bytes : 16];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 15, grp4 = lane >> 4;
 
   WorkItem w;
-  if (!work_item(blockIdx.x, q_tiles, a.batch, a.num_heads, a.num_kv_heads, w)) return;
+  if (!work_item(hw, q_tiles, a.batch, a.num_heads, a.num_kv_heads, w)) return;
   const int qt = w.qt, h = w.h, b = w.b, g = w.g;
 
   const int q_start = a.cu_seqlens_q[b];
@@ -1053,6 +1049,30 @@ __global__ __launch_bounds__(512 / CB, 4 / CB) void prefill16_kernel(PrefillArgs
       *reinterpret_cast<uint2*>(op + 16 * db + 4 * grp4) = make_uint2(w0, w1);
     }
   }
+}
+
+template <int KVT, int D>
+struct PrefillLds {  // LDS of prefill16_body, in bytes (each buffer 1 KiB-aligned)
+  static constexpr bool F8 = scaled8(KVT);
+  static constexpr int copied = Tile<D, 4, F8 ? 1 : 2>::bytes;  // one K or V tile as copied
+  static constexpr int bf16 = F8 ? Tile<D, 4>::bytes : 1024;    // one dequantised tile
+  static constexpr int bytes = 4 * copied + 2 * bf16;
+};
+
+template <int KVT, int D, bool PAGED, int CB>
+__global__ __launch_bounds__(512 / CB, 4 / CB) void prefill16_kernel(PrefillArgs a, int q_tiles) {
+  // The body is device code only: the host pass of the compiler, which
+  // needs no more than the kernel's signature, rejects some of its template
+  // instantiations when both one-byte cache types are built in one file.
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr bool F8 = scaled8(KVT);
+  using TC = Tile<D, 8 / CB, F8 ? 1 : 2>;
+  using T = Tile<D, 8 / CB>;
+  // copy targets (two stages); with one-byte caches, bf16 tiles dequantised from them
+  __shared__ __attribute__((aligned(1024))) uint8_t k0b[TC::bytes], v0b[TC::bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k1b[TC::bytes], v1b[TC::bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t kxb[F8 ? T::bytes : 16], vxb[F8 ? T::bytes : 16];
+  prefill16_body<KVT, D, PAGED, CB>(a, q_tiles, blockIdx.x, k0b, v0b, k1b, v1b, kxb, vxb);
 #endif
 }
 
