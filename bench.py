@@ -46,6 +46,8 @@ def parse():
                     help="diagnostic: time one named workload and print its kernel times only")
     ap.add_argument("--append", action="store_true",
                     help="diagnostic (--only): store the decode tokens with the appending decode")
+    ap.add_argument("--mixed", action="store_true",
+                    help="diagnostic (--only): prefill and decode through the one mixed-step call")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 512 MiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -120,13 +122,14 @@ def decode_traffic():
 class Runner:
     """A workload step on the GPU with `copies` rotated replicas of its KV pool."""
 
-    def __init__(self, step, copies=1, split_keys=0, append=False):
+    def __init__(self, step, copies=1, split_keys=0, append=False, mixed=False):
         import torch
         from workloads.device import to_dev
         self.torch = torch
         self.s = step
         self.split_keys = split_keys
         self.append = append
+        self.mixed = mixed  # prefill and decode through the one mixed-step call
         self.copies = []
         for _ in range(copies):
             self.copies.append((to_dev(step.k_cache, step.cache_dtype),
@@ -177,6 +180,18 @@ class Runner:
             pkv.kv_cache_write(self.k_new, self.v_new, kc, vc, self.slot_map, self.k_scale, self.v_scale)
         if ev is not None:
             ev[1].record()
+        if self.mixed:
+            p = self.p
+            pkv.mixed_attention(kc, vc, s.scale,
+                                dict(q=self.pq, cu_seqlens_q=self.pcq, cu_seqlens_k=self.pck,
+                                     max_seqlen_q=p["max_seqlen_q"], max_seqlen_k=p["max_seqlen_k"],
+                                     block_table=self.pbt, out=self.pout),
+                                dict(q=self.dq, block_table=self.dbt, cache_seqlens=self.dlen, out=self.dout),
+                                self.k_scale, self.v_scale, workspace=self.dws)
+            if ev is not None:
+                ev[2].record()
+                ev[3].record()
+            return
         if self.has_prefill:
             p = self.p
             pkv.varlen_prefill(self.pq, kc, vc, self.pcq, self.pck, p["max_seqlen_q"],
@@ -298,22 +313,31 @@ def copies_for(step):
     return max(1, math.ceil(ROTATE_BYTES / pool))
 
 
-def measure(name, steps, warmup, split_keys=0, append=False, **overrides):
+def measure(name, steps, warmup, split_keys=0, append=False, mixed=False, **overrides):
     """Time one workload step.  append=True: the decode sequences' new rows
     are stored by the appending decode call (one launch for their write and
     their attention); the slot-map write then covers the prefill tokens only,
     and the decode figures count the appended rows' write bytes as well."""
     import workloads
     step = workloads.config(name, **overrides)
-    r = Runner(step, copies_for(step), split_keys, append)
+    r = Runner(step, copies_for(step), split_keys, append, mixed)
     t = r.time(steps, warmup)
     res = dict(t)
+    if mixed:  # one call for both parts: its time is the prefill's plus the decode's share
+        res["mixed_call_ms"] = t["prefill_ms"] + t["decode_ms"]
     step_write = write_bytes(step)
     res["write_bytes"] = step_write * r.write_tokens // max(step.num_tokens, 1)
     # per-call events carry a few microseconds of their own: the write's
     # rate comes from the back-to-back region
     res["write_gbs"] = res["write_bytes"] / (t["write_region_ms"] * 1e6) if r.write_tokens else 0.0
     res["write_gbs_single_call_events"] = res["write_bytes"] / (t["write_ms"] * 1e6) if r.write_tokens else 0.0
+    if mixed:
+        res["decode_bytes"] = decode_bytes(step)
+        res["prefill_flops"] = prefill_flops(step)
+        del r
+        import torch
+        torch.cuda.empty_cache()
+        return step, res
     if r.has_decode:
         res["decode_bytes"] = decode_bytes(step) + (step_write - res["write_bytes"])
         res["decode_gbs"] = res["decode_bytes"] / (t["decode_ms"] * 1e6)
@@ -371,7 +395,7 @@ def main():
 
     if args.only:
         print(f"[bench] {args.only} (diagnostic)", flush=True)
-        _, res = measure(args.only, args.steps, args.warmup, args.split_keys, args.append)
+        _, res = measure(args.only, args.steps, args.warmup, args.split_keys, args.append, args.mixed)
         print(json.dumps({"diagnostic": args.only,
                           **{k: (round(v, 5) if isinstance(v, float) else v) for k, v in res.items()}}),
               flush=True)
@@ -434,6 +458,14 @@ def main():
             _, res = measure(name, max(3, args.steps // 4), 2, args.split_keys, **kw)
             line["kernels"][name] = {k: (round(v, 5) if isinstance(v, float) else v)
                                      for k, v in res.items()}
+        for name in ("mixed_fp8", "mixed_int8"):
+            print(f"[bench] {name} (one mixed-step call)", flush=True)
+            _, res = measure(name, max(3, args.steps // 2), 3, args.split_keys, mixed=True)
+            sep = line["kernels"][name]
+            line["kernels"][name + "_one_call"] = {
+                "ms_per_step": round(res["ms_per_step"], 5), "region_ms_per_step": round(res["region_ms_per_step"], 5),
+                "mixed_call_ms": round(res["mixed_call_ms"], 5),
+                "separate_calls_ms": round(sep["prefill_ms"] + sep["decode_ms"], 5)}
         pre = line["kernels"]["varlen_prefill_prefix"]
         line["secondary"] = {
             "varlen_prefill_tflops": pre["prefill_tflops"],
