@@ -92,8 +92,9 @@ def prefill_flops(step):
 # measured in the same runs.  The figures belong to the decode sources with
 # the given digest: after any change to them the traffic is reported as null
 # until the counters are taken again.
-DECODE_TRAFFIC = {"digest": "26442499afddc454", "read_bytes": 551967996, "write_bytes": 3891149}
+DECODE_TRAFFIC = {"digest": "b72907d2f88dc8d2", "read_bytes": 551906775, "write_bytes": 3891026}
 DECODE_SOURCES = ("paged_kv_cache_map_amd/csrc/paged_decode.hip",
+                  "paged_kv_cache_map_amd/csrc/attention.hip",
                   "paged_kv_cache_map_amd/csrc/pkv_device.hpp",
                   "paged_kv_cache_map_amd/csrc/pkv_plan.cpp",
                   "paged_kv_cache_map_amd/csrc/pkv_internal.h")
