@@ -206,3 +206,32 @@ def test_decode_workspace_plan():
     assert pkv.paged_decode_workspace_size(2, 32, 2, 128, 16, 8) == max(mfma, valu)
     # unsupported argument -> 0
     assert pkv.paged_decode_workspace_size(3, 8, 3, 128, 16, 4) == 0
+
+
+def mixed(**kw):
+    a = dict(kc=FAKE, vc=FAKE, cdt=pkv.FP8_E4M3, ksc=FAKE, vsc=FAKE, nb=10, bs=16, hq=8, hkv=2, d=128, scale=0.1,
+             qdt=pkv.BF16, pout=FAKE, pq=FAKE, cq=FAKE, ck=FAKE, pb=2, mq=10, mk=10, pbt=FAKE, pmax=4, tq=12,
+             dout=FAKE, dq=FAKE, dbt=FAKE, dmax=4, sl=FAKE, db=3, ws=FAKE, wsb=1 << 30, stream=NULL)
+    a.update(kw)
+    return pkv.library().pkv_mixed_attention(
+        a["kc"], a["vc"], a["cdt"], a["ksc"], a["vsc"], a["nb"], a["bs"], a["hq"], a["hkv"], a["d"], a["scale"],
+        a["qdt"], a["pout"], a["pq"], a["cq"], a["ck"], a["pb"], a["mq"], a["mk"], a["pbt"], a["pmax"], a["tq"],
+        a["dout"], a["dq"], a["dbt"], a["dmax"], a["sl"], a["db"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pb=-1), pkv.ERR_INVALID),
+    (dict(pbt=NULL), pkv.ERR_INVALID),                # the prefill reads the paged cache
+    (dict(ksc=NULL), pkv.ERR_INVALID),                # one-byte cache without scales
+    (dict(dq=NULL), pkv.ERR_INVALID),
+    (dict(d=96), pkv.ERR_UNSUPPORTED),
+    (dict(qdt=pkv.F32), pkv.ERR_UNSUPPORTED),
+    (dict(wsb=0, ws=NULL), pkv.ERR_INVALID),          # decode workspace too small
+])
+def test_mixed_rejects(kw, code):
+    assert mixed(**kw) == code
+    assert pkv.library().pkv_last_error()
+
+
+def test_mixed_nothing_to_do_is_a_no_op():
+    assert mixed(pb=0, db=0) == pkv.OK
