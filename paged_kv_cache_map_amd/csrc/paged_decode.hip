@@ -908,7 +908,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs
   const int gg = (h / G) * head_groups + (h % G) / GW;
   const int hh = (h % G) % GW;
   const int nch = (pre[b + 1] - pre[b]) / ug;
-  if (nch == 0) {
+  // (T == 0 implies nch == 0; testing it keeps T's load next to the others)
+  if (nch == 0 || T == 0) {
 #pragma unroll
     for (int e = 0; e < NV; ++e) store_out<QT>(a.out, bh * D + lane * NV + e, 0.0f);
     return;
@@ -920,6 +921,40 @@ __global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs
   const int n = wl - wf + 1;
   const float* ws_o = a.workspace;
   const float* ws_ml = a.workspace + (int64_t)a.stream_slots * GW * D;
+  if (n <= kBatch) {
+    // the common case: every part's (max, sum) and output row in flight at
+    // once (the general loop below, for one pass, in one round trip)
+    const int wj = wf + min(lane, n - 1);
+    const bool has = lane < n && (T * wj / W < T * (wj + 1) / W);
+    const int64_t slot = (int64_t)(wj + u) * GW + hh;
+    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + slot * 2);  // (max, sum), one load
+    const float m_raw = ml.x, l_raw = ml.y;
+    float ov[kBatch][NV];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t si = (int64_t)(wf + min(i, n - 1) + u) * GW + hh;
+#pragma unroll
+      for (int e = 0; e < NV; ++e) ov[i][e] = ws_o[si * D + lane * NV + e];
+    }
+    const float mj = has ? m_raw : kNegBig;
+    const float mn = wave_max(mj);
+    const float f = has ? fast_exp2(mj - mn) : 0.0f;
+    const float Ls = wave_sum(has ? l_raw * f : 0.0f);
+    float Of[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) Of[e] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const float fi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), i));
+      const bool use = i < n && fi > 0.0f;
+#pragma unroll
+      for (int e = 0; e < NV; ++e) Of[e] = use ? fmaf(ov[i][e], fi, Of[e]) : Of[e];
+    }
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) store_out<QT>(a.out, bh * D + lane * NV + e, Of[e] * inv);
+    return;
+  }
   float mx = kNegBig, L = 0.0f, O[NV];
 #pragma unroll
   for (int e = 0; e < NV; ++e) O[e] = 0.0f;
