@@ -166,3 +166,15 @@ def test_append_repeated_steps_grow_the_cache():
         assert_cache_equal(gk, kc, "bf16", f"k_cache step {it}")
         assert_cache_equal(gv, vc, "bf16", f"v_cache step {it}")
         assert max_err(got, want) <= TOL["bf16"], it
+
+
+def test_append_batch_past_the_stream_table():
+    """2100 sequences (more than the stream plan's chunk table holds): the
+    append kernel, then the fixed-split decode."""
+    rng = np.random.default_rng(23)
+    prefix = rng.integers(0, 40, size=2100)
+    step = workloads.build_step("append_big_batch", 2100, num_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                                q_dtype="bf16", cache_dtype="bf16", prefix=prefix, new=[1] * 2100,
+                                kinds=["decode"] * 2100)
+    pairs = sample_pairs(np.random.default_rng(24), 2100, 8, 64)
+    check_append(step, pairs=pairs)

@@ -96,3 +96,21 @@ def test_mixed_step_more_decode_waves_than_chunks():
                                 q_dtype="bf16", cache_dtype="fp8", prefix=[700, 3, 0], new=[400, 1, 1],
                                 kinds=["prefill", "decode", "decode"])
     run_mixed(step)
+
+
+def test_mixed_step_two_launch_paths():
+    """head_dim 64 with an fp8 cache, and a decode batch past the stream
+    plan's table: the call launches the prefill and the decode one after the
+    other, with the same results."""
+    step = workloads.build_step("mixed_fp8_d64", 64, num_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                                q_dtype="bf16", cache_dtype="fp8", prefix=[40, 0, 300, 7],
+                                new=[100, 33, 1, 1], kinds=["prefill", "prefill", "decode", "decode"])
+    run_mixed(step)
+    rng = np.random.default_rng(65)
+    n_dec = 2100
+    prefix = np.concatenate([[120], rng.integers(0, 30, size=n_dec)])
+    new = np.concatenate([[64], np.ones(n_dec, np.int64)])
+    step = workloads.build_step("mixed_fp8_big_batch", 65, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                                q_dtype="bf16", cache_dtype="fp8", prefix=prefix, new=new,
+                                kinds=["prefill"] + ["decode"] * n_dec)
+    run_mixed(step, pairs=sample_pairs(rng, n_dec, 8, 64))
