@@ -309,6 +309,38 @@ def measure_copy_blocks(steps, warmup, pairs=4096, num_blocks=12288):
             "gbs": round(nbytes / (ms * 1e6), 2), "frac_hbm": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4)}
 
 
+def measure_write_sweep(steps, sizes=(65536, 262144)):
+    """The slot-map write alone at large token counts (8 KV heads x 128, bf16
+    source and cache, block size 16, slots a random permutation of the pool):
+    where launch latency no longer matters.  Algorithmic bytes per token:
+    2 x 2 KiB read + 2 x 2 KiB written + 4 (its slot)."""
+    import torch
+    import paged_kv_cache_map_amd as pkv
+    out = {}
+    rng = np.random.default_rng(9)
+    for t in sizes:
+        k = torch.empty((t, 8, 128), dtype=torch.bfloat16, device="cuda").normal_()
+        v = torch.empty_like(k).normal_()
+        kc = torch.empty((t // 16, 16, 8, 128), dtype=torch.bfloat16, device="cuda")
+        vc = torch.empty_like(kc)
+        slots = torch.from_numpy(rng.permutation(t).astype(np.int32)).cuda()
+        pkv.kv_cache_write(k, v, kc, vc, slots)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(steps):
+            pkv.kv_cache_write(k, v, kc, vc, slots)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        nbytes = t * (2 * 8 * 128 * (2 + 2) + 4)
+        out[str(t)] = {"ms": round(ms, 5), "gbs": round(nbytes / (ms * 1e6), 2),
+                       "frac_hbm": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4)}
+        del k, v, kc, vc, slots
+        torch.cuda.empty_cache()
+    return out
+
+
 def copies_for(step):
     pool = step.k_cache.nbytes + step.v_cache.nbytes
     return max(1, math.ceil(ROTATE_BYTES / pool))
@@ -478,6 +510,8 @@ def main():
             "mixed_int8_decode_gbs": line["kernels"]["mixed_int8"]["decode_gbs"],
             "mixed_int8_prefill_tflops": line["kernels"]["mixed_int8"]["prefill_tflops"],
         }
+    print("[bench] write sweep", flush=True)
+    line["kernels"]["write_sweep_tokens"] = measure_write_sweep(max(5, args.steps // 2))
     print("[bench] copy_blocks", flush=True)
     line["kernels"]["copy_blocks"] = measure_copy_blocks(max(5, args.steps), 2)
     if args.copy_probe:
