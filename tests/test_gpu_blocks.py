@@ -19,6 +19,8 @@ pytestmark = pytest.mark.gpu
 def _pool(seed, shape, dtype):
     if dtype == "fp8":
         return configs._fp8_codes(seed, 4, shape), configs._fp8_codes(seed, 5, shape)
+    if dtype == "int8":
+        return configs._int8_codes(seed, 4, shape), configs._int8_codes(seed, 5, shape)
     return configs._normal(seed, 4, shape, dtype), configs._normal(seed, 5, shape, dtype)
 
 
@@ -29,6 +31,7 @@ COPY_CASES = [
     (40, 32, 2, 64, "f32", 15),
     (50, 8, 1, 64, "fp8", 20),     # 512-byte blocks: most lanes of a workgroup idle
     (20, 256, 8, 128, "bf16", 8),  # 512 KiB blocks: 32 workgroups per block and cache
+    (90, 16, 8, 128, "int8", 40),
 ]
 
 
@@ -51,7 +54,7 @@ def test_copy_blocks_bit_exact(nb, bs, hkv, d, dt, npairs):
     assert_cache_equal(gv, wv, dt, "v_cache")
 
 
-@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+@pytest.mark.parametrize("dt", ["bf16", "fp8", "int8"])
 def test_forked_sequences_copy_on_write_then_decode(dt):
     """Prompts written through the block manager's slots; each prompt is
     forked once; both copies then decode three tokens each with the appending
@@ -72,11 +75,12 @@ def test_forked_sequences_copy_on_write_then_decode(dt):
         rows.append(row)
         lens.append(n)
     shape = (nb, bs, hkv, d)
-    k_pool = np.zeros(shape, np.uint8 if dt == "fp8" else np.uint16)
+    k_pool = np.zeros(shape, {"fp8": np.uint8, "int8": np.int8}.get(dt, np.uint16))
     v_pool = np.zeros_like(k_pool)
     k_new = configs._normal(70, 6, (len(slot_map), hkv, d), "bf16")
     v_new = configs._normal(70, 7, (len(slot_map), hkv, d), "bf16")
-    scales = (np.full(hkv, 4.0 / 448, np.float32), np.full(hkv, 4.0 / 448, np.float32)) if dt == "fp8" else (None, None)
+    top = {"fp8": 448.0, "int8": 127.0}.get(dt)
+    scales = (np.full(hkv, 4.0 / top, np.float32), np.full(hkv, 4.0 / top, np.float32)) if top else (None, None)
     ks, vs = [None if x is None else to_dev(x, "f32") for x in scales]
     gk, gv = to_dev(k_pool, dt), to_dev(v_pool, dt)
     say("fork scenario", dt, "prompt write")
