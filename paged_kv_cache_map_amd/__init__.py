@@ -44,6 +44,12 @@ def _load_library():
     if not LIB_PATH.exists():
         raise ImportError(f"{LIB_PATH} is missing; build it with "
                           "`python -m paged_kv_cache_map_amd.build`")
+    # torch ships its own HIP runtime under the same soname as the system's.
+    # Loaded first, it is the one the library binds to, so the library runs
+    # on the runtime that owns the tensors and streams it is handed; loaded
+    # the other way round, the process would hold two runtimes, each with its
+    # own device state.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(str(LIB_PATH))
     vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                              ctypes.c_size_t)
