@@ -15,6 +15,7 @@ import torch
 import paged_kv_cache_map_amd as pkv
 import workloads
 from oracle import paged
+from workloads import configs
 from gpu_helpers import (TOL, GpuStep, assert_cache_equal, max_err, oracle_append_decode, oracle_prefill,
                          oracle_write, out_f64, sample_pairs, say, to_dev)
 
@@ -178,3 +179,48 @@ def test_append_batch_past_the_stream_table():
                                 kinds=["decode"] * 2100)
     pairs = sample_pairs(np.random.default_rng(24), 2100, 8, 64)
     check_append(step, pairs=pairs)
+
+
+@pytest.mark.parametrize("cdt", ["f32", "bf16"])
+@pytest.mark.parametrize("split", [0, 128])
+def test_append_bad_metadata_stores_nothing(cdt, split):
+    """The appending call's handling of metadata that leaves a new token no
+    slot (include/pkv.h: an entry that is negative or >= num_blocks is an
+    empty block; lengths are clamped to the table): the row is not stored and
+    the key is left out of the softmax, so the output is the plain decode
+    over the keys that remain.  Sequence 0's new token opens a block whose
+    entry is -1; sequence 1 (empty) has an out-of-range entry and returns
+    zeros; sequence 2 appends normally; sequence 3's table is full."""
+    rng = np.random.default_rng(21 + split)
+    hq, hkv, d, bs, width, nb = 8, 2, 64, 16, 3, 24
+    qdt = "f32" if cdt == "f32" else "bf16"
+    lens = np.array([16, 0, 31, 48], np.int32)
+    table = rng.permutation(nb)[: 4 * width].reshape(4, width).astype(np.int32)
+    table[0, 1] = -1
+    table[1, 0] = nb + 5
+    seed = 400 + split
+    kc = configs._normal(seed, 1, (nb, bs, hkv, d), cdt)
+    vc = configs._normal(seed, 2, (nb, bs, hkv, d), cdt)
+    q = configs._normal(seed, 3, (4, hq, d), qdt)
+    kn = configs._normal(seed, 4, (4, hkv, d), qdt)
+    vn = configs._normal(seed, 5, (4, hkv, d), qdt)
+    scale = 0.125
+    say("append bad metadata", cdt, "split", split)
+    gk, gv = to_dev(kc, cdt), to_dev(vc, cdt)
+    got = out_f64(pkv.paged_decode_append(to_dev(q, qdt), to_dev(kn, qdt), to_dev(vn, qdt), gk, gv,
+                                          to_dev(table, "i32"), to_dev(lens, "i32"), scale, split_keys=split))
+    torch.cuda.synchronize()
+    # only sequence 2's rows are stored
+    want2, wk, wv = paged.paged_decode_append(q[2:3], qdt, kn[2:3], vn[2:3], kc, vc, cdt, table[2:3], lens[2:3],
+                                              scale)
+    assert_cache_equal(gk, wk, cdt, "k_cache")
+    assert_cache_equal(gv, wv, cdt, "v_cache")
+    want = np.zeros((4, hq, d))
+    want[0] = paged.paged_decode(q[0:1], qdt, kc, vc, cdt, table[0:1], np.array([16]), scale)[0]
+    want[2] = want2[0]
+    want[3] = paged.paged_decode(q[3:4], qdt, kc, vc, cdt, table[3:4], np.array([48]), scale)[0]
+    assert np.array_equal(got[1], np.zeros((hq, d)))
+    err = max_err(got, want)
+    print("append bad metadata", cdt, split, "max|err|", err, flush=True)
+    assert err <= TOL[cdt]
+
