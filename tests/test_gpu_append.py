@@ -181,7 +181,7 @@ def test_append_batch_past_the_stream_table():
     check_append(step, pairs=pairs)
 
 
-@pytest.mark.parametrize("cdt", ["f32", "bf16"])
+@pytest.mark.parametrize("cdt", ["f32", "bf16", "fp8", "int8"])
 @pytest.mark.parametrize("split", [0, 128])
 def test_append_bad_metadata_stores_nothing(cdt, split):
     """The appending call's handling of metadata that leaves a new token no
@@ -199,8 +199,16 @@ def test_append_bad_metadata_stores_nothing(cdt, split):
     table[0, 1] = -1
     table[1, 0] = nb + 5
     seed = 400 + split
-    kc = configs._normal(seed, 1, (nb, bs, hkv, d), cdt)
-    vc = configs._normal(seed, 2, (nb, bs, hkv, d), cdt)
+    if cdt in ("fp8", "int8"):  # codes of the one-byte cache, per-head scales
+        codes = configs._fp8_codes if cdt == "fp8" else configs._int8_codes
+        kc, vc = codes(seed, 1, (nb, bs, hkv, d)), codes(seed, 2, (nb, bs, hkv, d))
+        top = 448.0 if cdt == "fp8" else 127.0
+        scales = (np.full(hkv, 3.0 / top, np.float32), np.full(hkv, 5.0 / top, np.float32))
+    else:
+        kc = configs._normal(seed, 1, (nb, bs, hkv, d), cdt)
+        vc = configs._normal(seed, 2, (nb, bs, hkv, d), cdt)
+        scales = (None, None)
+    ks, vs = [None if x is None else to_dev(x, "f32") for x in scales]
     q = configs._normal(seed, 3, (4, hq, d), qdt)
     kn = configs._normal(seed, 4, (4, hkv, d), qdt)
     vn = configs._normal(seed, 5, (4, hkv, d), qdt)
@@ -208,17 +216,17 @@ def test_append_bad_metadata_stores_nothing(cdt, split):
     say("append bad metadata", cdt, "split", split)
     gk, gv = to_dev(kc, cdt), to_dev(vc, cdt)
     got = out_f64(pkv.paged_decode_append(to_dev(q, qdt), to_dev(kn, qdt), to_dev(vn, qdt), gk, gv,
-                                          to_dev(table, "i32"), to_dev(lens, "i32"), scale, split_keys=split))
+                                          to_dev(table, "i32"), to_dev(lens, "i32"), scale, ks, vs, split_keys=split))
     torch.cuda.synchronize()
     # only sequence 2's rows are stored
     want2, wk, wv = paged.paged_decode_append(q[2:3], qdt, kn[2:3], vn[2:3], kc, vc, cdt, table[2:3], lens[2:3],
-                                              scale)
+                                              scale, *scales)
     assert_cache_equal(gk, wk, cdt, "k_cache")
     assert_cache_equal(gv, wv, cdt, "v_cache")
     want = np.zeros((4, hq, d))
-    want[0] = paged.paged_decode(q[0:1], qdt, kc, vc, cdt, table[0:1], np.array([16]), scale)[0]
+    want[0] = paged.paged_decode(q[0:1], qdt, kc, vc, cdt, table[0:1], np.array([16]), scale, *scales)[0]
     want[2] = want2[0]
-    want[3] = paged.paged_decode(q[3:4], qdt, kc, vc, cdt, table[3:4], np.array([48]), scale)[0]
+    want[3] = paged.paged_decode(q[3:4], qdt, kc, vc, cdt, table[3:4], np.array([48]), scale, *scales)[0]
     assert np.array_equal(got[1], np.zeros((hq, d)))
     err = max_err(got, want)
     print("append bad metadata", cdt, split, "max|err|", err, flush=True)
