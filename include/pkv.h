@@ -206,11 +206,18 @@ int pkv_paged_decode(void* out, const void* q, int q_dtype,
  *                 v_new_stride ELEMENTS apart (>= num_kv_heads * head_dim),
  *                 16-byte aligned.
  *   k_cache, v_cache  modified in place (one row per sequence and head).
- *   cache_seqlens [batch] keys cached before this call.  A sequence whose
- *                 position p is negative or past the block table stores
- *                 nothing; its result is unspecified (memory-safe).  The block
- *                 holding p must be allocated in block_table, and no two
- *                 sequences may append to the same slot.
+ *   cache_seqlens [batch] keys cached before this call.  The block holding
+ *                 p should be allocated in block_table, and no two sequences
+ *                 may append to the same slot.  Metadata that leaves the new
+ *                 token no slot is handled as in pkv_paged_decode: a
+ *                 position past the block table stores nothing and the
+ *                 sequence attends its max_blocks_per_seq * block_size
+ *                 cached keys (lengths are clamped); a block entry that is
+ *                 negative or >= num_blocks stores nothing and reads as an
+ *                 empty block (its keys, the new one included, are left out
+ *                 of the softmax; a sequence left with no key returns
+ *                 zeros).  A negative cache_seqlens[b] stores nothing; its
+ *                 result is unspecified (memory-safe).
  *   Every other argument, the workspace size
  *   (pkv_paged_decode_workspace_size with the same geometry) and the errors
  *   are those of pkv_paged_decode; also PKV_ERR_INVALID for NULL k_new/v_new
