@@ -10,12 +10,15 @@
 // decode kernel cannot.
 //
 // Design (gfx950): one grid.  Its first `decode_wgs` workgroups (one per CU)
-// are the persistent stream-K decode workers (decode_mfma_body), the rest are
-// prefill work items (prefill16_body), numbered as the prefill launch numbers
-// them.  Both bodies run at two waves per SIMD with at most 256 registers a
-// lane, so a CU holds one decode workgroup and one prefill workgroup at a
-// time: the decode streams K/V from HBM while the prefill keeps the matrix
-// cores busy, instead of each waiting for the other's launch.  The LDS of a
+// are the persistent stream-K decode workers (decode_mfma_body), the rest
+// are prefill work items (prefill_body), numbered as the prefill launch
+// numbers them.  Both bodies run at two waves per SIMD with at most 256
+// registers a lane, so a CU can hold a decode workgroup and a prefill
+// workgroup at once: the decode streams K/V from HBM while the prefill keeps
+// the matrix cores busy, instead of each waiting for the other's launch.
+// Which CUs receive which workgroups is the hardware dispatcher's choice
+// (two decode workers may share a CU); the roles are fixed by blockIdx
+// only.  The LDS of a
 // workgroup is the larger of the two bodies' needs (one body runs per
 // workgroup).  One-byte caches (fp8, int8) at head_dim 128: the shapes whose
 // decode and prefill both run at two waves per SIMD.
@@ -29,8 +32,8 @@ namespace {
 template <int CT, int D>
 struct MixedLds {
   using Dl = mfd::DecodeLds<CT, D>;
-  using Pl = dma::PrefillLds<CT, D>;
-  static constexpr int bytes = (Dl::bytes > Pl::bytes ? Dl::bytes : Pl::bytes);
+  static constexpr int prefill = pf::Lds<CT, D>::bytes + 1024;  // + the flag words
+  static constexpr int bytes = (Dl::bytes > prefill ? Dl::bytes : prefill);
 };
 
 template <int CT, int D, int G>
@@ -44,10 +47,11 @@ __global__ __launch_bounds__(kStreamThreads, 2) void mixed_kernel(DecodeArgs da,
         da, blockIdx.x, decode_wgs, reinterpret_cast<int32_t*>(lds), reinterpret_cast<int32_t*>(lds + L::pre),
         lds + L::pre + L::part, lds + L::pre + L::part + L::chunk);
   } else {
-    using P = dma::PrefillLds<CT, D>;
-    dma::prefill16_body<CT, D, true, 2>(pa, q_tiles, blockIdx.x - decode_wgs, lds, lds + P::copied,
-                                        lds + 2 * P::copied, lds + 3 * P::copied, lds + 4 * P::copied,
-                                        lds + 4 * P::copied + P::bf16);
+    using P = pf::Lds<CT, D>;
+    pf::Item it;
+    if (pf::item_of((int)blockIdx.x - decode_wgs, q_tiles, pa.batch * pa.num_kv_heads, pa.num_kv_heads, it))
+      pf::prefill_body<CT, D, true>(pa, it, lds, lds + P::stage, lds + 2 * P::stage,
+                                    reinterpret_cast<uint32_t*>(lds + P::bytes));
   }
 #endif
 }
@@ -55,8 +59,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void mixed_kernel(DecodeArgs da,
 template <int CT, int G>
 hipError_t launch_mixed_g(const DecodeArgs& da, const PrefillArgs& pa, hipStream_t stream) {
   constexpr int D = 128;
-  static_assert(mfd::depth<CT>() == 2 && mfd::occupancy<CT>() == 2 && PKV_PREFILL_CB == 2,
-                "both bodies at two waves per SIMD");
+  static_assert(mfd::depth<CT>() == 2 && mfd::occupancy<CT>() == 2, "both bodies at two waves per SIMD");
   // one decode workgroup per CU (half of what the decode launch alone would
   // use: the other half of each CU runs prefill work items), never more than
   // the decode has 4-wave shares of chunks for
@@ -71,10 +74,12 @@ hipError_t launch_mixed_g(const DecodeArgs& da, const PrefillArgs& pa, hipStream
   if (dwg * kWaves > kStreamMaxWaves) dwg = kStreamMaxWaves / kWaves;
   if (dwg < 1) dwg = 1;
   dwg = (dwg + 7) / 8 * 8;
-  const int q_tiles = (pa.max_seqlen_q + 127) / 128;
-  const int64_t pgrid = work_grid(q_tiles, pa.batch, pa.num_heads, pa.num_kv_heads);
-  const int64_t grid = dwg + pgrid;
-  if (grid > 0x7fffffff / 2) return hipErrorInvalidValue;
+  const int q_tiles = pf::tiles_of(pa.max_seqlen_q, pa.num_heads / pa.num_kv_heads);
+  const int64_t items = pf::grid_of(q_tiles, pa.batch, pa.num_kv_heads);
+  if (items > 0x7fffffff / 2) return hipErrorInvalidValue;
+  // one workgroup per prefill work item after the decode workers (a
+  // multiple of 8, so an item keeps the XCD the prefill launch gives it)
+  const int64_t grid = dwg + items;
   hipLaunchKernelGGL((mixed_kernel<CT, D, G>), dim3((unsigned)grid), dim3(kStreamThreads), 0, stream, da, pa,
                      q_tiles, (int)dwg);
   hipError_t e = hipGetLastError();
