@@ -22,7 +22,14 @@
  * - Every pointer argument is a DEVICE pointer, except where a comment says
  *   otherwise.  Scalars are passed by value.  Index arrays are int32.
  * - The caller allocates and owns every buffer, including the decode
- *   workspace.  The library keeps no device memory between calls.
+ *   workspace.  The library's only device memory of its own is one static
+ *   array per GPU (64 KiB): the work-queue counters of pkv_varlen_prefill,
+ *   one set per stream for the first 64 streams that call it (later streams
+ *   run the prefill without queues, at one workgroup per work item).  Each
+ *   launch clears its stream's set with a small kernel first, so calls on
+ *   one stream never see each other's counts.  A graph captured with a
+ *   prefill call keeps the capturing stream's set: two replays of it that
+ *   overlap in time (on different streams) race on the counters.
  * - Every call validates its scalar arguments on the host, enqueues its
  *   kernels on `stream` (a hipStream_t; NULL = the null stream) and returns
  *   without synchronising.  It reads no device memory on the host, so

@@ -47,11 +47,14 @@ __global__ __launch_bounds__(kStreamThreads, 2) void mixed_kernel(DecodeArgs da,
         da, blockIdx.x, decode_wgs, reinterpret_cast<int32_t*>(lds), reinterpret_cast<int32_t*>(lds + L::pre),
         lds + L::pre + L::part, lds + L::pre + L::part + L::chunk);
   } else {
+    // one prefill work item per workgroup, numbered as the prefill launch
+    // numbers them (the decode workers are a multiple of 8, so an item keeps
+    // its XCD).  Taking items from the work queues instead measured no
+    // faster here: the decode workers already fill the CUs' other half.
     using P = pf::Lds<CT, D>;
-    pf::Item it;
-    if (pf::item_of((int)blockIdx.x - decode_wgs, q_tiles, pa.batch * pa.num_kv_heads, pa.num_kv_heads, it))
-      pf::prefill_body<CT, D, true>(pa, it, lds, lds + P::stage, lds + 2 * P::stage,
-                                    reinterpret_cast<uint32_t*>(lds + P::bytes));
+    pf::prefill_items<CT, D, true>(pa, q_tiles, -1, (int)blockIdx.x - decode_wgs, lds, lds + P::stage,
+                                   lds + 2 * P::stage, reinterpret_cast<uint32_t*>(lds + P::bytes),
+                                   reinterpret_cast<int*>(lds + P::bytes + 16));
   }
 #endif
 }
@@ -77,8 +80,6 @@ hipError_t launch_mixed_g(const DecodeArgs& da, const PrefillArgs& pa, hipStream
   const int q_tiles = pf::tiles_of(pa.max_seqlen_q, pa.num_heads / pa.num_kv_heads);
   const int64_t items = pf::grid_of(q_tiles, pa.batch, pa.num_kv_heads);
   if (items > 0x7fffffff / 2) return hipErrorInvalidValue;
-  // one workgroup per prefill work item after the decode workers (a
-  // multiple of 8, so an item keeps the XCD the prefill launch gives it)
   const int64_t grid = dwg + items;
   hipLaunchKernelGGL((mixed_kernel<CT, D, G>), dim3((unsigned)grid), dim3(kStreamThreads), 0, stream, da, pa,
                      q_tiles, (int)dwg);

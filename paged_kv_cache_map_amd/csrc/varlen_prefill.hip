@@ -45,11 +45,17 @@
 //   end of the request (tile 0 = the last rows, which see the most keys), and
 //   dealt so that the pairs (request, KV head) go round-robin over the 8
 //   XCDs: the tiles sharing a pair's K/V share one L2, and the longest tiles
-//   of every request run first.
+//   of every request run first.  A persistent grid (two workgroups a CU)
+//   takes the items at run time from one counter per XCD, then from the
+//   other XCDs' counters once its own runs dry: CUs and XCDs run at
+//   different speeds under this load, and a fixed deal of the items leaves
+//   the fast ones idle at the end.  The counters are a small static array,
+//   one set per stream, cleared by a fill kernel before each launch.
 //
 // fp32 kernel: a plain per-row wave kernel (lanes over head_dim), kept for
 // fp32 accuracy checks; it is not tuned.
 
+#include <mutex>
 #include <type_traits>
 
 #include "pkv_device.hpp"
@@ -269,6 +275,39 @@ __device__ __forceinline__ Request request(const PrefillArgs& a, int b) {
     else if (r.lk > a.total_k - r.k_start) r.lk = a.total_k - r.k_start;
   }
   return r;
+}
+
+// Work items are handed out at run time: a persistent grid (the
+// workgroups that fit on the GPU) takes them from one counter per XCD, in
+// item_of() order on that XCD (the last query tiles of every request
+// first, so the longest items start first); a workgroup whose XCD has none
+// left takes the other XCDs' items.  Workgroups on slower CUs or XCDs simply
+// take fewer items, and no workgroup slot waits for the dispatcher.  The
+// counters live in a small static array holding kQueueSlots sets; each
+// stream has a set of its own (kernels on one stream never overlap), which
+// queue_reset_kernel clears on that stream just before each launch.
+constexpr int kQueueSlots = 64;
+constexpr int kQueueStride = 32;  // words between two counters (one 128-byte line each)
+__device__ uint32_t g_queue[kQueueSlots * 8 * kQueueStride];
+
+__global__ void queue_reset_kernel(int slot) {
+  if (threadIdx.x < 8) g_queue[(slot * 8 + threadIdx.x) * kQueueStride] = 0u;
+}
+
+// The next work item (item_of() number: item j of XCD xx is 8 j + xx) for a
+// workgroup on XCD x, or -1 when every counter is past its XCD's items.
+// `dry` marks the counters this workgroup found empty.  One lane calls it.
+__device__ __forceinline__ int next_item(uint32_t* queues, int x, int q_tiles, int pairs, uint32_t& dry) {
+#pragma unroll 1
+  for (int d = 0; d < 8; ++d) {
+    const int xx = (x + d) & 7;
+    if ((dry >> xx) & 1u) continue;
+    const uint32_t n = (uint32_t)q_tiles * (uint32_t)((pairs - xx + 7) >> 3);  // items on XCD xx
+    const uint32_t j = atomicAdd(queues + xx * kQueueStride, 1u);
+    if (j < n) return (int)(8 * j + xx);
+    dry |= 1u << xx;
+  }
+  return -1;
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
@@ -686,8 +725,37 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
   }
 }
 
+// The work items of one workgroup: with a counter set (slot >= 0), items
+// from the queues until they are empty; else work item `hw` alone.  `item`:
+// an int of LDS to share the next item through.
 template <int KVT, int D, bool PAGED>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int q_tiles) {
+__device__ __forceinline__ void prefill_items(const PrefillArgs& a, int q_tiles, int slot, int hw, uint8_t* s0,
+                                              uint8_t* s1, uint8_t* bf, uint32_t* flags, int* item) {
+  const int pairs = a.batch * a.num_kv_heads;
+  if (slot < 0) {
+    Item it;
+    if (item_of(hw, q_tiles, pairs, a.num_kv_heads, it)) prefill_body<KVT, D, PAGED>(a, it, s0, s1, bf, flags);
+    return;
+  }
+  uint32_t* const queues = g_queue + slot * 8 * kQueueStride;
+  const int x = blockIdx.x & 7;  // this workgroup's XCD
+  uint32_t dry = 0;
+  for (;;) {  // ends once every counter is past its XCD's items
+    if (threadIdx.x == 0) *item = next_item(queues, x, q_tiles, pairs, dry);
+    __syncthreads();
+    const int next = *item;
+    __syncthreads();  // every wave has read it before lane 0 writes the next
+    if (next < 0) break;
+    Item it;
+    if (item_of(next, q_tiles, pairs, a.num_kv_heads, it)) {
+      prefill_body<KVT, D, PAGED>(a, it, s0, s1, bf, flags);
+      __syncthreads();  // the next item's copies reuse the buffers
+    }
+  }
+}
+
+template <int KVT, int D, bool PAGED>
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int q_tiles, int slot) {
   // The body is device code only: the host pass of the compiler, which
   // needs no more than the kernel's signature, rejects some of its template
   // instantiations when both one-byte cache types are built in one file.
@@ -696,10 +764,46 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int
   __shared__ __attribute__((aligned(1024))) uint8_t s0[L::stage], s1[L::stage];
   __shared__ __attribute__((aligned(1024))) uint8_t bf[L::bf16 > 0 ? L::bf16 : 16];
   __shared__ uint32_t flags[2];
-  Item it;
-  if (item_of(blockIdx.x, q_tiles, a.batch * a.num_kv_heads, a.num_kv_heads, it))
-    prefill_body<KVT, D, PAGED>(a, it, s0, s1, bf, flags);
+  __shared__ int item;
+  prefill_items<KVT, D, PAGED>(a, q_tiles, slot, blockIdx.x, s0, s1, bf, flags, &item);
 #endif
+}
+
+// The counter set of a stream: each stream gets one of its own on first use
+// (kQueueSlots in all; -1 once they are taken, and the launch then runs one
+// workgroup per item).
+__host__ inline int queue_slot(hipStream_t stream) {
+  static std::mutex mu;
+  static hipStream_t keys[kQueueSlots];
+  static int used = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (keys[i] == stream) return i;
+  if (used == kQueueSlots) return -1;
+  keys[used] = stream;
+  return used++;
+}
+
+// Clear a counter set before a launch that uses it (a fill kernel rather
+// than a memset, so that the call can be captured in a graph).
+__host__ inline hipError_t reset_queues(int slot, hipStream_t stream) {
+  hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, stream, slot);
+  return hipGetLastError();
+}
+
+// Persistent workgroups: as many as fit on the GPU at once (occupancy x
+// CUs), never more than the items.
+__host__ inline int64_t workers_for(int64_t items, int per_cu) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    cus = (hipGetDevice(&dev) == hipSuccess &&
+           hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+              ? n
+              : 256;
+  }
+  const int64_t w = (int64_t)cus * per_cu;
+  return items < w ? items : w;
 }
 
 template <int KVT, int D, bool PAGED>
@@ -708,7 +812,14 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const int64_t items = grid_of(q_tiles, a.batch, a.num_kv_heads);
   if (items == 0) return hipSuccess;
   if (items > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<KVT, D, PAGED>), dim3((unsigned)items), dim3(kThreads), 0, stream, a, q_tiles);
+  const int slot = queue_slot(stream);
+  if (slot >= 0) {
+    const hipError_t e = reset_queues(slot, stream);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t grid = slot >= 0 ? workers_for(items, 2) : items;
+  hipLaunchKernelGGL((prefill_kernel<KVT, D, PAGED>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a, q_tiles,
+                     slot);
   return hipGetLastError();
 }
 
