@@ -1,11 +1,13 @@
 /*
  * pkv.h -- C ABI of libpkv.so: attention over a paged KV cache on AMD MI355X
- * (gfx950).  Hand-written HIP kernels behind six calls:
+ * (gfx950).  Hand-written HIP kernels behind seven calls:
  *
  *   pkv_kv_cache_write   scatter the step's new K/V rows into cache slots
  *   pkv_paged_decode     one query per sequence over its cached keys
  *   pkv_paged_decode_append  the same decode storing the step's new K/V rows
  *                        itself (one launch for write + decode)
+ *   pkv_paged_decode_noalloc the decode with library-held scratch, for
+ *                        callers that cannot allocate
  *   pkv_varlen_prefill   causal attention for a packed batch of query chunks
  *   pkv_mixed_attention  a chunked-prefill step's prefill and decode in one launch
  *   pkv_copy_blocks      copy-on-write of whole cache blocks
@@ -187,6 +189,35 @@ int pkv_paged_decode(void* out, const void* q, int q_dtype,
                      int32_t block_size, int32_t num_blocks, float softmax_scale,
                      int32_t split_keys, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * pkv_paged_decode_noalloc -- pkv_paged_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same kernels and the same results.  The kernels' partial
+ * results go to a static device array of PKV_NOALLOC_SCRATCH_BYTES (32 MiB)
+ * that each GPU holds from this call's first use on it until the process
+ * ends; the call itself allocates nothing (no hipMalloc, no hipFree).
+ *   Limit: sizes whose pkv_paged_decode_workspace_size exceeds
+ *   PKV_NOALLOC_SCRATCH_BYTES are rejected with PKV_ERR_INVALID (the
+ *   automatic plan at batch 256, 8 KV heads, G = 4, head_dim 128 needs about
+ *   12 MiB).  PKV_VALIDATE is ignored: its checks copy metadata to the host.
+ *   Sharing: every call on one GPU uses that GPU's one array, and nothing in
+ *   it needs to start at any value.  Calls whose kernels overlap in time on
+ *   one GPU (on different streams, or replays of captured graphs) race on it
+ *   and give wrong results; serialise them.
+ * Errors: those of pkv_paged_decode, and PKV_ERR_LAUNCH when the array's
+ * device address cannot be obtained.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int pkv_paged_decode_noalloc(void* out, const void* q, int q_dtype,
+                             const void* k_cache, const void* v_cache, int cache_dtype,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                             const int32_t* cache_seqlens, int32_t batch,
+                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, float softmax_scale,
+                             int32_t split_keys, void* stream);
 
 /*
  * pkv_paged_decode_append -- the decode step with its own cache write.

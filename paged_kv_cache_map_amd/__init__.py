@@ -65,6 +65,9 @@ def _load_library():
     lib.pkv_paged_decode.restype = ctypes.c_int
     lib.pkv_paged_decode.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, i32, vp,
                                      i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.pkv_paged_decode_noalloc.restype = ctypes.c_int
+    lib.pkv_paged_decode_noalloc.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, i32, vp,
+                                             i32, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.pkv_paged_decode_append.restype = ctypes.c_int
     lib.pkv_paged_decode_append.argtypes = [vp, vp, ctypes.c_int, vp, i64, vp, i64, vp, vp, ctypes.c_int,
                                             vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, i32,
@@ -201,6 +204,30 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale,
         b, hq, hkv, d, bs, nb, float(softmax_scale), int(split_keys), _ptr(workspace), ws_bytes,
         _stream(stream)))
     return out
+
+
+def paged_decode_noalloc(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, k_scale=None,
+                         v_scale=None, out=None, split_keys=0, stream=None):
+    """``paged_decode`` with the library's static scratch array instead of a workspace:
+    the C call allocates nothing (``out`` is allocated here only when not given)."""
+    import torch
+    _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B, Hq, D]")
+    _require(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+    _require(block_table.dim() == 2 and block_table.is_contiguous() and
+             block_table.dtype == torch.int32, "block_table must be contiguous int32 [B, max_blocks]")
+    _require(cache_seqlens.dtype == torch.int32, "cache_seqlens must be int32")
+    b, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(library().pkv_paged_decode_noalloc(
+        _ptr(out), _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens),
+        b, hq, hkv, d, bs, nb, float(softmax_scale), int(split_keys), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_NOALLOC_SCRATCH_BYTES
 
 
 def paged_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, softmax_scale,

@@ -22,7 +22,7 @@ ROCM = pathlib.Path(os.environ.get("ROCM_PATH", "/opt/rocm"))
 
 # attention.hip includes paged_decode.hip and varlen_prefill.hip (one unit: the
 # mixed-step kernel runs the bodies of both)
-HIP_SOURCES = ["kv_write.hip", "attention.hip", "block_copy.hip"]
+HIP_SOURCES = ["kv_write.hip", "attention.hip", "block_copy.hip", "decode_scratch.hip"]
 HOST_SOURCES = ["pkv_api.cpp", "pkv_plan.cpp", "pkv_blocks.cpp"]
 
 HIPCC_FLAGS = [

@@ -106,7 +106,8 @@ int decode_common(const char* name, const NewRows& nr, void* out, const void* q,
                   const int32_t* cache_seqlens, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
                   int32_t head_dim, int32_t block_size, int32_t num_blocks, float softmax_scale,
                   int32_t split_keys, void* workspace, size_t workspace_bytes, void* stream,
-                  pkv::DecodeArgs* prepared = nullptr, pkv::DecodePlan* prepared_plan = nullptr) {
+                  pkv::DecodeArgs* prepared = nullptr, pkv::DecodePlan* prepared_plan = nullptr,
+                  bool library_scratch = false) {
   const bool append = nr.k != nullptr || nr.v != nullptr;
   if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
     return fail(PKV_ERR_INVALID, "%s: sizes must be positive", name);
@@ -145,13 +146,24 @@ int decode_common(const char* name, const NewRows& nr, void* out, const void* q,
   if (!pkv::plan_decode(batch, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                         split_keys, cache_dtype != PKV_F32, &plan, &why))
     return fail(PKV_ERR_INVALID, "%s: %s", name, why);
+  if (library_scratch && plan.workspace_bytes > 0) {  // the static array instead of a workspace
+    if (plan.workspace_bytes > pkv::kNoAllocScratchBytes)
+      return fail(PKV_ERR_INVALID,
+                  "%s: these sizes need %zu bytes of decode scratch, above the %zu of the static array "
+                  "(call pkv_paged_decode with a workspace instead)",
+                  name, plan.workspace_bytes, pkv::kNoAllocScratchBytes);
+    const hipError_t e = pkv::noalloc_scratch(&workspace);
+    if (e != hipSuccess)
+      return fail(PKV_ERR_LAUNCH, "%s: no device address for the scratch array: %s", name, hipGetErrorString(e));
+    workspace_bytes = pkv::kNoAllocScratchBytes;
+  }
   if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes > 0 && !workspace))
     return fail(PKV_ERR_INVALID, "%s: workspace of %zu bytes needed, %zu given", name,
                 plan.workspace_bytes, workspace_bytes);
   if (plan.workspace_bytes > 0 && !aligned16(workspace))
     return fail(PKV_ERR_INVALID, "%s: workspace must be 16-byte aligned", name);
   hipStream_t s = (hipStream_t)stream;
-  if (validate_mode()) {
+  if (!library_scratch && validate_mode()) {  // (its checks copy metadata to host memory)
     std::vector<int32_t> lens, table;
     if (!fetch(lens, cache_seqlens, batch, s) ||
         !fetch(table, block_table, (int64_t)batch * max_blocks_per_seq, s))
@@ -412,6 +424,20 @@ int pkv_paged_decode(void* out, const void* q, int q_dtype, const void* k_cache,
                        v_scale, block_table, max_blocks_per_seq, cache_seqlens, batch, num_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, softmax_scale, split_keys, workspace,
                        workspace_bytes, stream);
+}
+
+static_assert(pkv::kNoAllocScratchBytes == PKV_NOALLOC_SCRATCH_BYTES, "one size for the scratch array");
+
+int pkv_paged_decode_noalloc(void* out, const void* q, int q_dtype, const void* k_cache, const void* v_cache,
+                             int cache_dtype, const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                             const int32_t* cache_seqlens, int32_t batch, int32_t num_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                             float softmax_scale, int32_t split_keys, void* stream) {
+  return decode_common("paged_decode_noalloc", NewRows{}, out, q, q_dtype, k_cache, v_cache, cache_dtype,
+                       k_scale, v_scale, block_table, max_blocks_per_seq, cache_seqlens, batch, num_heads,
+                       num_kv_heads, head_dim, block_size, num_blocks, softmax_scale, split_keys, nullptr, 0,
+                       stream, nullptr, nullptr, true);
 }
 
 int pkv_paged_decode_append(void* out, const void* q, int q_dtype, const void* k_new, int64_t k_new_stride,

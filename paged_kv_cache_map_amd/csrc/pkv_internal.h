@@ -90,6 +90,14 @@ struct DecodeArgs {
 
 hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 
+// Bytes of the static decode scratch array (one per GPU) behind
+// pkv_paged_decode_noalloc; equal to PKV_NOALLOC_SCRATCH_BYTES.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+
+// Device address of that array on the current device (looked up once per
+// device, on the first call with that device current).
+hipError_t noalloc_scratch(void** ptr);
+
 struct PrefillArgs {
   void* out;
   const void* q;

@@ -21,6 +21,7 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for want in ("pkv_kv_cache_write", "pkv_paged_decode", "pkv_paged_decode_append",
+                 "pkv_paged_decode_noalloc",
                  "pkv_varlen_prefill", "pkv_paged_decode_workspace_size", "pkv_last_error",
                  "pkv_version", "pkv_copy_blocks", "pkv_block_manager_create",
                  "pkv_block_manager_append_slot", "pkv_block_hash"):
@@ -101,6 +102,47 @@ def decode(**kw):
 ])
 def test_decode_rejects(kw, code):
     assert decode(**kw) == code
+
+
+def decode_noalloc(**kw):
+    a = dict(out=FAKE, q=FAKE, qdt=pkv.BF16, kc=FAKE, vc=FAKE, cdt=pkv.BF16, ksc=NULL, vsc=NULL,
+             bt=FAKE, maxblk=4, sl=FAKE, b=3, hq=8, hkv=2, d=128, bs=16, nb=10, scale=0.1, split=0,
+             stream=NULL)
+    a.update(kw)
+    return pkv.library().pkv_paged_decode_noalloc(
+        a["out"], a["q"], a["qdt"], a["kc"], a["vc"], a["cdt"], a["ksc"], a["vsc"], a["bt"],
+        a["maxblk"], a["sl"], a["b"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"],
+        a["split"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=0), pkv.ERR_INVALID),
+    (dict(q=NULL), pkv.ERR_INVALID),
+    (dict(d=80), pkv.ERR_UNSUPPORTED),
+    (dict(cdt=pkv.FP8_E4M3), pkv.ERR_INVALID),        # fp8 without scales
+    (dict(split=100), pkv.ERR_INVALID),
+    # stream-K plan at batch 2048, 8 KV heads, G = 4: (4096 + 16384) partial
+    # slots x 4 heads x 130 floats = 42.6 MB, above the 32 MiB array
+    (dict(b=2048, hq=32, hkv=8), pkv.ERR_INVALID),
+    # fixed splits of 128 keys over 4096-key tables: 64 x 32 x 32 x 130 floats
+    (dict(b=64, hq=32, hkv=8, maxblk=256, split=128), pkv.ERR_INVALID),
+])
+def test_decode_noalloc_rejects(kw, code):
+    assert decode_noalloc(**kw) == code
+    assert b"paged_decode_noalloc" in pkv.library().pkv_last_error()
+
+
+def test_decode_noalloc_limit_is_the_workspace_size():
+    """The no-alloc decode takes exactly the sizes whose workspace fits the
+    static array: the rejection above is the size rule, not another check."""
+    limit = pkv.NOALLOC_SCRATCH_BYTES
+    assert limit == 32 << 20
+    assert pkv.paged_decode_workspace_size(2048, 32, 8, 128, 16, 4, 0) > limit
+    assert pkv.paged_decode_workspace_size(64, 32, 8, 128, 16, 256, 128) > limit
+    assert 0 < pkv.paged_decode_workspace_size(256, 32, 8, 128, 16, 1017, 0) <= limit
+    assert 0 < pkv.paged_decode_workspace_size(8, 64, 8, 128, 16, 8193, 0) <= limit
+    text = HEADER.read_text()
+    assert "#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in text
 
 
 def append(**kw):
