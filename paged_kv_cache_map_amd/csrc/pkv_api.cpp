@@ -1,6 +1,7 @@
 // extern "C" entry points of libpkv.so: argument checks, the optional
 // metadata validation (PKV_VALIDATE=1) and dispatch to the kernel launchers.
 #include <hip/hip_runtime_api.h>
+#include <limits.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -129,6 +130,8 @@ int decode_common(const char* name, const NewRows& nr, void* out, const void* q,
   if (!group_ok(num_heads / num_kv_heads))
     return fail(PKV_ERR_UNSUPPORTED, "%s: group size %d not in {1,2,4,8,16}", name,
                 num_heads / num_kv_heads);
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)  // key positions are 32-bit in the kernels
+    return fail(PKV_ERR_INVALID, "%s: max_blocks_per_seq * block_size above 2^31 - 1", name);
   if (scaled_cache(cache_dtype) && (!k_scale || !v_scale))
     return fail(PKV_ERR_INVALID, "%s: fp8 and int8 caches need k_scale and v_scale", name);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
@@ -259,6 +262,8 @@ int prefill_common(void* out, const void* q, int q_dtype, const void* k, const v
                   block_size);
     if (max_blocks_per_seq <= 0 || num_blocks <= 0)
       return fail(PKV_ERR_INVALID, "varlen_prefill: max_blocks_per_seq and num_blocks must be positive");
+    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)  // key positions are 32-bit in the kernels
+      return fail(PKV_ERR_INVALID, "varlen_prefill: max_blocks_per_seq * block_size above 2^31 - 1");
   }
   if (scaled_cache(kv_dtype) && (!k_scale || !v_scale))
     return fail(PKV_ERR_INVALID, "varlen_prefill: fp8 and int8 caches need k_scale and v_scale");

@@ -191,8 +191,9 @@ int pkv_block_manager_append_slot(pkv_block_manager* m, int32_t* table_row, int3
 }
 
 uint64_t pkv_block_hash(uint64_t parent_hash, const int32_t* tokens, int32_t num_tokens) {
-  // FNV-1a (64-bit) over the parent's hash and the token ids, little-endian
-  uint64_t h = 1469598103934665603ull;
+  // FNV-1a (64-bit: offset basis 14695981039346656037, prime 2^40 + 2^8 +
+  // 0xb3) over the parent's hash and the token ids, little-endian
+  uint64_t h = 14695981039346656037ull;
   auto mix = [&h](uint64_t x, int bytes) {
     for (int i = 0; i < bytes; ++i) {
       h ^= (x >> (8 * i)) & 0xffu;

@@ -99,6 +99,8 @@ def decode(**kw):
     (dict(split=100), pkv.ERR_INVALID),               # not a multiple of 128
     (dict(split=128, maxblk=64, wsb=0, ws=NULL), pkv.ERR_INVALID),   # workspace too small
     (dict(out=ODD), pkv.ERR_INVALID),
+    (dict(maxblk=1 << 24, bs=256), pkv.ERR_INVALID),  # key positions past 2^31 - 1
+    (dict(maxblk=(1 << 27) + 1, bs=16), pkv.ERR_INVALID),
 ])
 def test_decode_rejects(kw, code):
     assert decode(**kw) == code
@@ -121,6 +123,7 @@ def decode_noalloc(**kw):
     (dict(d=80), pkv.ERR_UNSUPPORTED),
     (dict(cdt=pkv.FP8_E4M3), pkv.ERR_INVALID),        # fp8 without scales
     (dict(split=100), pkv.ERR_INVALID),
+    (dict(maxblk=1 << 24, bs=256), pkv.ERR_INVALID),  # key positions past 2^31 - 1
     # stream-K plan at batch 2048, 8 KV heads, G = 4: (4096 + 16384) partial
     # slots x 4 heads x 130 floats = 42.6 MB, above the 32 MiB array
     (dict(b=2048, hq=32, hkv=8), pkv.ERR_INVALID),
@@ -168,6 +171,7 @@ def append(**kw):
     (dict(qdt=pkv.F32), pkv.ERR_UNSUPPORTED),         # fp32 q and new rows with a bf16 cache
     (dict(split=100), pkv.ERR_INVALID),
     (dict(split=128, maxblk=64, wsb=0, ws=NULL), pkv.ERR_INVALID),
+    (dict(maxblk=1 << 24, bs=256), pkv.ERR_INVALID),  # key positions past 2^31 - 1
 ])
 def test_append_rejects(kw, code):
     assert append(**kw) == code
@@ -212,6 +216,8 @@ def prefill(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(causal=2), pkv.ERR_INVALID),
+    (dict(bt=FAKE, maxblk=1 << 24, bs=256, nb=10), pkv.ERR_INVALID),  # key positions past 2^31 - 1
+    (dict(bt=FAKE, maxblk=(1 << 27) + 1, bs=16, nb=10), pkv.ERR_INVALID),
     (dict(mq=-1), pkv.ERR_INVALID),
     (dict(hq=9, hkv=2), pkv.ERR_INVALID),
     (dict(kdt=pkv.FP8_E4M3, ksc=FAKE, vsc=FAKE), pkv.ERR_UNSUPPORTED),   # fp8 needs the paged cache

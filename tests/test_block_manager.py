@@ -217,3 +217,33 @@ def test_random_operations_match_the_model(seed):
         held = [b for r, n2 in seqs.values() for b in r[:-(-n2 // bs)]] + extra
         for b in range(nb):
             assert model.ref[b] == held.count(b), b
+
+
+def _fnv1a64(data: bytes) -> int:
+    """FNV-1a, 64-bit: offset basis 14695981039346656037, prime 1099511628211
+    (the published parameters of the Fowler/Noll/Vo hash)."""
+    h = 14695981039346656037
+    for byte in data:
+        h = ((h ^ byte) * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def test_fnv1a64_reference_matches_published_vectors():
+    # test vectors published with the FNV hash: the empty string hashes to the
+    # offset basis itself
+    assert _fnv1a64(b"") == 0xCBF29CE484222325
+    assert _fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert _fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+@pytest.mark.parametrize("parent,tokens", [
+    (0, []),
+    (0, [11, 12, 13, 14]),
+    (0xCBF29CE484222325, [0, 1, 2, 3, 4, 5, 6, 7]),
+    (0xFFFFFFFFFFFFFFFF, [2 ** 31 - 1, 0, 65535, 7]),
+])
+def test_block_hash_is_fnv1a64_of_parent_and_tokens(parent, tokens):
+    """pkv_block_hash = FNV-1a-64 over the parent hash (8 bytes) and the token
+    ids (4 bytes each), little-endian."""
+    data = parent.to_bytes(8, "little") + b"".join(t.to_bytes(4, "little", signed=True) for t in tokens)
+    assert pkv.block_hash(parent, tokens) == _fnv1a64(data)
