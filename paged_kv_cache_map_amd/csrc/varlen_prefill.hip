@@ -55,11 +55,11 @@
 // fp32 kernel: a plain per-row wave kernel (lanes over head_dim), kept for
 // fp32 accuracy checks; it is not tuned.
 
-#include <mutex>
 #include <type_traits>
 
 #include "pkv_device.hpp"
 #include "pkv_internal.h"
+#include "work_queue.hpp"
 
 
 namespace pkv {
@@ -283,16 +283,8 @@ __device__ __forceinline__ Request request(const PrefillArgs& a, int b) {
 // first, so the longest items start first); a workgroup whose XCD has none
 // left takes the other XCDs' items.  Workgroups on slower CUs or XCDs simply
 // take fewer items, and no workgroup slot waits for the dispatcher.  The
-// counters live in a small static array holding kQueueSlots sets; each
-// stream has a set of its own (kernels on one stream never overlap), which
-// queue_reset_kernel clears on that stream just before each launch.
-constexpr int kQueueSlots = 64;
-constexpr int kQueueStride = 32;  // words between two counters (one 128-byte line each)
-__device__ uint32_t g_queue[kQueueSlots * 8 * kQueueStride];
-
-__global__ void queue_reset_kernel(int slot) {
-  if (threadIdx.x < 8) g_queue[(slot * 8 + threadIdx.x) * kQueueStride] = 0u;
-}
+// counters are the stream's prefill set of the work-queue array, cleared on
+// that stream just before each launch.
 
 // The next work item (item_of() number: item j of XCD xx is 8 j + xx) for a
 // workgroup on XCD x, or -1 when every counter is past its XCD's items.
@@ -303,7 +295,7 @@ __device__ __forceinline__ int next_item(uint32_t* queues, int x, int q_tiles, i
     const int xx = (x + d) & 7;
     if ((dry >> xx) & 1u) continue;
     const uint32_t n = (uint32_t)q_tiles * (uint32_t)((pairs - xx + 7) >> 3);  // items on XCD xx
-    const uint32_t j = atomicAdd(queues + xx * kQueueStride, 1u);
+    const uint32_t j = atomicAdd(queues + xx * wq::kStride, 1u);
     if (j < n) return (int)(8 * j + xx);
     dry |= 1u << xx;
   }
@@ -737,7 +729,7 @@ __device__ __forceinline__ void prefill_items(const PrefillArgs& a, int q_tiles,
     if (item_of(hw, q_tiles, pairs, a.num_kv_heads, it)) prefill_body<KVT, D, PAGED>(a, it, s0, s1, bf, flags);
     return;
   }
-  uint32_t* const queues = g_queue + slot * 8 * kQueueStride;
+  uint32_t* const queues = wq::counters(slot);
   const int x = blockIdx.x & 7;  // this workgroup's XCD
   uint32_t dry = 0;
   for (;;) {  // ends once every counter is past its XCD's items
@@ -769,28 +761,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int
 #endif
 }
 
-// The counter set of a stream: each stream gets one of its own on first use
-// (kQueueSlots in all; -1 once they are taken, and the launch then runs one
-// workgroup per item).
-__host__ inline int queue_slot(hipStream_t stream) {
-  static std::mutex mu;
-  static hipStream_t keys[kQueueSlots];
-  static int used = 0;
-  std::lock_guard<std::mutex> lock(mu);
-  for (int i = 0; i < used; ++i)
-    if (keys[i] == stream) return i;
-  if (used == kQueueSlots) return -1;
-  keys[used] = stream;
-  return used++;
-}
-
-// Clear a counter set before a launch that uses it (a fill kernel rather
-// than a memset, so that the call can be captured in a graph).
-__host__ inline hipError_t reset_queues(int slot, hipStream_t stream) {
-  hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, stream, slot);
-  return hipGetLastError();
-}
-
 // Persistent workgroups: as many as fit on the GPU at once (occupancy x
 // CUs), never more than the items.
 __host__ inline int64_t workers_for(int64_t items, int per_cu) {
@@ -812,9 +782,9 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const int64_t items = grid_of(q_tiles, a.batch, a.num_kv_heads);
   if (items == 0) return hipSuccess;
   if (items > 0x7fffffff) return hipErrorInvalidValue;
-  const int slot = queue_slot(stream);
+  const int slot = wq::slot_of(stream);
   if (slot >= 0) {
-    const hipError_t e = reset_queues(slot, stream);
+    const hipError_t e = wq::reset(slot, stream);
     if (e != hipSuccess) return e;
   }
   const int64_t grid = slot >= 0 ? workers_for(items, 2) : items;
