@@ -130,6 +130,17 @@ def sample_pairs(rng, batch, heads, n):
     return sorted(pairs)
 
 
+def unit_pairs(rng, batch, hq, hkv):
+    """One q head, drawn at random, of every (sequence, KV head) unit."""
+    group = hq // hkv
+    return [(b, g * group + int(rng.integers(group))) for b in range(batch) for g in range(hkv)]
+
+
+def sequence_pairs(rng, batch, heads):
+    """Every sequence once (a random q head), plus the first and last pair."""
+    return sorted({(b, int(rng.integers(heads))) for b in range(batch)} | {(0, 0), (batch - 1, heads - 1)})
+
+
 def sample_rows(rng, cu, n):
     """Packed query rows: first and last row of every request plus n random ones."""
     rows = set()

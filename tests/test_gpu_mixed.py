@@ -11,7 +11,7 @@ import torch
 import paged_kv_cache_map_amd as pkv
 import workloads
 from gpu_helpers import (TOL, GpuStep, max_err, oracle_decode, oracle_prefill, oracle_write, out_f64, sample_pairs,
-                         sample_rows, say, to_dev)
+                         sample_rows, say, sequence_pairs, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,10 +66,12 @@ def test_mixed_step_reduced(name):
 
 @pytest.mark.parametrize("name", ["mixed_fp8", "mixed_int8"])
 def test_mixed_step_full_sampled(name):
+    """Every decode sequence once; the first and last row of every prefill
+    chunk and 256 more drawn at random."""
     step = workloads.config(name)
     rng = np.random.default_rng(31)
-    rows = sample_rows(rng, step.prefill_inputs()["cu_seqlens_q"], 48)
-    pairs = sample_pairs(rng, 256, 32, 40)
+    rows = sample_rows(rng, step.prefill_inputs()["cu_seqlens_q"], 256)
+    pairs = sequence_pairs(rng, 256, 32)
     run_mixed(step, rows=rows, pairs=pairs)
 
 

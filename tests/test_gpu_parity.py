@@ -12,7 +12,8 @@ import torch
 
 import workloads
 from gpu_helpers import (TOL, GpuStep, assert_cache_equal, max_err, oracle_decode, oracle_prefill,
-                         oracle_write, out_f64, sample_pairs, sample_rows, say, to_dev)
+                         oracle_write, out_f64, sample_pairs, sample_rows, say, sequence_pairs, to_dev,
+                         unit_pairs)
 import paged_kv_cache_map_amd as pkv
 from oracle import paged
 
@@ -81,8 +82,10 @@ def test_varlen_prefill_prefix_full_sampled():
 
 
 def test_llama70b_long_decode_sampled():
+    """Every (sequence, KV head) unit of the 8 x 131k-key decode, one q head each."""
     step = workloads.config("llama70b_long_decode")
-    pairs = sample_pairs(np.random.default_rng(1), 8, 64, 12)
+    pairs = unit_pairs(np.random.default_rng(1), 8, step.num_heads, step.num_kv_heads)
+    assert len(pairs) == 64
     run_step_and_check(step, full=False, pairs=pairs)
 
 
@@ -93,10 +96,13 @@ def test_mixed_fp8_reduced():
 
 
 def test_mixed_fp8_full_sampled():
+    """Every decode sequence once; the first and last row of every prefill
+    chunk and 256 more drawn at random."""
     step = workloads.config("mixed_fp8")
     rng = np.random.default_rng(2)
-    rows = sample_rows(rng, step.prefill_inputs()["cu_seqlens_q"], 48)
-    pairs = sample_pairs(rng, 256, 32, 40)
+    rows = sample_rows(rng, step.prefill_inputs()["cu_seqlens_q"], 256)
+    pairs = sequence_pairs(rng, 256, 32)
+    assert len(rows) >= 256 + 4 and {b for b, _ in pairs} == set(range(256))
     run_step_and_check(step, full=False, rows=rows, pairs=pairs)
 
 
