@@ -10,7 +10,7 @@
 // issues all of its loads first, with no branch in front of them (addresses
 // are clamped into the rows), and only then learns the token's slot; the
 // stores go through buffer descriptors whose size is zero when the slot is
-// -1 or out of range, so the hardware drops them.  Consecutive lanes touch
+// -1 or out of range, so the hardware drops them, and are non-temporal.  Consecutive lanes touch
 // consecutive bytes of source and destination, every access is a full piece,
 // and no lane waits on the slot map before its reads are in flight.  The
 // kernel is HBM-bound (every byte is read and written once); there is no LDS
@@ -34,6 +34,10 @@ constexpr int kTokensPerWg = 4;  // one token per wave
 #endif
 constexpr int kUnroll = PKV_WRITE_UNROLL;  // source pieces in flight per lane per pass
 constexpr int kWord3 = 0x00020000;
+// Cache policy of the row stores: non-temporal (the rows are not read again
+// by this kernel, and leaving them out of the caches keeps the source rows,
+// often fresh from the kernel that produced them, resident).
+constexpr int kStoreNT = 2;
 constexpr int kDropped = 0x7ffffff0;  // a buffer offset past any row: the store is dropped
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -41,12 +45,12 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 template <int SRC, int DST>
 __device__ __forceinline__ void store_piece(__amdgpu_buffer_rsrc_t r, int off, u32x4_t v) {
   if constexpr (SRC == DST) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStoreNT);
   } else if constexpr (SRC == kBF16) {
     const u32x2_t w = {v.x, v.y};
-    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, kStoreNT);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b32(v.x, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(v.x, r, off, 0, kStoreNT);
   }
 }
 
