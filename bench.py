@@ -4,15 +4,19 @@
 
 A step is one pass of the hot path over one batch: the KV write of the new
 tokens followed by the attention call(s) that read them (decode, prefill, or
-both for the mixed step).  The headline line measures the Llama-3.1-8B-shaped
-decode step (batch 64, 32/8 heads, head_dim 128, bf16, contexts U{512..4096},
-block size 16) done by the appending decode, which stores the 64 new tokens
-and attends in one call; `value` is that step's algorithmic HBM bytes (write
-+ decode) per second.  The same step as two calls (slot-map write, then the
-plain decode) is reported beside it.  Inputs are resident in HBM before timing starts; the KV pool is
-replicated and rotated so that consecutive steps never find it in the 256 MB
-Infinity Cache.  Kernel durations come from HIP events recorded on the stream
-the kernels run on.  One JSON line is printed.
+both for the mixed step).  The headline line measures the largest decode
+workload that fits one GPU, the Llama-3.1-70B-layer-shaped long-context step
+(8 sequences x 131 072 cached tokens, 64/8 heads, head_dim 128, bf16, block
+size 16, randomly scattered blocks) done by the appending decode, which
+stores the 8 new tokens and attends in one call; `value` is that step's
+algorithmic HBM bytes (write + decode) per second.  The same step as two
+calls (slot-map write, then the plain decode), the Llama-3.1-8B-shaped decode
+(batch 64, contexts U{512..4096}), the varlen prefill and the mixed steps are
+reported beside it, with the prefill kernel's own roofline.  Inputs are
+resident in HBM before timing starts; small KV pools are replicated and
+rotated so that consecutive steps never find them in the 256 MB Infinity
+Cache.  Kernel durations come from HIP events recorded on the stream the
+kernels run on.  One JSON line is printed.
 """
 
 import argparse
@@ -86,33 +90,37 @@ def prefill_flops(step):
     return 4 * step.num_heads * step.head_dim * pairs
 
 
-# HBM traffic of one decode call on the headline workload, from the hardware
-# counters (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, averaged per
-# dispatch), each scaled by bytes / counter of a plain 512 MiB device copy
-# measured in the same runs.  The figures belong to the decode sources with
-# the given digest: after any change to them the traffic is reported as null
-# until the counters are taken again.
-DECODE_TRAFFIC = {"digest": "3e9f96b9fa61984d", "read_bytes": 552071030, "write_bytes": 3891067}
-DECODE_SOURCES = ("paged_kv_cache_map_amd/csrc/paged_decode.hip",
+# HBM traffic of one call of the dominant kernels, from the hardware counters
+# (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, averaged per dispatch), each
+# scaled by bytes / counter of a plain 512 MiB device copy measured in the
+# same runs: the appending decode call (decode kernel + merge) on the headline
+# workload, and the prefill kernel on varlen_prefill_prefix.  The figures
+# belong to the kernel sources with the given digest: after any change to
+# them the traffic is reported as null until the counters are taken again.
+DECODE_TRAFFIC = {"digest": "2717d8d286f446bc", "read_bytes": 4317098516, "write_bytes": 4426414}
+PREFILL_TRAFFIC = {"digest": "2717d8d286f446bc", "read_bytes": 1684944773, "write_bytes": 127662100}
+KERNEL_SOURCES = ("paged_kv_cache_map_amd/csrc/paged_decode.hip",
+                  "paged_kv_cache_map_amd/csrc/varlen_prefill.hip",
                   "paged_kv_cache_map_amd/csrc/attention.hip",
+                  "paged_kv_cache_map_amd/csrc/work_queue.hpp",
                   "paged_kv_cache_map_amd/csrc/pkv_device.hpp",
                   "paged_kv_cache_map_amd/csrc/pkv_plan.cpp",
                   "paged_kv_cache_map_amd/csrc/pkv_internal.h")
 
 
-def decode_sources_digest():
+def kernel_sources_digest():
     import hashlib
     h = hashlib.sha256()
-    for rel in DECODE_SOURCES:
+    for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def decode_traffic():
-    if DECODE_TRAFFIC is None or DECODE_TRAFFIC["digest"] != decode_sources_digest():
+def traffic(table):
+    if table is None or table["digest"] != kernel_sources_digest():
         return None
-    return DECODE_TRAFFIC["read_bytes"] + DECODE_TRAFFIC["write_bytes"]
+    return table["read_bytes"] + table["write_bytes"]
 
 
 # ---------------------------------------------------------------------------
@@ -390,29 +398,78 @@ def measure(name, steps, warmup, split_keys=0, append=False, mixed=False, **over
 # ---------------------------------------------------------------------------
 
 
-def cpu_baseline(step, algorithmic_bytes, min_seconds=10.0):
-    from oracle import paged
+def _threads():
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001 - reporting only
-        blas_threads = 1
-    cores = len(os.sched_getaffinity(0))
-    d = step.decode_append_inputs()
-    reps, t0 = 0, time.perf_counter()
-    while True:  # whole steps, repeated until about ten seconds of CPU work
-        paged.paged_decode_append(d["q"], step.q_dtype, d["k_new"], d["v_new"], step.k_cache, step.v_cache,
-                                  step.cache_dtype, d["block_table"], d["cache_seqlens"], step.scale,
-                                  step.k_scale, step.v_scale)
-        reps += 1
+        blas = 1
+    return blas, len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_decode(step, min_seconds=10.0):
+    """The oracle's decode of whole sequences of the step, over the caches
+    after the step's write (made before timing), one sequence after another
+    until about ten seconds of CPU work; GB/s of the sequences' algorithmic
+    decode bytes."""
+    from oracle import paged
+    blas, cores = _threads()
+    kc, vc = paged.kv_cache_write(step.k_new, step.v_new, step.k_cache, step.v_cache, step.slot_map,
+                                  step.q_dtype, step.cache_dtype, step.k_scale, step.v_scale)
+    d = step.decode_inputs()
+    nseq = len(d["seq_ids"])
+    row = 2 * step.num_kv_heads * step.head_dim * ELT[step.cache_dtype]
+    done, nbytes, keys, t0 = 0, 0, 0, time.perf_counter()
+    while True:
+        sel = [done % nseq]
+        n = int(d["cache_seqlens"][sel[0]])
+        paged.paged_decode(d["q"][sel], step.q_dtype, kc, vc, step.cache_dtype, d["block_table"][sel],
+                           d["cache_seqlens"][sel], step.scale, step.k_scale, step.v_scale)
+        nbytes += n * row + 2 * step.num_heads * step.head_dim * ELT[step.q_dtype] + 4 + 4 * -(-n // step.block_size)
+        keys += n
+        done += 1
         secs = time.perf_counter() - t0
         if secs >= min_seconds:
             break
-    return {"value": round(reps * algorithmic_bytes / secs / 1e9, 4), "unit": "GB/s",
-            "cores": min(cores, blas_threads), "kind": "oracle",
-            "sample": (f"{reps} whole steps of the same workload (append of {len(d['seq_ids'])} tokens + "
-                       f"decode of {len(d['seq_ids'])} sequences), fp64 numpy, {secs:.1f} s; "
-                       f"BLAS threads {blas_threads}, host CPUs available {cores}")}
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": min(cores, blas), "kind": "oracle",
+            "sample": (f"{done} whole sequence{'s' if done != 1 else ''} ({keys} keys, all {step.num_heads} q heads) of the {step.name} "
+                       f"decode, oracle paged_decode over the caches after the step's write, fp64 numpy, "
+                       f"{secs:.1f} s; BLAS threads {blas}, host CPUs available {cores}")}
+
+
+def cpu_baseline_prefill(step, min_seconds=10.0, rows_per_call=64):
+    """The oracle's prefill of consecutive blocks of query rows of the step
+    (64 rows a call, requests in order), over the caches after the step's
+    write, until about ten seconds of CPU work; GFLOP/s of the rows' useful
+    flops (4 Hq D per visible (query, key) pair)."""
+    from oracle import paged
+    blas, cores = _threads()
+    kc, vc = paged.kv_cache_write(step.k_new, step.v_new, step.k_cache, step.v_cache, step.slot_map,
+                                  step.q_dtype, step.cache_dtype, step.k_scale, step.v_scale)
+    p = step.prefill_inputs()
+    cu_q, cu_k = p["cu_seqlens_q"].astype(np.int64), p["cu_seqlens_k"].astype(np.int64)
+    total = int(cu_q[-1])
+    flops, nrows, r0, t0 = 0, 0, 0, time.perf_counter()
+    while True:
+        b = int(np.searchsorted(cu_q, r0, side="right") - 1)
+        r1 = min(r0 + rows_per_call, int(cu_q[b + 1]))
+        rows = np.arange(r0, r1)
+        paged.varlen_prefill(p["q"], step.q_dtype, kc, vc, step.cache_dtype, p["cu_seqlens_q"], p["cu_seqlens_k"],
+                             step.scale, True, block_table=p["block_table"], k_scale=step.k_scale,
+                             v_scale=step.v_scale, rows=rows)
+        lq, lk = int(cu_q[b + 1] - cu_q[b]), int(cu_k[b + 1] - cu_k[b])
+        visible = (rows - cu_q[b]) + (lk - lq) + 1
+        flops += 4 * step.num_heads * step.head_dim * int(np.clip(visible, 0, lk).sum())
+        nrows += len(rows)
+        r0 = r1 % total
+        secs = time.perf_counter() - t0
+        if secs >= min_seconds:
+            break
+    return {"value": round(flops / secs / 1e9, 4), "unit": "GFLOP/s", "cores": min(cores, blas), "kind": "oracle",
+            "sample": (f"{nrows} query rows (blocks of up to {rows_per_call} rows, requests in order) of the "
+                       f"{step.name} prefill, all {step.num_heads} q heads, oracle varlen_prefill over the caches "
+                       f"after the step's write, fp64 numpy, {secs:.1f} s; BLAS threads {blas}, host CPUs "
+                       f"available {cores}")}
 
 
 def main():
@@ -429,21 +486,24 @@ def main():
     if args.only:
         print(f"[bench] {args.only} (diagnostic)", flush=True)
         _, res = measure(args.only, args.steps, args.warmup, args.split_keys, args.append, args.mixed)
+        if args.copy_probe:
+            res["copy_probe"] = copy_probe()
         print(json.dumps({"diagnostic": args.only,
                           **{k: (round(v, 5) if isinstance(v, float) else v) for k, v in res.items()}}),
               flush=True)
         return
 
-    # The headline step stores its 64 new tokens with the appending decode
-    # (one call for write + attention, the decode path's in-place update);
-    # the same step with the slot-map write and the plain decode as two calls
-    # is measured next to it.
-    print("[bench] llama8b_decode (appending decode)", flush=True)
-    step, main_res = measure("llama8b_decode", args.steps, args.warmup, args.split_keys, append=True)
+    # The headline step: the largest decode workload of one GPU, done by the
+    # appending decode (one call for the 8 new rows and the attention); the
+    # same step as two calls, and the 8B-shaped decode both ways, beside it.
+    head = "llama70b_long_decode"
+    print(f"[bench] {head} (appending decode)", flush=True)
+    step, main_res = measure(head, args.steps, args.warmup, args.split_keys, append=True)
     step_bytes = main_res["write_bytes"] + main_res["decode_bytes"]
     value = step_bytes / (main_res["ms_per_step"] * 1e6)
     d = step.decode_inputs()
     achieved = main_res["decode_bytes"] / (main_res["region_ms_per_step"] * 1e6)
+    rnd = lambda res: {k: (round(v, 5) if isinstance(v, float) else v) for k, v in res.items()}
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -457,12 +517,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, random block permutation)",
-        "config": {"workload": "llama8b_decode: Llama-3.1-8B-shaped single-layer decode step "
-                               "(kv write + paged decode, one appending-decode call)",
+        "config": {"workload": "llama70b_long_decode: Llama-3.1-70B-layer-shaped long-context decode step "
+                               "(kv write + paged decode of 8 sequences x 131072 cached tokens, one "
+                               "appending-decode call)",
                    "batch": int(len(d["seq_ids"])), "num_heads": step.num_heads,
                    "num_kv_heads": step.num_kv_heads, "head_dim": step.head_dim,
                    "block_size": step.block_size,
-                   "context": "cached lengths U{512..4096} (+1 new token)",
+                   "context": "131072 cached tokens each (+1 new token)",
                    "keys_total": int(d["cache_seqlens"].sum()),
                    "step_bytes": int(step_bytes)},
         # the timed steps are nothing but back-to-back appending-decode calls:
@@ -472,41 +533,59 @@ def main():
                      "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": decode_traffic(),
+                     "traffic": traffic(DECODE_TRAFFIC),
                      "algorithmic_bytes_per_launch": int(main_res["decode_bytes"]),
                      "avg_launch_ms": round(main_res["region_ms_per_step"], 5),
                      "avg_launch_ms_single_call_events": round(main_res["decode_ms"], 5)},
-        "kernels": {"llama8b_decode": {k: (round(v, 5) if isinstance(v, float) else v)
-                                       for k, v in main_res.items()}},
+        "kernels": {head: rnd(main_res)},
     }
+    print(f"[bench] {head} (slot-map write + plain decode)", flush=True)
+    _, sep = measure(head, args.steps, args.warmup, args.split_keys)
+    line["kernels"][head + "_separate_calls"] = {**rnd(sep), "step_gbs": round(step_bytes / (sep["ms_per_step"] * 1e6), 2)}
+    print("[bench] llama8b_decode (appending decode)", flush=True)
+    s8, r8 = measure("llama8b_decode", args.steps, args.warmup, args.split_keys, append=True)
+    b8 = r8["write_bytes"] + r8["decode_bytes"]
+    line["kernels"]["llama8b_decode"] = {**rnd(r8), "step_gbs": round(b8 / (r8["ms_per_step"] * 1e6), 2),
+                                         "call_gbs": round(r8["decode_bytes"] / (r8["region_ms_per_step"] * 1e6), 2)}
     print("[bench] llama8b_decode (slot-map write + plain decode)", flush=True)
-    _, sep = measure("llama8b_decode", args.steps, args.warmup, args.split_keys)
-    line["kernels"]["llama8b_decode_separate_calls"] = {
-        **{k: (round(v, 5) if isinstance(v, float) else v) for k, v in sep.items()},
-        "step_gbs": round(step_bytes / (sep["ms_per_step"] * 1e6), 2)}
+    _, s8sep = measure("llama8b_decode", args.steps, args.warmup, args.split_keys)
+    line["kernels"]["llama8b_decode_separate_calls"] = {**rnd(s8sep),
+                                                        "step_gbs": round(b8 / (s8sep["ms_per_step"] * 1e6), 2)}
+    pre_step = None
     if args.configs == "all":
-        for name, kw in (("varlen_prefill_prefix", {}), ("llama70b_long_decode", {}),
-                         ("mixed_fp8", {}), ("mixed_int8", {})):
+        for name in ("varlen_prefill_prefix", "mixed_fp8", "mixed_int8"):
             print(f"[bench] {name}", flush=True)
-            _, res = measure(name, max(3, args.steps // 4), 2, args.split_keys, **kw)
-            line["kernels"][name] = {k: (round(v, 5) if isinstance(v, float) else v)
-                                     for k, v in res.items()}
+            st, res = measure(name, max(3, args.steps // 4), 2, args.split_keys)
+            if name == "varlen_prefill_prefix":
+                pre_step = st
+            line["kernels"][name] = rnd(res)
         for name in ("mixed_fp8", "mixed_int8"):
             print(f"[bench] {name} (one mixed-step call)", flush=True)
             _, res = measure(name, max(3, args.steps // 2), 3, args.split_keys, mixed=True)
-            sep = line["kernels"][name]
+            sep_calls = line["kernels"][name]
             line["kernels"][name + "_one_call"] = {
                 "ms_per_step": round(res["ms_per_step"], 5), "region_ms_per_step": round(res["region_ms_per_step"], 5),
                 "mixed_call_ms": round(res["mixed_call_ms"], 5),
-                "separate_calls_ms": round(sep["prefill_ms"] + sep["decode_ms"], 5)}
+                "separate_calls_ms": round(sep_calls["prefill_ms"] + sep_calls["decode_ms"], 5)}
         pre = line["kernels"]["varlen_prefill_prefix"]
+        # the prefill call's events bracket its counter-clearing kernel (a few
+        # microseconds) and the prefill kernel
+        line["roofline_prefill"] = {
+            "kernel": "prefill_kernel<bf16, D=128, paged> (varlen_prefill_prefix call)",
+            "bound": "mfma", "achieved": pre["prefill_tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(pre["prefill_tflops"] / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic(PREFILL_TRAFFIC),
+            "algorithmic_flops_per_launch": int(pre["prefill_flops"]),
+            "avg_launch_ms": pre["prefill_ms"]}
         line["secondary"] = {
             "varlen_prefill_tflops": pre["prefill_tflops"],
             "varlen_prefill_frac_mfma": pre["prefill_frac_mfma"],
             "varlen_write_gbs": pre["write_gbs"],
-            "long_decode_gbs": line["kernels"]["llama70b_long_decode"]["decode_gbs"],
+            "llama8b_decode_call_gbs": line["kernels"]["llama8b_decode"]["call_gbs"],
+            "llama8b_decode_step_gbs": line["kernels"]["llama8b_decode"]["step_gbs"],
             "mixed_fp8_decode_gbs": line["kernels"]["mixed_fp8"]["decode_gbs"],
             "mixed_fp8_prefill_tflops": line["kernels"]["mixed_fp8"]["prefill_tflops"],
+            "mixed_fp8_one_call_ms": line["kernels"]["mixed_fp8_one_call"]["mixed_call_ms"],
             "mixed_int8_decode_gbs": line["kernels"]["mixed_int8"]["decode_gbs"],
             "mixed_int8_prefill_tflops": line["kernels"]["mixed_int8"]["prefill_tflops"],
         }
@@ -518,8 +597,16 @@ def main():
         print("[bench] copy probe", flush=True)
         line["kernels"]["copy_probe"] = copy_probe()
     if not args.no_cpu:
-        print("[bench] cpu baseline (oracle)", flush=True)
-        line["cpu_baseline"] = cpu_baseline(step, step_bytes)
+        print(f"[bench] cpu baseline (oracle, {head} decode)", flush=True)
+        line["cpu_baseline"] = cpu_baseline_decode(step)
+        del step
+        if pre_step is None:
+            import workloads
+            pre_step = workloads.config("varlen_prefill_prefix")
+        print("[bench] cpu baseline (oracle, varlen_prefill_prefix prefill)", flush=True)
+        line["cpu_baseline_prefill"] = cpu_baseline_prefill(pre_step)
+        print("[bench] cpu baseline (oracle, llama8b_decode decode)", flush=True)
+        line["cpu_baseline_llama8b_decode"] = cpu_baseline_decode(s8)
     print(json.dumps(line), flush=True)
 
 
