@@ -320,6 +320,9 @@ def test_page2_varlen_example_contiguous(dtype, causal):
     (4, 2, 64, 8, "bf16"),
     (8, 2, 64, 64, "fp8"),
     (32, 8, 128, 16, "fp8"),
+    (8, 8, 128, 8, "fp8"),       # fp8 P.V at G = 1, block size 8
+    (64, 8, 128, 256, "fp8"),    # G = 8, block size 256
+    (16, 1, 128, 32, "fp8"),     # G = 16
     (4, 2, 64, 16, "f32"),
 ])
 def test_prefill_shapes(hq, hkv, d, bs, dtype):
@@ -331,6 +334,47 @@ def test_prefill_shapes(hq, hkv, d, bs, dtype):
                                 q_dtype="f32" if dtype == "f32" else "bf16", cache_dtype=dtype,
                                 prefix=pre, new=lq, kinds=["prefill"] * 4)
     run_step_and_check(step)
+
+
+@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8", "int8"])
+def test_prefill_bad_block_ids_read_as_empty_blocks(cache_dtype):
+    """Block ids past the pool or negative inside a request's keys: the
+    prefill stays in its buffers and leaves those blocks' keys out, as the
+    decode does.  Expected values: per row, the oracle's attention over the
+    keys it sees that lie in valid blocks."""
+    prefix, new = [200, 90, 300], [120, 64, 33]
+    step = workloads.build_step(f"prefill_bad_blocks_{cache_dtype}", 4321, num_heads=32, num_kv_heads=8,
+                                head_dim=128, block_size=16, q_dtype="bf16", cache_dtype=cache_dtype,
+                                prefix=prefix, new=new, kinds=["prefill"] * 3)
+    say("prefill bad block ids", cache_dtype)
+    g = GpuStep(step)
+    g.write()
+    kc, vc = oracle_write(step)
+    p = step.prefill_inputs()
+    bt = p["block_table"].copy()
+    bs, hkv, hd, hq = step.block_size, step.num_kv_heads, step.head_dim, step.num_heads
+    bt[0, 3] = step.num_blocks + 5     # keys 48..63 of request 0
+    bt[1, 0] = -1                      # keys 0..15 of request 1
+    bt[2, 18] = step.num_blocks        # keys 288..303 of request 2 (the last cached ones and 4 new ones)
+    g.pre_bt = to_dev(bt, "i32")
+    out = out_f64(g.prefill())
+    cu_q, cu_k = p["cu_seqlens_q"], p["cu_seqlens_k"]
+    q64 = paged.to_f64(p["q"], step.q_dtype)
+    want = np.zeros_like(out)
+    for b in range(3):
+        lq, lk = int(cu_q[b + 1] - cu_q[b]), int(cu_k[b + 1] - cu_k[b])
+        valid = [j for j in range(lk) if 0 <= bt[b, j // bs] < step.num_blocks]
+        slots = np.array([bt[b, j // bs] * bs + j % bs for j in valid], dtype=np.int64)
+        k64 = np.stack([paged._rows_to_f64(kc.reshape(-1, hkv, hd)[slots][:, gi:gi + 1], cache_dtype,
+                                           step.k_scale, gi)[:, 0] for gi in range(hkv)], axis=1)
+        v64 = np.stack([paged._rows_to_f64(vc.reshape(-1, hkv, hd)[slots][:, gi:gi + 1], cache_dtype,
+                                           step.v_scale, gi)[:, 0] for gi in range(hkv)], axis=1)
+        keys = np.array(valid)
+        for i in range(lq):
+            seen = keys <= i + lk - lq
+            r = int(cu_q[b]) + i
+            want[r] = paged.attention(q64[r][None], k64[seen], v64[seen], step.scale, False)[0]
+    assert max_err(out, want) <= TOL[cache_dtype]
 
 
 def test_prefill_noncausal_contiguous_matches_oracle():
