@@ -77,7 +77,7 @@ hipError_t launch_mixed_g(const DecodeArgs& da, const PrefillArgs& pa, hipStream
   if (dwg * kWaves > kStreamMaxWaves) dwg = kStreamMaxWaves / kWaves;
   if (dwg < 1) dwg = 1;
   dwg = (dwg + 7) / 8 * 8;
-  const int q_tiles = pf::tiles_of(pa.max_seqlen_q, pa.num_heads / pa.num_kv_heads);
+  const int q_tiles = pf::tiles_of(pa.max_seqlen_q, pa.num_heads / pa.num_kv_heads, pf::col_blocks<CT, D>());
   const int64_t items = pf::grid_of(q_tiles, pa.batch, pa.num_kv_heads);
   if (items > 0x7fffffff / 2) return hipErrorInvalidValue;
   const int64_t grid = dwg + items;

@@ -19,7 +19,10 @@
 //   q head) pairs: the G q heads that share a KV head sit side by side
 //   (column c = row c / G, head c % G), so one K/V tile serves all of them,
 //   a workgroup (4 waves, 128 columns) covers 128 / G query rows, and the
-//   causal diagonal crosses fewer rows per tile.
+//   causal diagonal crosses fewer rows per tile.  At head_dim 64 with bf16
+//   caches a wave takes two such 32-column blocks (256 columns a
+//   workgroup), and each K and V operand it reads from LDS feeds both:
+//   the LDS reads per flop, which limit the kernel, are halved.
 // * Per 64-key tile and wave: S^T = K Q^T (keys x columns, 16 MFMAs at
 //   head_dim 128), so each lane holds 16 scores of one column per 32-key
 //   block and its partner lane (l ^ 32) the other 16: the row max needs one
@@ -235,10 +238,20 @@ __device__ __forceinline__ bool item_of(int hw, int q_tiles, int pairs, int num_
   return true;
 }
 
-__host__ __forceinline__ int rows_per_item(int group) { return kWaves * kCols / group; }
+// 32-column blocks per wave.  With two, each K and V operand read from LDS
+// serves two MFMAs, half the LDS reads per flop: bf16 caches at head_dim 64
+// (240 VGPRs, still two workgroups a CU).  Head_dim 128 (two blocks would
+// need about 300 registers a lane) and one-byte caches (their dequantised
+// tiles, and the mixed-step kernel's decode workers beside them) keep one.
+template <int KVT, int D>
+__host__ __device__ constexpr int col_blocks() {
+  return (scaled8(KVT) || D != 64) ? 1 : 2;
+}
 
-__host__ __forceinline__ int tiles_of(int max_seqlen_q, int group) {
-  const int r = rows_per_item(group);
+__host__ __forceinline__ int rows_per_item(int group, int cb) { return kWaves * kCols * cb / group; }
+
+__host__ __forceinline__ int tiles_of(int max_seqlen_q, int group, int cb) {
+  const int r = rows_per_item(group, cb);
   return (max_seqlen_q + r - 1) / r;
 }
 
@@ -422,6 +435,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
                                              uint8_t* bf, uint32_t* flags) {
   constexpr bool ONE = scaled8(KVT);
   static_assert(!ONE || PAGED, "one-byte caches are paged");
+  constexpr int CB = col_blocks<KVT, D>();  // 32-column blocks per wave
   using L = Lds<KVT, D>;
   using C = typename L::C;  // tiles as copied
   using B = typename L::B;  // bf16 tiles the matrix cores read
@@ -435,7 +449,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
 
   const int G = a.num_heads / a.num_kv_heads;  // a power of two (checked on the host)
   const int lg = __builtin_ctz(G);
-  const int rpw = kCols >> lg;  // query rows per wave
+  const int rpw = (kCols * CB) >> lg;  // query rows per wave
   const int rwg = rpw * kWaves;  // per workgroup
 
   const int b = it.b, g = it.g;
@@ -449,10 +463,16 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
   if (key_end < 0) key_end = 0;
   const int n_tiles = (key_end + kBN - 1) / kBN;
 
-  // this lane's column: query row qrow, q head `head`
+  // this lane's column in column block cb: query row qrow[cb], q head
+  // `head` (column 32 cb + col of the wave)
   const int wr0 = r0 + rpw * wave;  // the wave's first row
-  const int qrow = wr0 + (col >> lg);
-  const bool qvalid = qrow >= 0;
+  int qrow[CB];
+  bool qvalid[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    qrow[cb] = wr0 + ((kCols * cb + col) >> lg);
+    qvalid[cb] = qrow[cb] >= 0;
+  }
   const int head = g * G + (col & (G - 1));
   const bool wave_rows = wr0 + rpw > 0;  // the wave has a row that exists
   // keys [0, full_end) are visible to every column of the wave, keys past
@@ -460,7 +480,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
   const int lo_row = max(wr0, 0);
   const int full_end = a.causal ? min(lk, lo_row + offset + 1) : lk;
   const int any_end = a.causal ? min(lk, wr0 + rpw + offset) : lk;
-  const int lim = a.causal ? min(lk, qrow + offset + 1) : lk;
+  int lim[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) lim[cb] = a.causal ? min(lk, qrow[cb] + offset + 1) : lk;
 
   // The row max is taken over unscaled scores, which needs scale > 0: a
   // negative scale is applied as |scale| to -q (bf16 negation is exact), a
@@ -477,12 +499,13 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
   // elements 16 ks + 8 half .. + 7 (rows that do not exist read row 0 and
   // are zeroed once the first tile has landed, so that the q loads and the
   // first copy are in flight together)
-  uint4 qf[KS];
-  {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         ((int64_t)(q_start + (qvalid ? qrow : 0)) * a.num_heads + head) * D + half * 8;
+  uint4 qf[CB][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(qp + ks * 16);
+  for (int cb = 0; cb < CB; ++cb) {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((int64_t)(q_start + (qvalid[cb] ? qrow[cb] : 0)) * a.num_heads + head) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[cb][ks] = *reinterpret_cast<const uint4*>(qp + ks * 16);
   }
 
   // LDS read offsets.  K (A operand of S^T): row 32 kb + col, piece 2 ks + half.
@@ -526,10 +549,15 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
   const int32_t* table = PAGED ? a.block_table + (int64_t)b * a.max_blocks_per_seq : nullptr;
   const int log2bs = PAGED ? __builtin_ctz(a.block_size) : 0;
 
-  f32x16_t o[DB];
+  f32x16_t o[CB][DB];
+  float m[CB], l[CB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
-  float m = kNegBig, l = 0.0f;
+  for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[cb][db] = f32x16_t{};
+    m[cb] = kNegBig;
+    l[cb] = 0.0f;
+  }
 
   // One tile: S^T = K Q^T (two 32-key blocks), mask (only on tiles that
   // cross the causal diagonal or the sequence end, or hold keys in blocks
@@ -537,56 +565,68 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
   // max, lazy running max, p = exp2(s scale - m) packed to bf16 as the B
   // operands of O^T += V^T P^T, row sums of the packed p.
   auto compute = [&](const uint8_t* kt, const uint8_t* vt, int key0, uint32_t bad) __attribute__((always_inline)) {
-    f32x16_t sv[2] = {f32x16_t{}, f32x16_t{}};
+    // each K (and V) operand read serves the CB column blocks
+    f32x16_t sv[CB][2];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) sv[cb][0] = sv[cb][1] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const uint4 kf = *reinterpret_cast<const uint4*>(kt + (kl ^ (ks << 5)) + kb * 32 * RB);
-        sv[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), sv[kb], 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          sv[cb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[cb][ks]), sv[cb][kb], 0, 0, 0);
       }
     // register i of block kb holds key 32 kb + 8 (i / 4) + 4 half + i % 4
     if (key0 + kBN > full_end || bad != 0) {
-      const int lim_rel = lim - key0 - 4 * half;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int cb = 0; cb < CB; ++cb) {
+        const int lim_rel = lim[cb] - key0 - 4 * half;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int grp = 4 * kb + (i >> 2);  // 8-key group, copied by wave grp / 2
-          const bool skip =
-              32 * kb + 8 * (i >> 2) + (i & 3) >= lim_rel || ((bad >> (8 * (grp >> 1) + (grp & 1))) & 1u);
-          sv[kb][i] = skip ? -INFINITY : sv[kb][i];
-        }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int grp = 4 * kb + (i >> 2);  // 8-key group, copied by wave grp / 2
+            const bool skip =
+                32 * kb + 8 * (i >> 2) + (i & 3) >= lim_rel || ((bad >> (8 * (grp >> 1) + (grp & 1))) & 1u);
+            sv[cb][kb][i] = skip ? -INFINITY : sv[cb][kb][i];
+          }
+      }
     }
-    float x = fmaxf(sv[0][0], sv[0][1]);
-#pragma unroll
-    for (int i = 2; i < 16; ++i) x = fmaxf(x, sv[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x = fmaxf(x, sv[1][i]);
-    const float mx = max_halves(x) * scale;
-    // lazy running max: move it (and rescale) only when it grows by > 2^8
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleBits) != 0) {
-      const float mn = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - mn);
-      m = mn;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    }
-    const float neg_m = -m;
     // P^T as bf16 B operands, one per 16-key k-step: the lane's own scores
-    uint4 pb[4];
+    uint4 pb[CB][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kb = ks >> 1, i0 = 8 * (ks & 1);
-      float p[8];
+    for (int cb = 0; cb < CB; ++cb) {
+      float x = fmaxf(sv[cb][0][0], sv[cb][0][1]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = fast_exp2(fmaf(sv[kb][i0 + j], scale, neg_m));
-      pb[ks] = make_uint4(cvt2_bf16(p[0], p[1]), cvt2_bf16(p[2], p[3]), cvt2_bf16(p[4], p[5]), cvt2_bf16(p[6], p[7]));
-      l = dot2_bf16(pb[ks].x, 0x3f803f80u, l);
-      l = dot2_bf16(pb[ks].y, 0x3f803f80u, l);
-      l = dot2_bf16(pb[ks].z, 0x3f803f80u, l);
-      l = dot2_bf16(pb[ks].w, 0x3f803f80u, l);
+      for (int i = 2; i < 16; ++i) x = fmaxf(x, sv[cb][0][i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x = fmaxf(x, sv[cb][1][i]);
+      const float mx = max_halves(x) * scale;
+      // lazy running max: move it (and rescale) only when it grows by > 2^8
+      if (__builtin_amdgcn_ballot_w64(mx > m[cb] + kRescaleBits) != 0) {
+        const float mn = fmaxf(m[cb], mx);
+        const float alpha = fast_exp2(m[cb] - mn);
+        m[cb] = mn;
+        l[cb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[cb][db] *= alpha;
+      }
+      const float neg_m = -m[cb];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int kb = ks >> 1, i0 = 8 * (ks & 1);
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = fast_exp2(fmaf(sv[cb][kb][i0 + j], scale, neg_m));
+        pb[cb][ks] = make_uint4(cvt2_bf16(p[0], p[1]), cvt2_bf16(p[2], p[3]), cvt2_bf16(p[4], p[5]),
+                                cvt2_bf16(p[6], p[7]));
+        l[cb] = dot2_bf16(pb[cb][ks].x, 0x3f803f80u, l[cb]);
+        l[cb] = dot2_bf16(pb[cb][ks].y, 0x3f803f80u, l[cb]);
+        l[cb] = dot2_bf16(pb[cb][ks].z, 0x3f803f80u, l[cb]);
+        l[cb] = dot2_bf16(pb[cb][ks].w, 0x3f803f80u, l[cb]);
+      }
     }
     // O^T += V^T P^T; V^T operands by transposed reads (keys 16 ks + 8 x +
     // 4 half + c / 4 of each 16-lane group)
@@ -596,8 +636,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
       for (int db = 0; db < DB; ++db) {
         const uint2 lo = read_tr(vt + voff[db] + 16 * ks * RB);
         const uint2 hi = read_tr(vt + voff[db] + (16 * ks + 8) * RB);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)),
-                                                        as_bf16x8(pb[ks]), o[db], 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          o[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)),
+                                                              as_bf16x8(pb[cb][ks]), o[cb][db], 0, 0, 0);
       }
   };
 
@@ -616,9 +658,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
     // the q rows were loaded before the copies: wait for them alone
     __builtin_amdgcn_s_waitcnt(kWaitVm0 | (2 * C::dma_per_wave));
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = qvalid ? make_uint4(qf[ks].x ^ q_sign, qf[ks].y ^ q_sign, qf[ks].z ^ q_sign, qf[ks].w ^ q_sign)
-                      : make_uint4(0u, 0u, 0u, 0u);
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[cb][ks] = qvalid[cb] ? make_uint4(qf[cb][ks].x ^ q_sign, qf[cb][ks].y ^ q_sign, qf[cb][ks].z ^ q_sign,
+                                             qf[cb][ks].w ^ q_sign)
+                                : make_uint4(0u, 0u, 0u, 0u);
     // Each step: wait for tile t, start the copy of tile t + 1, (one-byte
     // caches: dequantise this wave's rows of tile t), compute tile t if the
     // wave has keys in it, fetch the block-table entries of tile t + 2.
@@ -702,18 +747,21 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
 
   // normalise and store: lane holds O^T elements 32 db + 8 j + 4 half + i of
   // its column (register 4 j + i)
-  const float lt = sum_halves(l);
-  if (qvalid) {
-    const float inv = lt > 0.0f ? (ONE ? ((const __attribute__((address_space(4))) float*)a.v_scale)[g] : 1.0f) / lt
-                                : 0.0f;
-    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q_start + qrow) * a.num_heads + head) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int cb = 0; cb < CB; ++cb) {
+    const float lt = sum_halves(l[cb]);
+    if (qvalid[cb]) {
+      const float inv = lt > 0.0f ? (ONE ? ((const __attribute__((address_space(4))) float*)a.v_scale)[g] : 1.0f) / lt
+                                  : 0.0f;
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q_start + qrow[cb]) * a.num_heads + head) * D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint2*>(op + 32 * db + 8 * j + 4 * half) =
-            make_uint2(cvt2_bf16(o[db][4 * j] * inv, o[db][4 * j + 1] * inv),
-                       cvt2_bf16(o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv));
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint2*>(op + 32 * db + 8 * j + 4 * half) =
+              make_uint2(cvt2_bf16(o[cb][db][4 * j] * inv, o[cb][db][4 * j + 1] * inv),
+                         cvt2_bf16(o[cb][db][4 * j + 2] * inv, o[cb][db][4 * j + 3] * inv));
+    }
   }
 }
 
@@ -753,6 +801,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int
   // instantiations when both one-byte cache types are built in one file.
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = Lds<KVT, D>;
+  // (an AGPR named here lets the register allocator give the accumulators
+  // AGPRs when a wave has a SIMD to itself)
   __shared__ __attribute__((aligned(1024))) uint8_t s0[L::stage], s1[L::stage];
   __shared__ __attribute__((aligned(1024))) uint8_t bf[L::bf16 > 0 ? L::bf16 : 16];
   __shared__ uint32_t flags[2];
@@ -778,7 +828,7 @@ __host__ inline int64_t workers_for(int64_t items, int per_cu) {
 
 template <int KVT, int D, bool PAGED>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
-  const int q_tiles = tiles_of(a.max_seqlen_q, a.num_heads / a.num_kv_heads);
+  const int q_tiles = tiles_of(a.max_seqlen_q, a.num_heads / a.num_kv_heads, col_blocks<KVT, D>());
   const int64_t items = grid_of(q_tiles, a.batch, a.num_kv_heads);
   if (items == 0) return hipSuccess;
   if (items > 0x7fffffff) return hipErrorInvalidValue;
