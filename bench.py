@@ -97,8 +97,8 @@ def prefill_flops(step):
 # workload, and the prefill kernel on varlen_prefill_prefix.  The figures
 # belong to the kernel sources with the given digest: after any change to
 # them the traffic is reported as null until the counters are taken again.
-DECODE_TRAFFIC = {"digest": "2717d8d286f446bc", "read_bytes": 4317098516, "write_bytes": 4426414}
-PREFILL_TRAFFIC = {"digest": "2717d8d286f446bc", "read_bytes": 1684944773, "write_bytes": 127662100}
+DECODE_TRAFFIC = {"digest": "468c2012ef3ba8c6", "read_bytes": 4317085511, "write_bytes": 4426396}
+PREFILL_TRAFFIC = {"digest": "468c2012ef3ba8c6", "read_bytes": 1694819342, "write_bytes": 127689508}
 KERNEL_SOURCES = ("paged_kv_cache_map_amd/csrc/paged_decode.hip",
                   "paged_kv_cache_map_amd/csrc/varlen_prefill.hip",
                   "paged_kv_cache_map_amd/csrc/attention.hip",
