@@ -318,6 +318,10 @@ def test_page2_varlen_example_contiguous(dtype, causal):
     (8, 8, 128, 16, "bf16"),
     (16, 1, 128, 32, "bf16"),
     (4, 2, 64, 8, "bf16"),
+    # bf16 at head_dim 64: two 32-column blocks a wave (64 columns: 64 / G rows)
+    (8, 8, 64, 16, "bf16"),      # G = 1: the second block holds rows 32-63
+    (32, 8, 64, 32, "bf16"),     # G = 4
+    (16, 1, 64, 16, "bf16"),     # G = 16: 4 rows a wave, the second block rows 2-3
     (8, 2, 64, 64, "fp8"),
     (32, 8, 128, 16, "fp8"),
     (8, 8, 128, 8, "fp8"),       # fp8 P.V at G = 1, block size 8
@@ -333,6 +337,17 @@ def test_prefill_shapes(hq, hkv, d, bs, dtype):
                                 head_dim=d, block_size=bs,
                                 q_dtype="f32" if dtype == "f32" else "bf16", cache_dtype=dtype,
                                 prefix=pre, new=lq, kinds=["prefill"] * 4)
+    run_step_and_check(step)
+
+
+def test_prefill_head_dim_64_many_items_per_request():
+    """bf16 at head_dim 64 (two column blocks a wave, 64 rows an item at G =
+    4): requests of up to 700 rows over up to 1000 cached keys span up to 11
+    work items each, with ragged last items and a one-row request."""
+    step = workloads.build_step("prefill_d64_items", 6401, num_heads=32, num_kv_heads=8, head_dim=64,
+                                block_size=16, q_dtype="bf16", cache_dtype="bf16",
+                                prefix=[0, 300, 64, 1000], new=[700, 1, 257, 513],
+                                kinds=["prefill"] * 4)
     run_step_and_check(step)
 
 
@@ -377,9 +392,10 @@ def test_prefill_bad_block_ids_read_as_empty_blocks(cache_dtype):
     assert max_err(out, want) <= TOL[cache_dtype]
 
 
-def test_prefill_noncausal_contiguous_matches_oracle():
+@pytest.mark.parametrize("d", [128, 64])
+def test_prefill_noncausal_contiguous_matches_oracle(d):
     c = workloads.random_varlen_contig("nc", 321, [70, 1, 200, 0, 33], [5, 260, 1, 9, 120],
-                                       num_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16")
+                                       num_heads=8, num_kv_heads=2, head_dim=d, dtype="bf16")
     for causal in (False, True):
         out = pkv.varlen_prefill(to_dev(c.q, "bf16"), to_dev(c.k, "bf16"), to_dev(c.v, "bf16"),
                                  to_dev(c.cu_seqlens_q, "i32"), to_dev(c.cu_seqlens_k, "i32"),
