@@ -52,6 +52,8 @@ def parse():
                     help="diagnostic (--only): store the decode tokens with the appending decode")
     ap.add_argument("--mixed", action="store_true",
                     help="diagnostic (--only): prefill and decode through the one mixed-step call")
+    ap.add_argument("--set", action="append", default=[], metavar="KEY=VALUE",
+                    help="diagnostic (--only): a workload override such as batch=3000 or cache_dtype=fp8")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 512 MiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -485,10 +487,15 @@ def main():
 
     if args.only:
         print(f"[bench] {args.only} (diagnostic)", flush=True)
-        _, res = measure(args.only, args.steps, args.warmup, args.split_keys, args.append, args.mixed)
+        overrides = {}
+        for item in args.set:
+            key, val = item.split("=", 1)
+            overrides[key] = int(val) if val.lstrip("-").isdigit() else val
+        _, res = measure(args.only, args.steps, args.warmup, args.split_keys, args.append, args.mixed,
+                         **overrides)
         if args.copy_probe:
             res["copy_probe"] = copy_probe()
-        print(json.dumps({"diagnostic": args.only,
+        print(json.dumps({"diagnostic": args.only, "overrides": overrides,
                           **{k: (round(v, 5) if isinstance(v, float) else v) for k, v in res.items()}}),
               flush=True)
         return

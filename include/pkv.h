@@ -172,7 +172,8 @@ size_t pkv_paged_decode_workspace_size(int32_t batch, int32_t num_heads, int32_t
  *               multiple of 128.  Long contexts are cut into units processed
  *               in parallel; a second kernel merges their partial results.
  *               The automatic plan deals equal shares of 32-key chunks to a
- *               persistent grid (batch <= 2048), else uses fixed splits.
+ *               persistent grid; a batch over 2048 runs as equal slices of
+ *               at most 2048 sequences, launched in order on `stream`.
  *   workspace   device scratch of at least pkv_paged_decode_workspace_size()
  *               bytes for the same arguments (NULL allowed when that is 0).
  *               Its contents on entry do not matter.
@@ -326,7 +327,7 @@ int pkv_varlen_prefill(void* out, const void* q, int q_dtype,
  * num_blocks, block_size, the head counts, head_dim, softmax_scale and
  * q_dtype.  For one-byte caches (FP8, INT8) at head_dim 128, with a decode
  * batch that the automatic plan serves with its matrix-core stream-K kernel
- * (batch <= 2048), both kinds of work run in ONE kernel launch (each CU runs
+ * in one slice (batch <= 2048), both kinds of work run in ONE kernel launch (each CU runs
  * a decode worker and prefill tiles side by side; then the decode's merge
  * kernel); otherwise the prefill kernel and the decode kernels are launched
  * one after the other.  prefill_batch or decode_batch may be 0 (that part is

@@ -1823,9 +1823,8 @@ hipError_t launch_c(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream
   return hipErrorInvalidValue;
 }
 
-}  // namespace
-
-hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
+// One launch sequence (decode, then merge) over the batch of `a`.
+hipError_t launch_whole(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
   const bool append = a.k_new != nullptr;
   if (p.stream && p.mfma) {
     if (a.cache_dtype == kBF16) return append ? mfd::launch<kBF16, true>(a, stream) : mfd::launch<kBF16, false>(a, stream);
@@ -1842,6 +1841,30 @@ hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p, hipStre
   if (a.cache_dtype == kFP8) return launch_c<kFP8>(a, p, stream);
   if (a.cache_dtype == kI8) return launch_c<kI8>(a, p, stream);
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
+  if (!p.stream || p.slice >= a.batch) return launch_whole(a, p, stream);
+  // Slices of the batch, in stream order: each slice's merge has read the
+  // workspace before the next slice's decode writes it.
+  const int64_t row_bytes = (int64_t)a.num_heads * a.head_dim * (a.q_dtype == kF32 ? 4 : 2);
+  for (int32_t b0 = 0; b0 < a.batch; b0 += p.slice) {
+    DecodeArgs s = a;
+    s.batch = a.batch - b0 < p.slice ? a.batch - b0 : p.slice;
+    s.out = static_cast<uint8_t*>(a.out) + b0 * row_bytes;
+    s.q = static_cast<const uint8_t*>(a.q) + b0 * row_bytes;
+    s.block_table = a.block_table + (int64_t)b0 * a.max_blocks_per_seq;
+    s.cache_seqlens = a.cache_seqlens + b0;
+    if (a.k_new != nullptr) {
+      s.k_new = a.k_new + b0 * a.k_new_stride;
+      s.v_new = a.v_new + b0 * a.v_new_stride;
+    }
+    const hipError_t e = launch_whole(s, p, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace pkv

@@ -512,9 +512,10 @@ int pkv_mixed_attention(const void* k_cache, const void* v_cache, int cache_dtyp
   }
   hipStream_t s = (hipStream_t)stream;
   // one launch for both kinds of work where the shared kernel is built: one-byte
-  // caches at head_dim 128 on the matrix-core decode plan
+  // caches at head_dim 128 on the matrix-core decode plan, the decode batch in
+  // one slice
   const bool fused = has_decode && !p_empty && scaled_cache(cache_dtype) && head_dim == 128 && plan.stream &&
-                     plan.mfma;
+                     plan.mfma && plan.slice >= decode_batch;
   if (fused) return launch_status(pkv::launch_mixed(da, pa, s), "mixed_attention");
   if (!p_empty) {
     const int rc = launch_status(pkv::launch_varlen_prefill(pa, s), "mixed_attention");

@@ -36,7 +36,8 @@ struct DecodePlan {
   int32_t split_keys;   // fixed splits: multiple of kDecodeKeysPerWg
   int32_t num_splits;   // fixed splits: units per sequence at the longest possible length
   int32_t head_groups;  // q-head groups of at most 8 per KV head
-  int64_t stream_slots; // stream-K: partial slots (waves + units)
+  int64_t stream_slots; // stream-K: partial slots (waves + units) of one launch
+  int32_t slice;         // stream-K: sequences per launch (the batch, or equal slices of it)
   size_t workspace_bytes;
 };
 
@@ -45,7 +46,7 @@ constexpr int kDecodeChunk = 32;                              // keys per wave i
 constexpr int kDecodeKeysPerWg = kDecodeWaves * kDecodeChunk;  // 128
 constexpr int kDecodeMaxSplitKeys = 8192;                     // bounds the LDS block table
 constexpr int kStreamThreads = 256;                           // stream-K decode workgroup
-constexpr int kStreamMaxBatch = 2048;                         // LDS chunk-count table
+constexpr int kStreamMaxBatch = 2048;                         // LDS chunk-count table of one launch
 constexpr int kStreamMaxWaves = 4096;                         // bounds the stream-K workspace
 
 // Fills `plan`; returns false (with a message in *why) for arguments the

@@ -36,26 +36,32 @@ bool plan_decode(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t
   int32_t head_groups = use_mfma ? 1 : valu_groups;
   const int64_t max_keys = (int64_t)max_blocks_per_seq * block_size;
   plan->head_groups = head_groups;
-  // Automatic plan: stream-K, when the batch fits its chunk-count table and
-  // the chunk count fits in 31 bits.
-  const int64_t units = (int64_t)batch * num_kv_heads * head_groups;
+  // Automatic plan: stream-K, when the chunk count of a launch fits in 31
+  // bits.  A launch's chunk-count table lives in LDS and holds at most
+  // kStreamMaxBatch sequences: a larger batch runs as equal slices, launched
+  // one after another on the stream, that share one workspace.
+  const int64_t slices = ((int64_t)batch + kStreamMaxBatch - 1) / kStreamMaxBatch;
+  const int32_t slice = (int32_t)((batch + slices - 1) / slices);
+  const int64_t units = (int64_t)slice * num_kv_heads * head_groups;
   const int64_t max_chunks = units * ((max_keys + kDecodeChunk - 1) / kDecodeChunk);
-  if (split_keys == 0 && batch <= kStreamMaxBatch && max_chunks < (int64_t)1 << 31) {
+  if (split_keys == 0 && max_chunks < (int64_t)1 << 31) {
     const int64_t per_unit_heads = group / head_groups;
     plan->stream = true;
     plan->mfma = use_mfma;
     plan->split_keys = 0;
     plan->num_splits = 0;
+    plan->slice = slice;
     plan->stream_slots = kStreamMaxWaves + units;
-    // partial triples of every slot, then the chunk prefix of the batch
+    // partial triples of every slot, then the chunk prefix of the slice
     plan->workspace_bytes =
         (size_t)plan->stream_slots * per_unit_heads * (size_t)(head_dim + 2) * sizeof(float) +
-        (size_t)(batch + 1) * sizeof(int32_t);
+        (size_t)(slice + 1) * sizeof(int32_t);
     return true;
   }
   plan->stream = false;
   plan->mfma = false;
   plan->stream_slots = 0;
+  plan->slice = batch;
   head_groups = valu_groups;  // the fixed-split kernel runs on the vector ALUs
   int64_t sk;
   if (split_keys == 0) {

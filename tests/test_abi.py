@@ -256,6 +256,18 @@ def test_decode_workspace_plan():
     assert pkv.paged_decode_workspace_size(3, 8, 3, 128, 16, 4) == 0
 
 
+def test_decode_workspace_plan_in_slices():
+    """A batch over 2048 (one launch's chunk-count table) runs the stream plan
+    in equal slices that share one workspace: the size is that of one slice."""
+    def stream(b, hq, hkv, d):
+        return (4096 + b * hkv) * (hq // hkv) * (d + 2) * 4 + (b + 1) * 4
+    assert pkv.paged_decode_workspace_size(2048, 8, 2, 128, 16, 4) == stream(2048, 8, 2, 128)
+    assert pkv.paged_decode_workspace_size(2049, 8, 2, 128, 16, 4) == stream(1025, 8, 2, 128)
+    assert pkv.paged_decode_workspace_size(4096, 8, 2, 128, 16, 4) == stream(2048, 8, 2, 128)
+    assert pkv.paged_decode_workspace_size(4100, 8, 2, 128, 16, 4) == stream(1367, 8, 2, 128)
+    assert pkv.paged_decode_workspace_size(65535, 32, 8, 64, 16, 4) == stream(2048, 32, 8, 64)
+
+
 def mixed(**kw):
     a = dict(kc=FAKE, vc=FAKE, cdt=pkv.FP8_E4M3, ksc=FAKE, vsc=FAKE, nb=10, bs=16, hq=8, hkv=2, d=128, scale=0.1,
              qdt=pkv.BF16, pout=FAKE, pq=FAKE, cq=FAKE, ck=FAKE, pb=2, mq=10, mk=10, pbt=FAKE, pmax=4, tq=12,

@@ -170,8 +170,8 @@ def test_append_repeated_steps_grow_the_cache():
 
 
 def test_append_batch_past_the_stream_table():
-    """2100 sequences (more than the stream plan's chunk table holds): the
-    append kernel, then the fixed-split decode."""
+    """2100 sequences (more than one stream launch's chunk table holds): the
+    appending matrix-core stream kernel over two slices of 1050 sequences."""
     rng = np.random.default_rng(23)
     prefix = rng.integers(0, 40, size=2100)
     step = workloads.build_step("append_big_batch", 2100, num_heads=8, num_kv_heads=2, head_dim=64, block_size=16,

@@ -101,9 +101,9 @@ def test_mixed_step_more_decode_waves_than_chunks():
 
 
 def test_mixed_step_two_launch_paths():
-    """head_dim 64 with an fp8 cache, and a decode batch past the stream
-    plan's table: the call launches the prefill and the decode one after the
-    other, with the same results."""
+    """head_dim 64 with an fp8 cache, and a decode batch past one stream
+    launch's table (the decode runs in two slices): the call launches the
+    prefill and the decode one after the other, with the same results."""
     step = workloads.build_step("mixed_fp8_d64", 64, num_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
                                 q_dtype="bf16", cache_dtype="fp8", prefix=[40, 0, 300, 7],
                                 new=[100, 33, 1, 1], kinds=["prefill", "prefill", "decode", "decode"])

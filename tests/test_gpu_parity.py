@@ -284,11 +284,35 @@ def test_decode_bad_block_ids_read_as_empty_blocks(cache_dtype, split):
 
 
 def test_decode_batch_past_the_stream_table():
-    """More sequences than the stream plan's LDS chunk table holds: the
-    library takes the fixed-split plan (vector kernels)."""
+    """More sequences than one stream launch's LDS chunk table holds (2048):
+    the automatic plan runs the matrix-core stream kernels over two slices of
+    1050 sequences, one after the other."""
     step = workloads.config("llama8b_decode", batch=2100, len_lo=1, len_hi=40)
     rng = np.random.default_rng(31)
     run_step_and_check(step, full=False, pairs=sample_pairs(rng, 2100, step.num_heads, 300))
+
+
+@pytest.mark.parametrize("cdt", ["f32", "fp8", "int8"])
+def test_decode_batch_in_uneven_slices(cdt):
+    """4100 sequences: three stream slices of 1367, 1367 and 1366 (the vector
+    stream kernel for fp32, the matrix-core one for the one-byte caches);
+    sampled rows from every slice, the slice edges among them."""
+    rng = np.random.default_rng(37)
+    n = 4100
+    prefix = rng.integers(0, 70, size=n)
+    step = workloads.build_step(f"decode_slices_{cdt}", 4100, num_heads=8, num_kv_heads=2, head_dim=128,
+                                block_size=16, q_dtype="f32" if cdt == "f32" else "bf16", cache_dtype=cdt,
+                                prefix=prefix, new=[1] * n, kinds=["decode"] * n)
+    pairs = sample_pairs(rng, n, 8, 200) + [(b, h) for b in (0, 1366, 1367, 2733, 2734, 4099) for h in (0, 7)]
+    run_step_and_check(step, full=False, pairs=pairs)
+
+
+def test_decode_batch_past_the_stream_table_fixed_splits():
+    """The same batch of 2100 on an explicit fixed-split plan (vector
+    kernels, one grid over the whole batch)."""
+    step = workloads.config("llama8b_decode", batch=2100, len_lo=1, len_hi=300)
+    rng = np.random.default_rng(33)
+    run_step_and_check(step, full=False, pairs=sample_pairs(rng, 2100, step.num_heads, 300), split_keys=128)
 
 
 # ---------------------------------------------------------------------------
