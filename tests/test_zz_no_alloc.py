@@ -66,3 +66,24 @@ def test_noalloc_decode_on_a_side_stream():
                                        stream=side)
     side.synchronize()
     assert torch.equal(ref, got)
+
+
+def test_noalloc_decode_in_slices():
+    """2100 sequences: the stream plan runs two slices of 1050 one after the
+    other, both through the static array."""
+    rng = np.random.default_rng(41)
+    n = 2100
+    step = workloads.build_step("noalloc_slices", 41, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                                q_dtype="bf16", cache_dtype="bf16", prefix=rng.integers(0, 60, size=n),
+                                new=[1] * n, kinds=["decode"] * n)
+    need = pkv.paged_decode_workspace_size(n, 8, 2, 128, 16, step.decode_inputs()["block_table"].shape[1])
+    assert 0 < need <= pkv.NOALLOC_SCRATCH_BYTES, need
+    g = GpuStep(step)
+    g.write()
+    say("noalloc: two slices")
+    ref, got = _both(g)
+    assert torch.equal(ref, got)
+    pairs = [(b, h) for b in (0, 1049, 1050, 2099) for h in range(8)]
+    kc, vc = oracle_write(step)
+    idx = tuple(np.array(pairs).T)
+    assert max_err(out_f64(got)[idx], oracle_decode(step, kc, vc, pairs=pairs)[idx]) <= TOL["bf16"]
