@@ -801,8 +801,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int
   // instantiations when both one-byte cache types are built in one file.
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = Lds<KVT, D>;
-  // (an AGPR named here lets the register allocator give the accumulators
-  // AGPRs when a wave has a SIMD to itself)
   __shared__ __attribute__((aligned(1024))) uint8_t s0[L::stage], s1[L::stage];
   __shared__ __attribute__((aligned(1024))) uint8_t bf[L::bf16 > 0 ? L::bf16 : 16];
   __shared__ uint32_t flags[2];
