@@ -85,10 +85,7 @@ hipError_t launch_mixed_g(const DecodeArgs& da, const PrefillArgs& pa, hipStream
                      q_tiles, (int)dwg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t rows = (int64_t)da.batch * da.num_heads;
-  hipLaunchKernelGGL((stream_merge_kernel<kBF16, D, G>), dim3((unsigned)((rows + kWaves - 1) / kWaves)),
-                     dim3(kStreamThreads), 0, stream, da, 1, (int)(dwg * kWaves));
-  return hipGetLastError();
+  return launch_stream_merge<kBF16, D, G>(da, 1, (int)(dwg * kWaves), stream);
 }
 
 template <int CT>

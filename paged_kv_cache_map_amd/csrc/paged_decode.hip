@@ -890,79 +890,65 @@ __global__ __launch_bounds__(kStreamThreads) void decode_stream_kernel(DecodeArg
 // Combine the partial triples of units split between waves and write zero
 // rows for empty sequences.  One wave per (sequence, q head): one round trip
 // for the prefix, one for every part's (max, sum) (a lane per part), then the
-// parts' outputs, eight in flight per lane:
+// parts' outputs, up to 32 in flight per lane:
 //   out = sum_w o_w 2^(m_w - m) / sum_w l_w 2^(m_w - m),  m = max_w m_w.
-template <int QT, int D, int GW>
-__global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs a, int head_groups,
-                                                                      int W) {
+// Units of at most KB parts (the common case) take one pass with all their
+// parts' rows in flight at once.
+template <int QT, int D, int GW, int KB>
+__device__ __forceinline__ void merge_parts_once(const DecodeArgs& a, int64_t bh, int lane, int64_t T, int W,
+                                                 int wf, int n, int u, int hh) {
   constexpr int NV = D / 64;
-  constexpr int kBatch = 8;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int64_t bh = (int64_t)blockIdx.x * kWaves + wave;
-  if (bh >= (int64_t)a.batch * a.num_heads) return;
-  const int b = (int)(bh / a.num_heads), h = (int)(bh % a.num_heads);
-  const int32_t* pre = stream_prefix(a, GW, D);
-  const int64_t T = pre[a.batch];
-  const int ug = a.num_kv_heads * head_groups;
-  const int G = a.num_heads / a.num_kv_heads;
-  const int gg = (h / G) * head_groups + (h % G) / GW;
-  const int hh = (h % G) % GW;
-  const int nch = (pre[b + 1] - pre[b]) / ug;
-  // (T == 0 implies nch == 0; testing it keeps T's load next to the others)
-  if (nch == 0 || T == 0) {
-#pragma unroll
-    for (int e = 0; e < NV; ++e) store_out<QT>(a.out, bh * D + lane * NV + e, 0.0f);
-    return;
-  }
-  const int64_t ustart = pre[b] + (int64_t)gg * nch;
-  const int wf = wave_of(ustart, T, W), wl = wave_of(ustart + nch - 1, T, W);
-  if (wf == wl) return;  // one wave processed the whole unit and wrote the row
-  const int u = b * ug + gg;
-  const int n = wl - wf + 1;
   const float* ws_o = a.workspace;
   const float* ws_ml = a.workspace + (int64_t)a.stream_slots * GW * D;
-  if (n <= kBatch) {
-    // the common case: every part's (max, sum) and output row in flight at
-    // once (the general loop below, for one pass, in one round trip)
-    const int wj = wf + min(lane, n - 1);
-    const bool has = lane < n && (T * wj / W < T * (wj + 1) / W);
-    const int64_t slot = (int64_t)(wj + u) * GW + hh;
-    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + slot * 2);  // (max, sum), one load
-    const float m_raw = ml.x, l_raw = ml.y;
-    float ov[kBatch][NV];
+  const int wj = wf + min(lane, n - 1);
+  const bool has = lane < n && (T * wj / W < T * (wj + 1) / W);
+  const int64_t slot = (int64_t)(wj + u) * GW + hh;
+  const float2 ml = *reinterpret_cast<const float2*>(ws_ml + slot * 2);  // (max, sum), one load
+  const float m_raw = ml.x, l_raw = ml.y;
+  float ov[KB][NV];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int64_t si = (int64_t)(wf + min(i, n - 1) + u) * GW + hh;
+  for (int i = 0; i < KB; ++i) {
+    const int64_t si = (int64_t)(wf + min(i, n - 1) + u) * GW + hh;
 #pragma unroll
-      for (int e = 0; e < NV; ++e) ov[i][e] = ws_o[si * D + lane * NV + e];
-    }
-    const float mj = has ? m_raw : kNegBig;
-    const float mn = wave_max(mj);
-    const float f = has ? fast_exp2(mj - mn) : 0.0f;
-    const float Ls = wave_sum(has ? l_raw * f : 0.0f);
-    float Of[NV];
-#pragma unroll
-    for (int e = 0; e < NV; ++e) Of[e] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const float fi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), i));
-      const bool use = i < n && fi > 0.0f;
-#pragma unroll
-      for (int e = 0; e < NV; ++e) Of[e] = use ? fmaf(ov[i][e], fi, Of[e]) : Of[e];
-    }
-    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-#pragma unroll
-    for (int e = 0; e < NV; ++e) store_out<QT>(a.out, bh * D + lane * NV + e, Of[e] * inv);
-    return;
+    for (int e = 0; e < NV; ++e) ov[i][e] = ws_o[si * D + lane * NV + e];
   }
-  float mx = kNegBig, L = 0.0f, O[NV];
+  const float mj = has ? m_raw : kNegBig;
+  const float mn = wave_max(mj);
+  const float f = has ? fast_exp2(mj - mn) : 0.0f;
+  const float Ls = wave_sum(has ? l_raw * f : 0.0f);
+  float Of[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) Of[e] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < KB; ++i) {
+    const float fi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), i));
+    const bool use = i < n && fi > 0.0f;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) Of[e] = use ? fmaf(ov[i][e], fi, Of[e]) : Of[e];
+  }
+  const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) store_out<QT>(a.out, bh * D + lane * NV + e, Of[e] * inv);
+}
+
+// The running combination of parts [jb, je) of a unit (wave-wide: a lane per
+// part for the (max, sum) pairs, then the parts' rows kBatch at a time).
+template <int D, int GW>
+__device__ __forceinline__ void merge_range(const DecodeArgs& a, int lane, int64_t T, int W, int wf, int jb,
+                                            int je, int u, int hh, float& mx, float& L, float (&O)[D / 64]) {
+  constexpr int NV = D / 64;
+  constexpr int kBatch = 32;
+  const float* ws_o = a.workspace;
+  const float* ws_ml = a.workspace + (int64_t)a.stream_slots * GW * D;
+  mx = kNegBig;
+  L = 0.0f;
 #pragma unroll
   for (int e = 0; e < NV; ++e) O[e] = 0.0f;
-  for (int j0 = 0; j0 < n; j0 += 64) {
+  for (int j0 = jb; j0 < je; j0 += 64) {
     // lane i: wave wf + j0 + i; waves that own no chunk at all wrote nothing
-    const int j = min(j0 + lane, n - 1);
+    const int j = min(j0 + lane, je - 1);
     const int wj = wf + j;
-    const bool has = j0 + lane < n && (T * wj / W < T * (wj + 1) / W);
+    const bool has = j0 + lane < je && (T * wj / W < T * (wj + 1) / W);
     const int64_t slot = (int64_t)(wj + u) * GW + hh;
     const float m_raw = ws_ml[slot * 2];
     const float l_raw = ws_ml[slot * 2 + 1];
@@ -974,7 +960,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs
 #pragma unroll
     for (int e = 0; e < NV; ++e) O[e] *= alpha;
     mx = mn;
-    const int cnt = min(64, n - j0);
+    const int cnt = min(64, je - j0);
     for (int i0 = 0; i0 < cnt; i0 += kBatch) {
       float ov[kBatch][NV];
 #pragma unroll
@@ -993,9 +979,90 @@ __global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs
       }
     }
   }
+}
+
+// wide = 0: one wave per (sequence, q head) row.  wide = 1 (units split
+// into many parts, few rows): one workgroup per row, its four waves taking a
+// quarter of the parts each and combining their results through LDS in a
+// fixed order.
+template <int QT, int D, int GW>
+__global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs a, int head_groups, int W,
+                                                                      int wide) {
+  constexpr int NV = D / 64;
+  __shared__ float sm_ml[kWaves][2];
+  __shared__ float sm_o[kWaves][D];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // (in the wide form every exit below is taken by the whole workgroup)
+  const int64_t bh = wide ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * kWaves + wave;
+  if (bh >= (int64_t)a.batch * a.num_heads) return;
+  const bool writer = !wide || wave == 0;
+  const int b = (int)(bh / a.num_heads), h = (int)(bh % a.num_heads);
+  const int32_t* pre = stream_prefix(a, GW, D);
+  const int64_t T = pre[a.batch];
+  const int ug = a.num_kv_heads * head_groups;
+  const int G = a.num_heads / a.num_kv_heads;
+  const int gg = (h / G) * head_groups + (h % G) / GW;
+  const int hh = (h % G) % GW;
+  const int nch = (pre[b + 1] - pre[b]) / ug;
+  // (T == 0 implies nch == 0; testing it keeps T's load next to the others)
+  if (nch == 0 || T == 0) {
+    if (writer) {
+#pragma unroll
+      for (int e = 0; e < NV; ++e) store_out<QT>(a.out, bh * D + lane * NV + e, 0.0f);
+    }
+    return;
+  }
+  const int64_t ustart = pre[b] + (int64_t)gg * nch;
+  const int wf = wave_of(ustart, T, W), wl = wave_of(ustart + nch - 1, T, W);
+  if (wf == wl) return;  // one wave processed the whole unit and wrote the row
+  const int u = b * ug + gg;
+  const int n = wl - wf + 1;
+  if (n <= 8) {
+    if (writer) merge_parts_once<QT, D, GW, 8>(a, bh, lane, T, W, wf, n, u, hh);
+    return;
+  }
+  float mx, L, O[NV];
+  if (!wide) {
+    if (n <= 32) return merge_parts_once<QT, D, GW, 32>(a, bh, lane, T, W, wf, n, u, hh);
+    merge_range<D, GW>(a, lane, T, W, wf, 0, n, u, hh, mx, L, O);
+  } else {
+    merge_range<D, GW>(a, lane, T, W, wf, n * wave / kWaves, n * (wave + 1) / kWaves, u, hh, mx, L, O);
+    if (lane == 0) {
+      sm_ml[wave][0] = mx;
+      sm_ml[wave][1] = L;
+    }
+#pragma unroll
+    for (int e = 0; e < NV; ++e) sm_o[wave][lane * NV + e] = O[e];
+    __syncthreads();
+    if (wave != 0) return;
+    mx = fmaxf(fmaxf(sm_ml[0][0], sm_ml[1][0]), fmaxf(sm_ml[2][0], sm_ml[3][0]));
+    L = 0.0f;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) O[e] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) {
+      const float f = fast_exp2(sm_ml[q][0] - mx);
+      L = fmaf(sm_ml[q][1], f, L);
+#pragma unroll
+      for (int e = 0; e < NV; ++e) O[e] = fmaf(sm_o[q][lane * NV + e], f, O[e]);
+    }
+  }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
   for (int e = 0; e < NV; ++e) store_out<QT>(a.out, bh * D + lane * NV + e, O[e] * inv);
+}
+
+// Launches the merge of a stream-K decode whose W waves covered `units`
+// units: the wide form where units average more than 16 parts each.
+template <int QT, int D, int GW>
+hipError_t launch_stream_merge(const DecodeArgs& a, int head_groups, int W, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.batch * a.num_heads;
+  const int64_t units = (int64_t)a.batch * a.num_kv_heads * head_groups;
+  const int wide = (int64_t)W > 16 * units ? 1 : 0;
+  const int64_t grid = wide ? rows : (rows + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL((stream_merge_kernel<QT, D, GW>), dim3((unsigned)grid), dim3(kStreamThreads), 0, stream, a,
+                     head_groups, W, wide);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -1732,10 +1799,7 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
                      dim3(kStreamThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t rows = (int64_t)a.batch * a.num_heads;
-  hipLaunchKernelGGL((stream_merge_kernel<kBF16, D, G>), dim3((unsigned)((rows + kWaves - 1) / kWaves)),
-                     dim3(kStreamThreads), 0, stream, a, 1, (int)(grid * kWaves));
-  return hipGetLastError();
+  return launch_stream_merge<kBF16, D, G>(a, 1, (int)(grid * kWaves), stream);
 }
 
 template <int CT, int D, bool APPEND>
@@ -1773,10 +1837,7 @@ hipError_t launch_stream_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t
                      0, stream, a, p.head_groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t rows = (int64_t)a.batch * a.num_heads;
-  hipLaunchKernelGGL((stream_merge_kernel<QT, D, GW>), dim3((unsigned)((rows + kWaves - 1) / kWaves)),
-                     dim3(kStreamThreads), 0, stream, a, p.head_groups, (int)(grid * kWaves));
-  return hipGetLastError();
+  return launch_stream_merge<QT, D, GW>(a, p.head_groups, (int)(grid * kWaves), stream);
 }
 
 template <int CT, int D, int GW>

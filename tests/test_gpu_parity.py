@@ -212,6 +212,19 @@ def test_decode_units_split_over_many_waves(prefix, hq, hkv, cache):
         assert max_err(out, want) <= TOL[cache]
 
 
+def test_decode_few_units_many_parts():
+    """The per-GPU share of the 70B decode at eight-way tensor parallelism
+    (one KV head, G = 8), shortened: 8 units over the whole grid, about 128
+    parts each, merged by a workgroup per row (four waves, a quarter of the
+    parts each); every row checked, twice for run-to-run bits."""
+    step = workloads.build_step("tp8_share", 92, num_heads=8, num_kv_heads=1, head_dim=128, block_size=16,
+                                q_dtype="bf16", cache_dtype="bf16", prefix=[20000, 19999, 20001, 4096, 12345, 1, 30000,
+                                                                            20000],
+                                new=[1] * 8, kinds=["decode"] * 8)
+    g = run_step_and_check(step)
+    assert torch.equal(g.decode().cpu(), g.decode().cpu()), "run-to-run results differ"
+
+
 def test_decode_zero_length_sequence_gives_zeros():
     step = workloads.config("tiny_decode")
     g = GpuStep(step)

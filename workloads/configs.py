@@ -386,7 +386,8 @@ def config(name: str, **overrides) -> Step:
         seed = 1004
         b = overrides.get("batch", 8)
         length = overrides.get("length", 131072)
-        return build_step(name, seed, num_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
+        return build_step(name, seed, num_heads=overrides.get("num_heads", 64),
+                          num_kv_heads=overrides.get("num_kv_heads", 8), head_dim=128, block_size=16,
                           q_dtype="bf16", cache_dtype="bf16", prefix=np.full(b, length, np.int32),
                           new=np.ones(b, np.int32), kinds=["decode"] * b)
     if name in ("mixed_fp8", "mixed_int8"):
