@@ -933,11 +933,10 @@ __device__ __forceinline__ void merge_parts_once(const DecodeArgs& a, int64_t bh
 
 // The running combination of parts [jb, je) of a unit (wave-wide: a lane per
 // part for the (max, sum) pairs, then the parts' rows kBatch at a time).
-template <int D, int GW>
+template <int D, int GW, int kBatch>
 __device__ __forceinline__ void merge_range(const DecodeArgs& a, int lane, int64_t T, int W, int wf, int jb,
                                             int je, int u, int hh, float& mx, float& L, float (&O)[D / 64]) {
   constexpr int NV = D / 64;
-  constexpr int kBatch = 32;
   const float* ws_o = a.workspace;
   const float* ws_ml = a.workspace + (int64_t)a.stream_slots * GW * D;
   mx = kNegBig;
@@ -981,16 +980,19 @@ __device__ __forceinline__ void merge_range(const DecodeArgs& a, int lane, int64
   }
 }
 
-// wide = 0: one wave per (sequence, q head) row.  wide = 1 (units split
-// into many parts, few rows): one workgroup per row, its four waves taking a
+// MODE 0: one wave per (sequence, q head) row, parts eight at a time (few
+// parts per unit; the fewest registers, for the most rows in flight).
+// MODE 1: the same with up to 32 parts in flight.  MODE 2 (units split into
+// many parts, few rows): one workgroup per row, its four waves taking a
 // quarter of the parts each and combining their results through LDS in a
 // fixed order.
-template <int QT, int D, int GW>
-__global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs a, int head_groups, int W,
-                                                                      int wide) {
+template <int QT, int D, int GW, int MODE>
+__global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs a, int head_groups, int W) {
   constexpr int NV = D / 64;
-  __shared__ float sm_ml[kWaves][2];
-  __shared__ float sm_o[kWaves][D];
+  constexpr bool wide = MODE == 2;
+  constexpr int kB = MODE == 0 ? 8 : 32;
+  __shared__ float sm_ml[wide ? kWaves : 1][2];
+  __shared__ float sm_o[wide ? kWaves : 1][wide ? D : 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   // (in the wide form every exit below is taken by the whole workgroup)
   const int64_t bh = wide ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * kWaves + wave;
@@ -1022,11 +1024,11 @@ __global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs
     return;
   }
   float mx, L, O[NV];
-  if (!wide) {
-    if (n <= 32) return merge_parts_once<QT, D, GW, 32>(a, bh, lane, T, W, wf, n, u, hh);
-    merge_range<D, GW>(a, lane, T, W, wf, 0, n, u, hh, mx, L, O);
+  if constexpr (!wide) {
+    if (MODE == 1 && n <= 32) return merge_parts_once<QT, D, GW, 32>(a, bh, lane, T, W, wf, n, u, hh);
+    merge_range<D, GW, kB>(a, lane, T, W, wf, 0, n, u, hh, mx, L, O);
   } else {
-    merge_range<D, GW>(a, lane, T, W, wf, n * wave / kWaves, n * (wave + 1) / kWaves, u, hh, mx, L, O);
+    merge_range<D, GW, kB>(a, lane, T, W, wf, n * wave / kWaves, n * (wave + 1) / kWaves, u, hh, mx, L, O);
     if (lane == 0) {
       sm_ml[wave][0] = mx;
       sm_ml[wave][1] = L;
@@ -1053,15 +1055,22 @@ __global__ __launch_bounds__(kStreamThreads) void stream_merge_kernel(DecodeArgs
 }
 
 // Launches the merge of a stream-K decode whose W waves covered `units`
-// units: the wide form where units average more than 16 parts each.
+// units, in the form for the parts per unit: at most 8 on average (MODE 0),
+// at most 16 (MODE 1), more (MODE 2, a workgroup per row).
 template <int QT, int D, int GW>
 hipError_t launch_stream_merge(const DecodeArgs& a, int head_groups, int W, hipStream_t stream) {
   const int64_t rows = (int64_t)a.batch * a.num_heads;
   const int64_t units = (int64_t)a.batch * a.num_kv_heads * head_groups;
-  const int wide = (int64_t)W > 16 * units ? 1 : 0;
-  const int64_t grid = wide ? rows : (rows + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL((stream_merge_kernel<QT, D, GW>), dim3((unsigned)grid), dim3(kStreamThreads), 0, stream, a,
-                     head_groups, W, wide);
+  const dim3 narrow_grid((unsigned)((rows + kWaves - 1) / kWaves));
+  if ((int64_t)W <= 8 * units)
+    hipLaunchKernelGGL((stream_merge_kernel<QT, D, GW, 0>), narrow_grid, dim3(kStreamThreads), 0, stream, a,
+                       head_groups, W);
+  else if ((int64_t)W <= 16 * units)
+    hipLaunchKernelGGL((stream_merge_kernel<QT, D, GW, 1>), narrow_grid, dim3(kStreamThreads), 0, stream, a,
+                       head_groups, W);
+  else
+    hipLaunchKernelGGL((stream_merge_kernel<QT, D, GW, 2>), dim3((unsigned)rows), dim3(kStreamThreads), 0, stream,
+                       a, head_groups, W);
   return hipGetLastError();
 }
 
