@@ -559,12 +559,14 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
     l[cb] = 0.0f;
   }
 
-  // One tile: S^T = K Q^T (two 32-key blocks), mask (only on tiles that
-  // cross the causal diagonal or the sequence end, or hold keys in blocks
-  // outside the pool: `bad` bit 8 w + x for wave w's half x), the column
-  // max, lazy running max, p = exp2(s scale - m) packed to bf16 as the B
-  // operands of O^T += V^T P^T, row sums of the packed p.
-  auto compute = [&](const uint8_t* kt, const uint8_t* vt, int key0, uint32_t bad) __attribute__((always_inline)) {
+  // One tile: S^T = K Q^T (two 32-key blocks), after_k() (the caller's
+  // work once the K operands are read), mask (only on tiles that cross the
+  // causal diagonal or the sequence end, or hold keys in blocks outside the
+  // pool: `bad` bit 8 w + x for wave w's half x), the column max, lazy
+  // running max, p = exp2(s scale - m) packed to bf16 as the B operands of
+  // O^T += V^T P^T, row sums of the packed p.
+  auto compute = [&](const uint8_t* kt, const uint8_t* vt, int key0, uint32_t bad,
+                     auto&& after_k) __attribute__((always_inline)) {
     // each K (and V) operand read serves the CB column blocks
     f32x16_t sv[CB][2];
 #pragma unroll
@@ -578,6 +580,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
         for (int cb = 0; cb < CB; ++cb)
           sv[cb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[cb][ks]), sv[cb][kb], 0, 0, 0);
       }
+    after_k();  // the next tile's copies
     // register i of block kb holds key 32 kb + 8 (i / 4) + 4 half + i % 4
     if (key0 + kBN > full_end || bad != 0) {
 #pragma unroll
@@ -664,9 +667,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
         qf[cb][ks] = qvalid[cb] ? make_uint4(qf[cb][ks].x ^ q_sign, qf[cb][ks].y ^ q_sign, qf[cb][ks].z ^ q_sign,
                                              qf[cb][ks].w ^ q_sign)
                                 : make_uint4(0u, 0u, 0u, 0u);
-    // Each step: wait for tile t, start the copy of tile t + 1, (one-byte
-    // caches: dequantise this wave's rows of tile t), compute tile t if the
-    // wave has keys in it, fetch the block-table entries of tile t + 2.
+    // Each step: wait for tile t, locate tile t + 1, (one-byte caches:
+    // dequantise this wave's rows of tile t), compute tile t if the wave has
+    // keys in it, starting the copy of tile t + 1 after the score products,
+    // fetch the block-table entries of tile t + 2.
     auto step = [&](int t, bool work, uint8_t* cur, uint8_t* nxt, uint32_t* fcur, uint32_t* fnxt)
                     __attribute__((always_inline)) {
       // this wave's copies of tile t and its flag byte have landed
@@ -680,12 +684,25 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
       // bit 8 w + x: wave w's half x of tile t lies in a block outside the
       // pool (read now, used after the copies are issued)
       const uint32_t bad_raw = (PAGED && work) ? *fcur : 0u;
+      // The copies of tile t + 1: a wave with keys in tile t issues them from
+      // inside compute(), once its score products have read their K operands,
+      // so that the copies' writes into LDS meet the softmax and the P.V
+      // reads rather than the K reads (a wave without keys here issues them
+      // now).
       if (t + 1 < n_tiles) {
         locate<PAGED>(hv, en, (t + 1) * kBN, lk, log2bs, a.num_blocks, wave, rs32, C::row_bytes);
-        copy_rows<C>(kbase, row_stride, hv, wave, nxt, dk);
-        copy_rows<C>(vbase, row_stride, hv, wave, nxt + C::bytes, dv);
+        if (!work) {
+          copy_rows<C>(kbase, row_stride, hv, wave, nxt, dk);
+          copy_rows<C>(vbase, row_stride, hv, wave, nxt + C::bytes, dv);
+        }
         if constexpr (PAGED) reinterpret_cast<uint8_t*>(fnxt)[wave] = (uint8_t)hv.bad;
       }
+      auto copies = [&]() __attribute__((always_inline)) {
+        if (t + 1 < n_tiles) {
+          copy_rows<C>(kbase, row_stride, hv, wave, nxt, dk);
+          copy_rows<C>(vbase, row_stride, hv, wave, nxt + C::bytes, dv);
+        }
+      };
       if constexpr (ONE) {
         // this wave's 16 copied rows of K and V -> bf16 tiles (16 codes per
         // lane and pass; rows that were not copied hold zeros)
@@ -712,7 +729,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
         const uint8_t* kt = ONE ? bk : cur;
         const uint8_t* vt = ONE ? bv : cur + C::bytes;
         const uint32_t bad = (uint32_t)__builtin_amdgcn_readfirstlane((int)bad_raw);
-        compute(kt, vt, t * kBN, bad);
+        compute(kt, vt, t * kBN, bad, copies);
       }
       // the entries of tile t + 2, after this tile's LDS reads (scalar loads
       // share a wait counter with LDS reads)
