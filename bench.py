@@ -99,8 +99,8 @@ def prefill_flops(step):
 # workload, and the prefill kernel on varlen_prefill_prefix.  The figures
 # belong to the kernel sources with the given digest: after any change to
 # them the traffic is reported as null until the counters are taken again.
-DECODE_TRAFFIC = {"digest": "375a0536eb30d31f", "read_bytes": 4317300878, "write_bytes": 4426340}
-PREFILL_TRAFFIC = {"digest": "375a0536eb30d31f", "read_bytes": 1689598578, "write_bytes": 127649024}
+DECODE_TRAFFIC = {"digest": "efeb15c87f602f6a", "read_bytes": 4317133099, "write_bytes": 4426389}
+PREFILL_TRAFFIC = {"digest": "efeb15c87f602f6a", "read_bytes": 1679527552, "write_bytes": 127677767}
 KERNEL_SOURCES = ("paged_kv_cache_map_amd/csrc/paged_decode.hip",
                   "paged_kv_cache_map_amd/csrc/varlen_prefill.hip",
                   "paged_kv_cache_map_amd/csrc/attention.hip",
