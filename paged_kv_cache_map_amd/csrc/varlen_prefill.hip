@@ -667,10 +667,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
         qf[cb][ks] = qvalid[cb] ? make_uint4(qf[cb][ks].x ^ q_sign, qf[cb][ks].y ^ q_sign, qf[cb][ks].z ^ q_sign,
                                              qf[cb][ks].w ^ q_sign)
                                 : make_uint4(0u, 0u, 0u, 0u);
-    // Each step: wait for tile t, locate tile t + 1, (one-byte caches:
-    // dequantise this wave's rows of tile t), compute tile t if the wave has
-    // keys in it, starting the copy of tile t + 1 after the score products,
-    // fetch the block-table entries of tile t + 2.
+    // Each step: wait for tile t, (one-byte caches: dequantise this wave's
+    // rows of tile t), compute tile t if the wave has keys in it, locating
+    // and copying tile t + 1 after the score products, fetch the block-table
+    // entries of tile t + 2.
     auto step = [&](int t, bool work, uint8_t* cur, uint8_t* nxt, uint32_t* fcur, uint32_t* fnxt)
                     __attribute__((always_inline)) {
       // this wave's copies of tile t and its flag byte have landed
@@ -684,25 +684,20 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Item& i
       // bit 8 w + x: wave w's half x of tile t lies in a block outside the
       // pool (read now, used after the copies are issued)
       const uint32_t bad_raw = (PAGED && work) ? *fcur : 0u;
-      // The copies of tile t + 1: a wave with keys in tile t issues them from
-      // inside compute(), once its score products have read their K operands,
-      // so that the copies' writes into LDS meet the softmax and the P.V
-      // reads rather than the K reads (a wave without keys here issues them
-      // now).
-      if (t + 1 < n_tiles) {
-        locate<PAGED>(hv, en, (t + 1) * kBN, lk, log2bs, a.num_blocks, wave, rs32, C::row_bytes);
-        if (!work) {
-          copy_rows<C>(kbase, row_stride, hv, wave, nxt, dk);
-          copy_rows<C>(vbase, row_stride, hv, wave, nxt + C::bytes, dv);
-        }
-        if constexpr (PAGED) reinterpret_cast<uint8_t*>(fnxt)[wave] = (uint8_t)hv.bad;
-      }
+      // Locating and copying tile t + 1: a wave with keys in tile t does it
+      // from inside compute(), once its score products have read their K
+      // operands, so that the products start sooner and the copies' writes
+      // into LDS meet the softmax and the P.V reads rather than the K reads
+      // (a wave without keys here does it now).
       auto copies = [&]() __attribute__((always_inline)) {
         if (t + 1 < n_tiles) {
+          locate<PAGED>(hv, en, (t + 1) * kBN, lk, log2bs, a.num_blocks, wave, rs32, C::row_bytes);
           copy_rows<C>(kbase, row_stride, hv, wave, nxt, dk);
           copy_rows<C>(vbase, row_stride, hv, wave, nxt + C::bytes, dv);
+          if constexpr (PAGED) reinterpret_cast<uint8_t*>(fnxt)[wave] = (uint8_t)hv.bad;
         }
       };
+      if (!work) copies();
       if constexpr (ONE) {
         // this wave's 16 copied rows of K and V -> bf16 tiles (16 codes per
         // lane and pass; rows that were not copied hold zeros)
