@@ -99,8 +99,8 @@ def prefill_flops(step):
 # workload, and the prefill kernel on varlen_prefill_prefix.  The figures
 # belong to the kernel sources with the given digest: after any change to
 # them the traffic is reported as null until the counters are taken again.
-DECODE_TRAFFIC = {"digest": "efeb15c87f602f6a", "read_bytes": 4317133099, "write_bytes": 4426389}
-PREFILL_TRAFFIC = {"digest": "efeb15c87f602f6a", "read_bytes": 1679527552, "write_bytes": 127677767}
+DECODE_TRAFFIC = {"digest": "050d554da647d6d2", "read_bytes": 4317107797, "write_bytes": 4426240}
+PREFILL_TRAFFIC = {"digest": "050d554da647d6d2", "read_bytes": 1669342094, "write_bytes": 127675573}
 KERNEL_SOURCES = ("paged_kv_cache_map_amd/csrc/paged_decode.hip",
                   "paged_kv_cache_map_amd/csrc/varlen_prefill.hip",
                   "paged_kv_cache_map_amd/csrc/attention.hip",
